@@ -1,0 +1,271 @@
+/*
+ * w4a16.h -- C ABI of libw4a16: the single-token decode step of a GQA
+ * transformer with weight-only INT4 projections (W4A16) and a paged fp16 KV
+ * cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title, section):
+ *   [RT-arch]  "How to build your own LLM runtime from scratch" (aikraft.ru
+ *              digest of a Towards Data Science article), "Architectural
+ *              decisions and optimizations": symmetric group-wise INT4
+ *              weights, group 128; RMSNorm and lm_head kept in FP16; GQA 7:1;
+ *              16-token KV pages, 4 KiB per head slice; INT4 GEMVs for the
+ *              gate/up/down projections.
+ *   [H100-kv]  "Building a Custom LLM Inference Runtime on H100", "The KV
+ *              Cache and PagedAttention": the KV cache split into pages and
+ *              managed like virtual memory, so sequences grow without
+ *              fragmentation.
+ *   [H100-bug] same page, "The Three Critical Bugs": Bug 1 (logical token
+ *              position -> physical block mapping), Bug 2 (aligned
+ *              intermediate buffers from a custom allocator), Bug 3 (no
+ *              asynchronous copy may be pending inside a captured graph).
+ *   [H100-graph] same page, "CUDA Graph Capture": the steady decode step is
+ *              captured once and replayed as one operation.
+ *   [H100-guide] same page, "Implementation Guide: Step-by-Step": KV cache
+ *              and activation buffers are allocated up front; an orchestrator
+ *              drives graph execution.
+ *
+ * Conventions
+ *   - Every int-returning call returns W4_OK (0) or a W4_E* code; on error
+ *     w4_last_error() gives a message (thread-local, valid until the next
+ *     call on the same thread). No C++ exception crosses this boundary.
+ *   - fp16 values travel as uint16_t holding IEEE binary16 bits.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP
+ *     device memory (for example a torch tensor's data_ptr()). Every device
+ *     pointer must be 256-byte aligned (W4_EALIGN otherwise).
+ *   - The caller owns every buffer. The library owns only the opaque
+ *     handles (w4_kv_pool, w4_model) and the graphs it captures, released by
+ *     the matching *_destroy. The library never allocates device memory:
+ *     its scratch lives in the caller's workspace.
+ *   - Device work is enqueued asynchronously on the caller's HIP stream
+ *     (`stream` is a hipStream_t; NULL means the default stream). Outputs are
+ *     valid once that stream has been synchronised.
+ *   - Validation failures return before any device work is enqueued and
+ *     change nothing.
+ *   - A model handle must be used by one thread at a time.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+enum {
+  W4_OK = 0,
+  W4_EINVAL = 1,    /* null pointer or unsupported shape / argument          */
+  W4_ERANGE = 2,    /* a value out of its range (q, page id, token, ctx ...) */
+  W4_EALIGN = 3,    /* device pointer not 256-byte aligned                   */
+  W4_ENOPAGES = 4,  /* KV page pool exhausted                                */
+  W4_EHIP = 5,      /* HIP runtime error; destroy the model afterwards       */
+  W4_ESTATE = 6     /* double free, unknown sequence, destroyed handle ...   */
+};
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* w4_last_error(void);
+/* Library version string. */
+const char* w4_version(void);
+
+/* ------------------------------------------------------------ weight packing
+ * INT4 packed format ("w4g128"). The quantisation is symmetric and
+ * group-wise with group 128 along the input dimension [RT-arch]: the weight
+ * of output row n, input column k is q[n,k] * s[n, k/128], q in [-8, 7],
+ * s fp16. The packer only re-lays (q, s); it never rounds or rescales.
+ *
+ * Row order. `role` permutes logical rows into physical rows so that the
+ * fused epilogues find related rows inside one 16-row tile:
+ *   W4_ROLE_PLAIN    identity.
+ *   W4_ROLE_QKV      n = (Hq + 2 Hkv) * head_dim rows (q heads, k heads, v
+ *                    heads, each head head_dim rows). Inside every head,
+ *                    physical tile p (p = 0 .. head_dim/16 - 1) holds logical
+ *                    head rows [8p, 8p+8) followed by [head_dim/2 + 8p,
+ *                    head_dim/2 + 8p + 8): the rotate-half RoPE pairs.
+ *                    head_dim must be a multiple of 16 and divide n.
+ *   W4_ROLE_GATE_UP  n = 2F rows: gate rows [0, F) then up rows [F, 2F).
+ *                    Physical tile t holds gate rows [8t, 8t+8) followed by
+ *                    up rows [F + 8t, F + 8t + 8). F must be a multiple of 8.
+ *
+ * Layout, with T = ceil(n/16) tiles and G = ceil(k/128) groups:
+ *   nibble section, T*G blocks of 1024 bytes; block (t, g) starts at byte
+ *   (t*G + g)*1024. In a block, lane l = 0..63 owns bytes [16l, 16l+16):
+ *   physical row 16t + (l & 15), input columns c0 = 128g + 32(l >> 4) + [0,32).
+ *   Those 16 bytes are four little-endian 32-bit words; word j holds columns
+ *   c0 + 8j + e, e = 0..7, each as u = q + 8 (offset binary, 0..15) in the
+ *   nibble at bit 4*(e/2) for even e and at bit 16 + 4*((e-1)/2) for odd e.
+ *   Columns >= k and rows >= n hold u = 8 (q = 0).
+ *   scale section, at byte T*G*1024: fp16 [T][G][16]; entry (t, g, i) is the
+ *   scale of physical row 16t + i for group g (0 for rows >= n).
+ *   Total size: w4_packed_bytes(n, k) = T*G*1024 + T*G*32.
+ * A 64-lane wavefront thus reads each block with one fully coalesced
+ * 16-byte-per-lane load, and the lane data of a block is also the B operand
+ * of four 16x16x32 fp16 MFMAs after nibble expansion.
+ */
+enum { W4_ROLE_PLAIN = 0, W4_ROLE_QKV = 1, W4_ROLE_GATE_UP = 2 };
+
+size_t w4_packed_bytes(int32_t n, int32_t k);
+
+/* Pack q (host int8 [n*k], row-major, every value in [-8, 7]) and scales
+ * (host fp16 [n * ceil(k/128)], row-major) into `out` (host, out_bytes >=
+ * w4_packed_bytes(n, k)). Pure and deterministic. W4_ERANGE if some q is
+ * outside [-8, 7]; W4_EINVAL on bad shapes or a role/head_dim mismatch.
+ * head_dim is read only for W4_ROLE_QKV. */
+int pack_weights_w4g128(const int8_t* q, const uint16_t* scales, int32_t n, int32_t k,
+                        uint32_t role, int32_t head_dim, void* out, size_t out_bytes);
+
+/* Packed fp16 format (lm_head, kept in FP16 [RT-arch]): T = ceil(n/16)
+ * tiles, C = ceil(k/32) column blocks; block (t, c) of 1024 bytes starts at
+ * (t*C + c)*1024; lane l owns bytes [16l, 16l+16) = the 8 fp16 values of row
+ * 16t + (l & 15), columns 32c + 8(l >> 4) + [0, 8). Zero padded. */
+size_t w4_packed_f16_bytes(int32_t n, int32_t k);
+int pack_weights_f16(const uint16_t* w, int32_t n, int32_t k, void* out, size_t out_bytes);
+
+/* ------------------------------------------------------------- KV page pool
+ * Host-side bookkeeping of a paged KV cache [H100-kv]: pages of 16 tokens
+ * [RT-arch], O(1) allocation from a free list, per-sequence page lists, and
+ * dense page tables for the device. Page ids index the device KV cache.
+ */
+typedef struct w4_kv_pool w4_kv_pool;
+
+int  kv_pool_create(int32_t num_pages, int32_t max_seqs, w4_kv_pool** out);
+void kv_pool_destroy(w4_kv_pool* pool);
+/* Allocate n pages into out_ids[n] (host). All or nothing: W4_ENOPAGES if
+ * fewer than n are free, and then nothing is allocated. */
+int  kv_alloc_pages(w4_kv_pool* pool, int32_t n, int32_t* out_ids);
+/* Return pages. W4_ESTATE (and nothing freed) if any id is not currently
+ * allocated, is owned by a sequence, or repeats; W4_ERANGE if out of range. */
+int  kv_free_pages(w4_kv_pool* pool, const int32_t* ids, int32_t n);
+int32_t kv_free_count(const w4_kv_pool* pool);
+/* Grow sequence `seq` (0 <= seq < max_seqs) to hold ctx_len tokens, i.e.
+ * ceil(ctx_len/16) pages, appending pages to its list. Never shrinks.
+ * All or nothing (W4_ENOPAGES). */
+int  kv_seq_reserve(w4_kv_pool* pool, int32_t seq, int32_t ctx_len);
+/* Free every page of `seq`. */
+int  kv_seq_release(w4_kv_pool* pool, int32_t seq);
+/* Number of pages held by `seq` (-1 if seq is out of range). */
+int32_t kv_seq_pages(const w4_kv_pool* pool, int32_t seq);
+/* Dense page table (host int32 [batch * max_pages]): row b lists the pages
+ * of seqs[b] in logical order -- logical token t of that sequence lives in
+ * page row[t / 16], slot t % 16 [H100-bug, Bug 1] -- padded with -1.
+ * W4_ERANGE if a sequence holds more than max_pages pages. */
+int  page_table(const w4_kv_pool* pool, const int32_t* seqs, int32_t batch, int32_t max_pages,
+                int32_t* out);
+
+/* ------------------------------------------------------------------- model */
+typedef struct w4_config {
+  int32_t hidden;      /* H                                              */
+  int32_t n_heads;     /* Hq query heads                                 */
+  int32_t n_kv_heads;  /* Hkv; Hq / Hkv (the GQA group) must be 1..8     */
+  int32_t head_dim;    /* D: 64 or 128                                   */
+  int32_t ffn;         /* F, multiple of 8                               */
+  int32_t vocab;       /* V (lm_head rows / embedding rows)              */
+  int32_t n_layers;    /* L                                              */
+  float   rms_eps;     /* RMSNorm epsilon                                */
+  float   rope_base;   /* RoPE base (rotate-half convention)             */
+} w4_config;
+
+/* Device KV cache: fp16 [L][2][P][Hkv][16][D] -- for layer l, K pages then V
+ * pages, each page holding one 4 KiB (for D = 128) slice per KV head
+ * [RT-arch]. */
+size_t kv_cache_bytes(const w4_config* cfg, int32_t num_pages);
+
+typedef struct w4_layer_weights {
+  const void*     qkv;        /* device, packed role QKV, n = (Hq+2Hkv)D, k = H */
+  const void*     o;          /* device, packed role PLAIN, n = H, k = Hq D      */
+  const void*     gate_up;    /* device, packed role GATE_UP, n = 2F, k = H      */
+  const void*     down;       /* device, packed role PLAIN, n = H, k = F         */
+  const uint16_t* attn_norm;  /* device fp16 [H]                                 */
+  const uint16_t* mlp_norm;   /* device fp16 [H]                                 */
+  const uint16_t* qkv_bias;   /* device fp16 [(Hq+2Hkv)D] logical order, or NULL */
+} w4_layer_weights;
+
+typedef struct w4_weights {
+  const w4_layer_weights* layers;  /* host array [L]                              */
+  const uint16_t* embed;           /* device fp16 [V][H] row-major (NULL: layers only) */
+  const uint16_t* final_norm;      /* device fp16 [H] (NULL: layers only)          */
+  const void*     lm_head;         /* device, pack_weights_f16, n = V, k = H (NULL: layers only) */
+} w4_weights;
+
+typedef struct w4_model w4_model;
+
+/* Bytes of device workspace a model needs for batches up to max_batch and
+ * page tables of max_pages_per_seq columns [H100-guide]. */
+size_t w4_workspace_bytes(const w4_config* cfg, int32_t max_batch, int32_t max_pages_per_seq);
+
+/* Bind weights, KV cache and workspace (all caller-owned device memory; the
+ * pointers are kept, not copied) into a model. Zero-fills the workspace
+ * with a kernel on the default stream and waits for it. */
+int  w4_model_create(const w4_config* cfg, const w4_weights* weights, void* kv_cache,
+                     int32_t num_pages, void* workspace, size_t ws_bytes, int32_t max_batch,
+                     int32_t max_pages_per_seq, w4_model** out);
+void w4_model_destroy(w4_model* model);
+/* 1: decode_step captures its kernel sequence into a hipGraph on first use
+ * (per batch size and output/input pointers) and replays it afterwards
+ * [H100-graph]; 0: launch kernel by kernel. Default 1. */
+int  w4_set_graph(w4_model* model, int enabled);
+
+/* One decode step for `batch` sequences. tokens, positions, ctx_lens: host
+ * int32 [batch]; page_tables: host int32 [batch * max_pages_per_seq].
+ * Contract: ctx_lens[b] counts the token being decoded and positions[b] ==
+ * ctx_lens[b] - 1; its K/V are written to every layer's cache at page
+ * page_tables[b][positions[b] / 16], slot positions[b] % 16, before
+ * attention reads tokens [0, ctx_lens[b]). logits: device fp16 [batch][V].
+ * The host arrays are validated (W4_ERANGE) and copied into the workspace on
+ * `stream` before any kernel runs, never inside a captured graph [H100-bug,
+ * Bug 3]. */
+int  decode_step(w4_model* model, const int32_t* tokens, const int32_t* positions,
+                 const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                 uint16_t* logits, void* stream);
+/* Same step with tokens/positions/page_tables/ctx_lens already in device
+ * memory (same layouts). They cannot be validated on the host: kernels clamp
+ * every index so no access leaves its buffer, skip the K/V write of a
+ * token whose page id is invalid, and count such events; read the count with
+ * w4_device_errors. */
+int  decode_step_device(w4_model* model, const int32_t* tokens, const int32_t* positions,
+                        const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                        uint16_t* logits, void* stream);
+/* Synchronises `stream` and returns the number of invalid indices seen by
+ * kernels since model creation (0 when every input was valid), or -1. */
+int64_t w4_device_errors(w4_model* model, void* stream);
+
+/* One decoder layer (no embedding, no lm_head): x_out = layer(x_in), with the
+ * KV write of every sequence. x_in, x_out: device fp16 [batch][H] (may be
+ * the same buffer). positions/page_tables/ctx_lens: host, as decode_step. */
+int  decode_layer(w4_model* model, int32_t layer, const uint16_t* x_in, uint16_t* x_out,
+                  const int32_t* positions, const int32_t* page_tables, const int32_t* ctx_lens,
+                  int32_t batch, void* stream);
+
+/* ------------------------------------------------------- standalone kernels */
+/* y = fp16(W x) for a w4g128-packed W (role PLAIN rows in physical order),
+ * fp32 accumulation. x: device fp16 [batch][k]; y: device fp16 [batch][n];
+ * 1 <= batch <= 16. */
+int  w4_gemv(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
+             int32_t batch, void* stream);
+/* y = fp16(W x) for a pack_weights_f16 W, fp32 accumulation, batch 1..16. */
+int  w4_gemv_f16(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
+                 int32_t batch, void* stream);
+
+/* Paged-attention decode [H100-kv]: for each sequence b and query head h,
+ * out[b][h] = fp16(sum_t softmax_t(q[b][h] . K_t / sqrt(D)) V_t) over tokens
+ * t in [0, ctx_lens[b]), K_t/V_t read from KV head h / (Hq/Hkv) through the
+ * page table. q: device fp16 [batch][Hq][D]; k_pool, v_pool: device fp16
+ * [num_pages][Hkv][16][D]; page_tables: device int32 [batch][max_pages];
+ * ctx_lens: device int32 [batch]; out: device fp16 [batch][Hq][D].
+ * Device-resident indices are clamped like decode_step_device: a page id
+ * outside [0, num_pages) contributes nothing, ctx_lens are clamped to
+ * [0, 16 max_pages], and an empty context yields zeros. workspace: device,
+ * >= paged_attention_workspace_bytes(...) (split partials and counters). */
+size_t paged_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                       int32_t head_dim, int32_t max_pages);
+int  paged_attention_decode(const uint16_t* q, const void* k_pool, const void* v_pool,
+                            const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                            int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                            int32_t num_pages, int32_t max_pages, void* workspace,
+                            size_t ws_bytes, uint16_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_H */
