@@ -226,6 +226,15 @@ int  decode_step(w4_model* model, const int32_t* tokens, const int32_t* position
 int  decode_step_device(w4_model* model, const int32_t* tokens, const int32_t* positions,
                         const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
                         uint16_t* logits, void* stream);
+/* The host validation decode_step and decode_layer run before enqueueing
+ * anything (pure host function, no device access): batch in [1, max_batch];
+ * tokens[b] in [0, vocab) (tokens may be NULL to skip); ctx_lens[b] in
+ * [1, 16 max_pages]; positions[b] == ctx_lens[b] - 1; page_tables[b][p] in
+ * [0, num_pages) for p < ceil(ctx_lens[b]/16); and no two sequences write the
+ * same (page, slot). Returns W4_OK, W4_EINVAL or W4_ERANGE. */
+int  w4_validate_step(const w4_config* cfg, int32_t num_pages, int32_t max_batch, int32_t max_pages,
+                      const int32_t* tokens, const int32_t* positions, const int32_t* page_tables,
+                      const int32_t* ctx_lens, int32_t batch);
 /* Synchronises `stream` and returns the number of invalid indices seen by
  * kernels since model creation (0 when every input was valid), or -1. */
 int64_t w4_device_errors(w4_model* model, void* stream);
@@ -236,6 +245,33 @@ int64_t w4_device_errors(w4_model* model, void* stream);
 int  decode_layer(w4_model* model, int32_t layer, const uint16_t* x_in, uint16_t* x_out,
                   const int32_t* positions, const int32_t* page_tables, const int32_t* ctx_lens,
                   int32_t batch, void* stream);
+
+/* ---------------------------------------------------- per-operation access
+ * For tests and profiling: run the step one operation at a time on the
+ * model's own residual buffer (W4_BUF_X), with inputs staged by
+ * w4_model_stage (host arrays, validated as decode_step). The operations,
+ * in step order, are the embedding gather, then per layer the five fused
+ * kernels of decode_layer, then the final RMSNorm + lm_head:
+ *   W4_OP_QKV      RMSNorm, qkv projection, RoPE, K/V write of the token
+ *   W4_OP_ATTN     paged attention -> W4_BUF_O
+ *   W4_OP_OPROJ    x += W_o o
+ *   W4_OP_GATE_UP  RMSNorm, gate/up projection, SiLU(gate) * up -> W4_BUF_H
+ *   W4_OP_DOWN     x += W_down h
+ * W4_BUF_XN holds the fp16 RMSNorm output of the last QKV, GATE_UP or
+ * LM_HEAD operation.
+ * w4_model_buffer returns the device address of a workspace buffer (fp16
+ * rows of *row_stride elements, one per sequence) or NULL. */
+enum { W4_OP_EMBED = 0, W4_OP_QKV = 1, W4_OP_ATTN = 2, W4_OP_OPROJ = 3, W4_OP_GATE_UP = 4,
+       W4_OP_DOWN = 5, W4_OP_LM_HEAD = 6 };
+enum { W4_BUF_X = 0, W4_BUF_Q = 1, W4_BUF_O = 2, W4_BUF_H = 3, W4_BUF_XN = 4 };
+int   w4_model_stage(w4_model* model, const int32_t* tokens, const int32_t* positions,
+                     const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                     void* stream);
+/* layer is ignored for W4_OP_EMBED / W4_OP_LM_HEAD; logits (device fp16
+ * [batch][V]) is used by W4_OP_LM_HEAD only. */
+int   w4_model_run_op(w4_model* model, int32_t op, int32_t layer, int32_t batch,
+                      uint16_t* logits, void* stream);
+void* w4_model_buffer(w4_model* model, int32_t which, int32_t* row_stride);
 
 /* ------------------------------------------------------- standalone kernels */
 /* y = fp16(W x) for a w4g128-packed W (role PLAIN rows in physical order),

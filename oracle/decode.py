@@ -41,17 +41,20 @@ def dequant_w4g128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
 
 def gemv_w4(q: np.ndarray, s: np.ndarray, x: np.ndarray, rows_per_chunk: int = 4096) -> np.ndarray:
     """y[n] = sum_k W[n, k] x[k] with W = dequant_w4g128(q, s), in float64.
+    x may carry leading batch dimensions ([..., K] -> [..., N]).
 
     The matrix is dequantised a band of rows at a time to bound memory; each
     output is still one full-length float64 dot product.
     """
     x = np.asarray(x, dtype=np.float64)
+    lead = x.shape[:-1]
+    xb = x.reshape(-1, x.shape[-1]).T                      # [K, B]
     n = q.shape[0]
-    y = np.empty(n, dtype=np.float64)
+    y = np.empty((n, xb.shape[1]), dtype=np.float64)
     for r0 in range(0, n, rows_per_chunk):
         r1 = min(n, r0 + rows_per_chunk)
-        y[r0:r1] = dequant_w4g128(q[r0:r1], s[r0:r1]) @ x
-    return y
+        y[r0:r1] = dequant_w4g128(q[r0:r1], s[r0:r1]) @ xb
+    return y.T.reshape(lead + (n,))
 
 
 # ---------------------------------------------------------------- elementwise
@@ -63,7 +66,7 @@ def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float, exact: bool = False) -
     decisions and optimizations -- RMSNorm stays in FP16.
     """
     x = np.asarray(x, dtype=np.float64)
-    ms = np.dot(x, x) / x.shape[0]
+    ms = (x * x).sum(axis=-1, keepdims=True) / x.shape[-1]
     return r16(x / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64), exact)
 
 
@@ -174,6 +177,61 @@ def lse_merge(parts) -> np.ndarray:
 
 # ---------------------------------------------------------------- layers
 
+def qkv_stage(x: np.ndarray, w, pos: int, shape, exact: bool = False):
+    """xn = rmsnorm(x, gamma_attn); then qkv_from_normed(xn)."""
+    xn = rmsnorm(np.asarray(x, dtype=np.float64), w.attn_norm, shape.eps, exact)
+    return qkv_from_normed(xn, w, pos, shape, exact)
+
+
+def qkv_from_normed(xn: np.ndarray, w, pos: int, shape, exact: bool = False):
+    """[q; k; v] = W_qkv xn (+ bias); returns (r(RoPE(q)) [Hq, D],
+    r(RoPE(k)) [Hkv, D], r(v) [Hkv, D]) at position pos. q and k are rotated
+    unrounded and rounded once afterwards."""
+    sh = shape
+    xn = np.asarray(xn, dtype=np.float64)
+    if xn.ndim == 2:   # a batch: one position per row
+        y_all = gemv_w4(w.qkv_q, w.qkv_s, xn)
+        outs = [_split_qkv(y_all[b], w, int(np.asarray(pos)[b]), sh, exact) for b in range(xn.shape[0])]
+        return tuple(np.stack(t) for t in zip(*outs))
+    return _split_qkv(gemv_w4(w.qkv_q, w.qkv_s, xn), w, pos, sh, exact)
+
+
+def _split_qkv(y, w, pos, sh, exact):
+    if w.qkv_bias is not None:
+        y = y + np.asarray(w.qkv_bias, dtype=np.float64)
+    nq, nkv = sh.q_rows, sh.kv_rows
+    q = y[:nq].reshape(sh.n_heads, sh.head_dim)
+    k = y[nq:nq + nkv].reshape(sh.n_kv_heads, sh.head_dim)
+    v = r16(y[nq + nkv:].reshape(sh.n_kv_heads, sh.head_dim), exact)
+    return rope(q, pos, sh.rope_base, exact), rope(k, pos, sh.rope_base, exact), v
+
+
+def oproj_stage(x: np.ndarray, o: np.ndarray, w, exact: bool = False) -> np.ndarray:
+    """x1 = r(x + W_o o), o the concatenated attention heads [..., Hq D]."""
+    x = np.asarray(x, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64).reshape(x.shape[:-1] + (-1,))
+    return r16(x + gemv_w4(w.o_q, w.o_s, o), exact)
+
+
+def gate_up_stage(x1: np.ndarray, w, shape, exact: bool = False) -> np.ndarray:
+    """xn2 = rmsnorm(x1, gamma_mlp); then gate_up_from_normed(xn2)."""
+    xn2 = rmsnorm(np.asarray(x1, dtype=np.float64), w.mlp_norm, shape.eps, exact)
+    return gate_up_from_normed(xn2, w, shape, exact)
+
+
+def gate_up_from_normed(xn2: np.ndarray, w, shape, exact: bool = False) -> np.ndarray:
+    """h = r(silu(W_gate xn2) * (W_up xn2)); g and u unrounded."""
+    gu = gemv_w4(w.gate_up_q, w.gate_up_s, np.asarray(xn2, dtype=np.float64))
+    g, u = gu[..., :shape.ffn], gu[..., shape.ffn:]
+    return r16(silu(g) * u, exact)
+
+
+def down_stage(x1: np.ndarray, h: np.ndarray, w, exact: bool = False) -> np.ndarray:
+    """x2 = r(x1 + W_down h)."""
+    return r16(np.asarray(x1, dtype=np.float64) + gemv_w4(w.down_q, w.down_s, np.asarray(h, dtype=np.float64)),
+               exact)
+
+
 def decode_layer(x: np.ndarray, w, k_pool: np.ndarray, v_pool: np.ndarray,
                  page_table_row: np.ndarray, ctx: int, shape, exact: bool = False) -> np.ndarray:
     """One decoder layer for one sequence; returns the new residual x [H] and
@@ -190,27 +248,13 @@ def decode_layer(x: np.ndarray, w, k_pool: np.ndarray, v_pool: np.ndarray,
       h = r(silu(W_gate xn2) * (W_up xn2))
       return r(x1 + W_down h)
     """
-    sh = shape
     pos = ctx - 1
-    x = np.asarray(x, dtype=np.float64)
-    xn = rmsnorm(x, w.attn_norm, sh.eps, exact)
-    y = gemv_w4(w.qkv_q, w.qkv_s, xn)
-    if w.qkv_bias is not None:
-        y = y + np.asarray(w.qkv_bias, dtype=np.float64)
-    nq, nkv = sh.q_rows, sh.kv_rows
-    q = y[:nq].reshape(sh.n_heads, sh.head_dim)
-    k = y[nq:nq + nkv].reshape(sh.n_kv_heads, sh.head_dim)
-    v = r16(y[nq + nkv:].reshape(sh.n_kv_heads, sh.head_dim), exact)
-    q = rope(q, pos, sh.rope_base, exact)
-    k = rope(k, pos, sh.rope_base, exact)
+    q, k, v = qkv_stage(x, w, pos, shape, exact)
     kv_write(k_pool, v_pool, page_table_row, pos, k, v)
     o = attention_decode(q, k_pool, v_pool, page_table_row, ctx, exact)
-    x1 = r16(x + gemv_w4(w.o_q, w.o_s, o.reshape(-1)), exact)
-    xn2 = rmsnorm(x1, w.mlp_norm, sh.eps, exact)
-    gu = gemv_w4(w.gate_up_q, w.gate_up_s, xn2)
-    g, u = gu[:sh.ffn], gu[sh.ffn:]
-    h = r16(silu(g) * u, exact)
-    return r16(x1 + gemv_w4(w.down_q, w.down_s, h), exact)
+    x1 = oproj_stage(x, o, w, exact)
+    h = gate_up_stage(x1, w, shape, exact)
+    return down_stage(x1, h, w, exact)
 
 
 def lm_head(x: np.ndarray, final_norm: np.ndarray, w_lm: np.ndarray, eps: float,

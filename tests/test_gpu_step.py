@@ -1,0 +1,79 @@
+"""decode_step (embedding, decoder layers, final RMSNorm, fp16 lm_head) against
+the oracle; graph replay against eager launches ("Building a Custom LLM
+Inference Runtime on H100", CUDA Graph Capture and The Three Critical Bugs,
+Bug 3)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import runs
+from tests.gpu_util import assert_close, to_np16
+from workloads.device import DeviceModel
+
+pytestmark = pytest.mark.gpu
+
+SMALL = wl.Shape(hidden=448, n_heads=7, n_kv_heads=1, head_dim=64, ffn=1536, vocab=5000, n_layers=3)
+
+
+def small_model(ctx, gamma="random", wid=30):
+    return DeviceModel(wl.custom("small_step", wid, SMALL, ctx, layers=3, lm_head=True, gamma=gamma))
+
+
+def step(dm, graph=True, inputs=None):
+    dm.model.w4_set_graph(graph)
+    t, p, pt, c = inputs or dm.step_inputs()
+    logits = torch.empty((len(t), dm.w.shape.vocab), dtype=torch.float16, device="cuda")
+    dm.model.decode_step(t, p, pt, c, logits)
+    torch.cuda.synchronize()
+    return to_np16(logits)
+
+
+@pytest.mark.parametrize("ctx", [[40], [64, 3, 17]])
+def test_small_step_matches_oracle(ctx):
+    dm = small_model(ctx)
+    got = step(dm, graph=False)
+    ref = runs.step(dm.w)["logits"]
+    assert_close(got, ref, "logits")
+
+
+def test_graph_equals_eager_and_replays_are_deterministic():
+    dm = small_model([50, 20])
+    a = step(dm, graph=False)
+    b = step(dm, graph=True)
+    c = step(dm, graph=True)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.array_equal(b.view(np.uint16), c.view(np.uint16))
+
+
+def test_graph_replays_follow_changing_inputs():
+    """One captured graph, new tokens / contexts / page tables every call: each
+    replay equals an eager run of the same inputs."""
+    dm = small_model([60, 30])
+    w = dm.w
+    rs = np.random.default_rng(3)
+    for it in range(6):
+        ctx = rs.integers(1, 64, 2).astype(np.int32)
+        pt = np.full_like(w.page_tables, -1)
+        perm = rs.permutation(w.num_pages).astype(np.int32)
+        n0, n1 = (ctx + 15) // 16
+        pt[0, :n0] = perm[:n0]
+        pt[1, :n1] = perm[n0:n0 + n1]
+        inputs = (rs.integers(0, SMALL.vocab, 2).astype(np.int32), ctx - 1, pt, ctx)
+        snap = dm.kv_cache.clone()
+        g = step(dm, True, inputs)
+        dm.kv_cache.copy_(snap)
+        e = step(dm, False, inputs)
+        assert np.array_equal(g.view(np.uint16), e.view(np.uint16)), f"replay {it}"
+
+
+def test_device_inputs_match_host_inputs():
+    dm = small_model([45, 9])
+    t, p, pt, c = dm.step_inputs()
+    a = step(dm, graph=True)
+    dev = [torch.from_numpy(np.ascontiguousarray(x, np.int32)).cuda() for x in (t, p, pt, c)]
+    logits = torch.empty((2, SMALL.vocab), dtype=torch.float16, device="cuda")
+    dm.model.decode_step_device(*dev, logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.view(np.uint16), to_np16(logits).view(np.uint16))
+    assert dm.model.w4_device_errors() == 0

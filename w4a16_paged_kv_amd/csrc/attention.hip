@@ -1,0 +1,287 @@
+// Paged-attention decode for gfx950.
+//
+// The KV cache is split into 16-token pages addressed through a page table
+// ("Building a Custom LLM Inference Runtime on H100", The KV Cache and
+// PagedAttention; "How to build your own LLM runtime from scratch",
+// Architectural decisions and optimizations: 16-token pages, 4 KiB per head
+// slice, GQA 7:1). Logical token t of sequence b lives in page
+// page_tables[b][t / 16], slot t % 16 (same page, The Three Critical Bugs,
+// Bug 1).
+//
+// One workgroup = (split of consecutive pages, KV head, sequence). Each of its
+// four wavefronts streams whole pages: one (page, KV head) K slice and V slice
+// is read from HBM once and used for all GQ query heads of the group from
+// registers. Softmax is online, in fp32 and base 2. The workgroup writes its
+// un-normalised (o, m, l) partial; the last workgroup of a (sequence, KV head)
+// to finish merges all partials with a log-sum-exp reduction and writes fp16
+// o. Every barrier sits in uniform control flow (the same page's Bug list
+// warns against barriers inside divergent branches).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "w4_internal.h"
+
+namespace w4 {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2_t as_h2a(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+__device__ __forceinline__ uint16_t f2h_a(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D, int GQ>
+__global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(GQ >= 1 && GQ <= 8, "group");
+  constexpr int NI = D / 32;          // 8-column sub-chunks per lane for scores
+  constexpr int LD = D / 8;           // lanes per token row for PV (8 columns each)
+  constexpr int TPI = 64 / LD;        // token rows per PV load instruction
+  constexpr int NTOK = kPage / TPI;   // tokens per lane for PV
+  __shared__ float s_m[4][8], s_l[4][8];
+  __shared__ float s_o[4][GQ][D];
+  __shared__ int s_last;
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ctx = a.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * kPage ? a.max_pages * kPage : ctx);
+  const int npages = (ctx + kPage - 1) / kPage;
+  const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
+  uint16_t* out = a.out + (size_t)b * a.out_stride + (size_t)kvh * GQ * D;
+  if (npages == 0) {  // empty context: zeros
+    if (split == 0)
+      for (int i = threadIdx.x; i < GQ * D; i += 256) out[i] = 0;
+    return;
+  }
+  if (split >= nsplit) return;
+  const int p_begin = split * a.pages_per_split;
+  const int p_end = min(npages, p_begin + a.pages_per_split);
+  const int32_t* pt = a.page_tables + (size_t)b * a.max_pages;
+
+  // q fragments: lane (tk = lane >> 2, c = lane & 3) covers columns 8c + 32i .. +8
+  const int tk = lane >> 2, c = lane & 3;
+  const uint16_t* qb = a.q + (size_t)b * a.q_stride + (size_t)kvh * GQ * D;
+  u4_t qf[GQ][NI];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) qf[h][i] = *reinterpret_cast<const u4_t*>(qb + h * D + 8 * c + 32 * i);
+
+  const float scale = kLog2e / sqrtf((float)D);
+  const int hA = c, hB = c + 4;            // heads whose softmax state this lane keeps
+  float mA = -INFINITY, mB = -INFINITY, lA = 0.f, lB = 0.f;
+  float o[GQ][8];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  const int d0 = 8 * (lane % LD);          // PV columns of this lane
+  const int t0 = lane / LD;                // first PV token row of this lane
+  const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
+
+  for (int p = p_begin + wave; p < p_end; p += 4) {
+    int page = pt[p];
+    const bool bad = page < 0 || page >= a.num_pages;
+    if (bad) {
+      if (lane == 0) atomicAdd(a.err, 1u);
+      page = 0;
+    }
+    const int valid = bad ? 0 : min(kPage, ctx - p * kPage);
+    const uint16_t* kb = a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice;
+    const uint16_t* vb = a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice;
+    u4_t kf[NI], vf[NTOK];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kf[i] = *reinterpret_cast<const u4_t*>(kb + tk * D + 8 * c + 32 * i);
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) vf[i] = *reinterpret_cast<const u4_t*>(vb + (t0 + TPI * i) * D + d0);
+
+    // scores of token tk for every head of the group
+    float s[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(as_h2a(qf[h][i][e]), as_h2a(kf[i][e]), acc, false);
+      acc += dpp_xor1(acc);
+      acc += dpp_xor2(acc);
+      s[h] = acc * scale;
+    }
+    float sA = -INFINITY, sB = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      if (h == hA) sA = s[h];
+      if (h == hB) sB = s[h];
+    }
+    if (tk >= valid) {
+      sA = -INFINITY;
+      sB = -INFINITY;
+    }
+    // page maximum over the 16 tokens (lanes sharing c)
+    float pmA = sA, pmB = sB;
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) {
+      pmA = fmaxf(pmA, __shfl_xor(pmA, off));
+      pmB = fmaxf(pmB, __shfl_xor(pmB, off));
+    }
+    const float nA = fmaxf(mA, pmA), nB = fmaxf(mB, pmB);
+    const float alA = nA == -INFINITY ? 1.f : exp2f(mA - nA);
+    const float alB = nB == -INFINITY ? 1.f : exp2f(mB - nB);
+    const float pA = nA == -INFINITY ? 0.f : exp2f(sA - nA);
+    const float pB = nB == -INFINITY ? 0.f : exp2f(sB - nB);
+    float sumA = pA, sumB = pB;
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) {
+      sumA += __shfl_xor(sumA, off);
+      sumB += __shfl_xor(sumB, off);
+    }
+    lA = lA * alA + sumA;
+    lB = lB * alB + sumB;
+    mA = nA;
+    mB = nB;
+
+    // masked tokens contribute nothing even if their slots hold NaN
+    if (valid < kPage) {
+#pragma unroll
+      for (int i = 0; i < NTOK; ++i)
+        if (t0 + TPI * i >= valid) vf[i] = (u4_t){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      const int src = h & 3;
+      const float al = __shfl(h < 4 ? alA : alB, src);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= al;
+#pragma unroll
+      for (int i = 0; i < NTOK; ++i) {
+        const float pv = __shfl(h < 4 ? pA : pB, 4 * (t0 + TPI * i) + src);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2_t v2 = as_h2a(vf[i][e]);
+          o[h][2 * e] = fmaf(pv, (float)v2[0], o[h][2 * e]);
+          o[h][2 * e + 1] = fmaf(pv, (float)v2[1], o[h][2 * e + 1]);
+        }
+      }
+    }
+  }
+  // reduce o over the lanes holding other token rows of the same columns
+#pragma unroll
+  for (int off = LD; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], off);
+  if (lane < 4) {
+    s_m[wave][hA] = mA;
+    s_l[wave][hA] = lA;
+    if (hB < 8) {
+      s_m[wave][hB] = mB;
+      s_l[wave][hB] = lB;
+    }
+  }
+  if (lane < LD)
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[wave][h][d0 + e] = o[h][e];
+  __syncthreads();
+
+  // combine the four wavefronts into this split's partial
+  float* part = a.partials + (((size_t)b * a.n_kv_heads + kvh) * a.max_splits + split) * GQ * (D + 2);
+  for (int idx = threadIdx.x; idx < GQ * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = exp2f(s_m[w][h] - M);
+        L += f * s_l[w][h];
+        O += f * s_o[w][h][d];
+      }
+    }
+    part[h * (D + 2) + d] = O;
+    if (d == 0) {
+      part[h * (D + 2) + D] = M;
+      part[h * (D + 2) + D + 1] = L;
+    }
+  }
+  // the last split to arrive merges (log-sum-exp over splits)
+  __threadfence();
+  __syncthreads();
+  uint32_t* counter = a.counters + (size_t)b * a.n_kv_heads + kvh;
+  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == (uint32_t)(nsplit - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * (D + 2);
+  for (int idx = threadIdx.x; idx < GQ * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, pb[((size_t)sp * GQ + h) * (D + 2) + D]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+      for (int sp = 0; sp < nsplit; ++sp) {
+        const float* ps = pb + ((size_t)sp * GQ + h) * (D + 2);
+        const float f = exp2f(ps[D] - M);
+        L += f * ps[D + 1];
+        O += f * ps[d];
+      }
+    }
+    out[h * D + d] = f2h_a(L > 0.f ? O / L : 0.f);
+  }
+  if (threadIdx.x == 0) *counter = 0u;
+}
+
+bool attention_supported(int head_dim, int group) {
+  return (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 ||
+                                                 group == 7 || group == 8);
+}
+
+int attention_pages_per_split(int batch, int n_kv_heads, int max_pages) {
+  const long units = (long)batch * n_kv_heads * max_pages;
+  long pps = (units + 4095) / 4096;
+  int p = 4;
+  while (p < pps && p < 64) p <<= 1;
+  return p;
+}
+
+template <int D, int GQ>
+static hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((paged_attn_kernel<D, GQ>), dim3(a.max_splits, a.n_kv_heads, a.batch),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d(const AttnArgs& a, int group, hipStream_t s) {
+  switch (group) {
+    case 1: return launch_dg<D, 1>(a, s);
+    case 2: return launch_dg<D, 2>(a, s);
+    case 4: return launch_dg<D, 4>(a, s);
+    case 7: return launch_dg<D, 7>(a, s);
+    case 8: return launch_dg<D, 8>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s) {
+  if (head_dim == 64) return launch_d<64>(a, group, s);
+  if (head_dim == 128) return launch_d<128>(a, group, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w4

@@ -1,0 +1,519 @@
+// W4A16 projections and the fp16 lm_head for gfx950.
+//
+// Weights: symmetric group-wise INT4, group 128 along the input dimension,
+// dequantised value q * s ("How to build your own LLM runtime from
+// scratch", Architectural decisions and optimizations). lm_head and RMSNorm
+// stay in FP16 (same section).
+//
+// Batch 1 is a bandwidth-bound GEMV and runs on the vector ALUs: every lane
+// expands 32 nibbles of one row to fp16 in registers (OR into the exponent of
+// 1024.0, subtract 1032: exact), takes v_dot2_f32_f16 against the activation
+// pairs staged in LDS, scales the fp32 group sum once, and the four lanes
+// holding a row are reduced across the wavefront at the end.
+// Batches 2..16 turn each projection into a skinny dense contraction and run
+// the same packed blocks through v_mfma_f32_16x16x32_f16.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "w4_internal.h"
+
+namespace w4 {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h2f(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
+__device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+// Nibbles at bits 4i and 16+4i of a packed word -> the exact fp16 pair
+// (q_{2i}, q_{2i+1}). 0x6400 is 1024.0; its ulp is 1, so 0x6400|u == 1024+u.
+__device__ __forceinline__ h2_t nib_pair(uint32_t word, int i) {
+  const uint32_t v = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+  return __builtin_bit_cast(h2_t, v) - (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+}
+
+__device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+
+// Sum over one lane's 32 columns of a block: 4 words x 4 nibble pairs.
+__device__ __forceinline__ float dot_block(const u4_t w, const uint16_t* __restrict__ xl) {
+  const u4_t* xp = reinterpret_cast<const u4_t*>(xl);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u4_t xv = xp[j];
+    s = __builtin_amdgcn_fdot2(nib_pair(w[j], 0), as_h2(xv[0]), s, false);
+    s = __builtin_amdgcn_fdot2(nib_pair(w[j], 1), as_h2(xv[1]), s, false);
+    s = __builtin_amdgcn_fdot2(nib_pair(w[j], 2), as_h2(xv[2]), s, false);
+    s = __builtin_amdgcn_fdot2(nib_pair(w[j], 3), as_h2(xv[3]), s, false);
+  }
+  return s;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Copies x[0..k) (fp16, k % 8 == 0) into LDS xs[0..kpad), zero padded, and if
+// gamma is given replaces it by fp16(x * rsqrt(mean(x^2) + eps) * gamma)
+// (RMSNorm, kept in FP16). red needs NT/64 floats. Ends with a barrier.
+template <int NT>
+__device__ void stage_x(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
+                        float eps, int k, int kpad, uint16_t* xs, float* red) {
+  const int tid = threadIdx.x;
+  float ss = 0.f;
+  for (int i = tid * 8; i < kpad; i += NT * 8) {
+    u4_t v = {0u, 0u, 0u, 0u};
+    if (i < k) v = *reinterpret_cast<const u4_t*>(x + i);
+    *reinterpret_cast<u4_t*>(xs + i) = v;
+    if (gamma) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const h2_t h = as_h2(v[c]);
+        const float a = (float)h[0], b = (float)h[1];
+        ss = fmaf(a, a, ss);
+        ss = fmaf(b, b, ss);
+      }
+    }
+  }
+  if (gamma) {
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) tot += red[w];
+    const float rs = 1.0f / sqrtf(tot / (float)k + eps);
+    for (int i = tid * 8; i < k; i += NT * 8) {
+      u4_t v = *reinterpret_cast<const u4_t*>(xs + i);
+      const u4_t g = *reinterpret_cast<const u4_t*>(gamma + i);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const h2_t hv = as_h2(v[c]), hg = as_h2(g[c]);
+        h2_t r;
+        r[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
+        r[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
+        v[c] = __builtin_bit_cast(uint32_t, r);
+      }
+      *reinterpret_cast<u4_t*>(xs + i) = v;
+    }
+  }
+  __syncthreads();
+}
+
+// Copies the staged (normalised) activations back to global memory.
+template <int NT>
+__device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* dst) {
+  for (int i = threadIdx.x * 8; i < k; i += NT * 8)
+    *reinterpret_cast<u4_t*>(dst + i) = *reinterpret_cast<const u4_t*>(xs + i);
+}
+
+// ------------------------------------------------------------- epilogues
+
+__device__ __forceinline__ void kv_store(const QkvEpilogue& e, int m, uint16_t* pool, int kvh,
+                                         int dim0, int dim1, float v0, float v1) {
+  const int pos = e.positions[m];
+  if (pos < 0 || pos >= e.max_pages * kPage) {
+    atomicAdd(e.err, 1u);
+    return;
+  }
+  const int page = e.page_tables[(size_t)m * e.max_pages + (pos >> 4)];
+  if (page < 0 || page >= e.num_pages) {
+    atomicAdd(e.err, 1u);
+    return;
+  }
+  uint16_t* slot = pool + (((size_t)page * e.n_kv_heads + kvh) * kPage + (pos & 15)) * e.head_dim;
+  slot[dim0] = f2h(v0);
+  slot[dim1] = f2h(v1);
+}
+
+// Rows i and i+8 of tile t hold the rotate-half RoPE pair (dim0, dim0 + D/2)
+// of one head (QKV packing role). q/k heads are rotated at the token's
+// position, theta = pos * base^(-2 dim0 / D), and rounded once to fp16; v
+// heads are rounded unrotated. k/v go to the token's page slot.
+__device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float y1) {
+  const QkvEpilogue& e = a.qkv;
+  const int D = e.head_dim;
+  const int head = (kTileRows * t) / D;
+  const int p = ((kTileRows * t) % D) / kTileRows;
+  const int dim0 = 8 * p + i, dim1 = D / 2 + 8 * p + i;
+  if (e.bias) {
+    y0 += h2f(e.bias[head * D + dim0]);
+    y1 += h2f(e.bias[head * D + dim1]);
+  }
+  if (head < e.n_heads + e.n_kv_heads) {
+    int pos = e.positions[m];
+    const double th = (double)pos * pow((double)e.rope_base, -2.0 * (double)dim0 / (double)D);
+    const float c = (float)cos(th), s = (float)sin(th);
+    const float r0 = y0 * c - y1 * s;
+    const float r1 = y1 * c + y0 * s;
+    if (head < e.n_heads) {
+      uint16_t* q = e.q_out + (size_t)m * e.q_stride + head * D;
+      q[dim0] = f2h(r0);
+      q[dim1] = f2h(r1);
+    } else {
+      kv_store(e, m, e.k_pool, head - e.n_heads, dim0, dim1, r0, r1);
+    }
+  } else {
+    kv_store(e, m, e.v_pool, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ constexpr int epi_items() {
+  return (EPI == EPI_SILU || EPI == EPI_QKV) ? 8 : 16;
+}
+
+// Applies the epilogue to item i of tile t for batch row m; vals[16] are the
+// fp32 results of the tile's 16 physical rows.
+template <int EPI>
+__device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i, const float* vals) {
+  if (EPI == EPI_QKV) {
+    epi_qkv(a, m, t, i, vals[i], vals[i + 8]);
+  } else if (EPI == EPI_SILU) {
+    const int o = 8 * t + i;
+    if (o < a.n / 2) {
+      const float g = vals[i], u = vals[i + 8];
+      a.y[(size_t)m * a.y_stride + o] = f2h(g / (1.0f + expf(-g)) * u);
+    }
+  } else {
+    const int row = kTileRows * t + i;
+    if (row < a.n) {
+      float v = vals[i];
+      if (EPI == EPI_RESID) v += h2f(a.resid[(size_t)m * a.y_stride + row]);
+      a.y[(size_t)m * a.y_stride + row] = f2h(v);
+    }
+  }
+}
+
+// ------------------------------------------------------------ batch 1, VALU
+
+constexpr int kUnroll = 8;  // blocks in flight per wavefront
+
+template <int EPI, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void w4_gemv_b1_kernel(GemvArgs a) {
+  constexpr int NT = WAVES * 64;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int G = a.groups;
+  const int kpad = G * kGroup;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);  // WAVES*16 + 16 + WAVES
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + (size_t)t * G * 64 + lane;
+  const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024) +
+                       (size_t)t * G * 16 + (lane & 15);
+
+  // weight loads of the first batch go out before the activation prologue
+  u4_t cur[kUnroll];
+  float csc[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int g = wave + u * WAVES;
+    cur[u] = g < G ? __builtin_nontemporal_load(wb + (size_t)g * 64) : (u4_t){0u, 0u, 0u, 0u};
+    csc[u] = g < G ? h2f(sb[(size_t)g * 16]) : 0.f;
+  }
+  stage_x<NT>(a.x, a.gamma, a.eps, a.k, kpad, xs, red + WAVES * 16 + 16);
+  if (a.xn_out && blockIdx.x == 0) store_xs<NT>(xs, a.k, a.xn_out);
+
+  const uint16_t* xl = xs + 32 * (lane >> 4);
+  float acc = 0.f;
+  for (int base = wave; base < G; base += kUnroll * WAVES) {
+    u4_t nxt[kUnroll];
+    float nsc[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int g = base + (kUnroll + u) * WAVES;
+      nxt[u] = g < G ? __builtin_nontemporal_load(wb + (size_t)g * 64) : (u4_t){0u, 0u, 0u, 0u};
+      nsc[u] = g < G ? h2f(sb[(size_t)g * 16]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int g = base + u * WAVES;
+      if (g < G) acc = fmaf(dot_block(cur[u], xl + g * kGroup), csc[u], acc);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      cur[u] = nxt[u];
+      csc[u] = nsc[u];
+    }
+  }
+  // lanes l, l+16, l+32, l+48 hold the same row
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (lane < 16) red[wave * 16 + lane] = acc;
+  __syncthreads();
+  float* vals = red + WAVES * 16;
+  if (threadIdx.x < 16) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += red[w * 16 + threadIdx.x];
+    vals[threadIdx.x] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < epi_items<EPI>()) epilogue<EPI>(a, 0, t, threadIdx.x, vals);
+}
+
+// ------------------------------------------------------- batch 2..16, MFMA
+// D[m][n] = sum_k x[m][k] W[n][k] over one 128-column group with four
+// v_mfma_f32_16x16x32_f16; lane l supplies A row m = l & 15 (batch row,
+// clamped to batch-1) and B column n = l & 15 (weight row), both for the
+// k-slots 8 (l >> 4) .. +8 of each step, which the packed layout provides.
+// The fp32 group result is scaled per weight row and accumulated.
+// Activations come pre-normalised; columns >= k read as zero.
+
+template <int EPI, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void w4_gemm_mfma_kernel(GemvArgs a) {
+  constexpr int NT = WAVES * 64;
+  __shared__ float red[WAVES][16][17];
+  __shared__ float tot[16][17];
+  const int G = a.groups;
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + (size_t)t * G * 64 + lane;
+  const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024) +
+                       (size_t)t * G * 16 + (lane & 15);
+  const int mrow = min(lane & 15, a.batch - 1);
+  const uint16_t* xr = a.x + (size_t)mrow * a.x_stride + 32 * (lane >> 4);
+
+  f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;
+  for (int base = wave; base < G; base += U * WAVES) {
+    u4_t wv[U];
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = base + u * WAVES;
+      wv[u] = g < G ? __builtin_nontemporal_load(wb + (size_t)g * 64) : (u4_t){0u, 0u, 0u, 0u};
+      sc[u] = g < G ? h2f(sb[(size_t)g * 16]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = base + u * WAVES;
+      if (g < G) {
+        f4_t d = {0.f, 0.f, 0.f, 0.f};
+        const u4_t* xp = reinterpret_cast<const u4_t*>(xr + (size_t)g * kGroup);
+        const int col0 = g * kGroup + 32 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u4_t xv = col0 + 8 * j < a.k ? xp[j] : (u4_t){0u, 0u, 0u, 0u};
+          const h8_t av = __builtin_bit_cast(h8_t, xv);
+          u4_t braw;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) braw[i] = __builtin_bit_cast(uint32_t, nib_pair(wv[u][j], i));
+          const h8_t bv = __builtin_bit_cast(h8_t, braw);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, d, 0, 0, 0);
+        }
+        acc += d * sc[u];
+      }
+    }
+  }
+  // acc[j] = D[m = 4 (lane >> 4) + j][n = lane & 15]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[wave][4 * (lane >> 4) + j][lane & 15] = acc[j];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 256; idx += NT) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += red[w][idx >> 4][idx & 15];
+    tot[idx >> 4][idx & 15] = v;
+  }
+  __syncthreads();
+  constexpr int per = epi_items<EPI>();
+  for (int item = threadIdx.x; item < a.batch * per; item += NT)
+    epilogue<EPI>(a, item / per, t, item % per, &tot[item / per][0]);
+}
+
+// ------------------------------------------------------------ fp16 lm_head
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void f16_gemv_b1_kernel(F16GemvArgs a) {
+  constexpr int NT = WAVES * 64;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int C = a.cblocks;
+  const int kpad = (C * 32 + kGroup - 1) / kGroup * kGroup;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+  float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * WAVES + wave;  // one 16-row tile per wavefront
+  const bool live = t < a.tiles;
+  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + (size_t)(live ? t : 0) * C * 64 + lane;
+
+  u4_t cur[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    cur[u] = (live && u < C) ? __builtin_nontemporal_load(wb + (size_t)u * 64) : (u4_t){0u, 0u, 0u, 0u};
+  stage_x<NT>(a.x, a.gamma, a.eps, a.k, kpad, xs, red);
+  if (a.xn_out && blockIdx.x == 0) store_xs<NT>(xs, a.k, a.xn_out);
+  if (!live) return;
+  const uint16_t* xl = xs + 8 * (lane >> 4);
+  float acc = 0.f;
+  for (int base = 0; base < C; base += kUnroll) {
+    u4_t nxt[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = base + kUnroll + u;
+      nxt[u] = c < C ? __builtin_nontemporal_load(wb + (size_t)c * 64) : (u4_t){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = base + u;
+      if (c < C) {
+        const u4_t xv = *reinterpret_cast<const u4_t*>(xl + 32 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(as_h2(cur[u][i]), as_h2(xv[i]), acc, false);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+  }
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  const int row = 16 * t + lane;
+  if (lane < 16 && row < a.n) a.y[row] = f2h(acc);
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void f16_gemm_mfma_kernel(F16GemvArgs a) {
+  const int C = a.cblocks;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * WAVES + wave;
+  if (t >= a.tiles) return;
+  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + (size_t)t * C * 64 + lane;
+  const int mrow = min(lane & 15, a.batch - 1);
+  const uint16_t* xr = a.x + (size_t)mrow * a.x_stride + 8 * (lane >> 4);
+  f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 8;
+  for (int base = 0; base < C; base += U) {
+    u4_t wv[U], xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = base + u;
+      wv[u] = c < C ? __builtin_nontemporal_load(wb + (size_t)c * 64) : (u4_t){0u, 0u, 0u, 0u};
+      xv[u] = (c < C && 32 * c + 8 * (lane >> 4) < a.k) ? *reinterpret_cast<const u4_t*>(xr + 32 * c)
+                                                           : (u4_t){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xv[u]),
+                                                  __builtin_bit_cast(h8_t, wv[u]), acc, 0, 0, 0);
+  }
+  const int row = 16 * t + (lane & 15);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = 4 * (lane >> 4) + j;
+    if (m < a.batch && row < a.n) a.y[(size_t)m * a.y_stride + row] = f2h(acc[j]);
+  }
+}
+
+// ------------------------------------------------------------ small kernels
+
+// y[b] = fp16(x[b] * rsqrt(mean(x[b]^2) + eps) * gamma), zero padded to the
+// next multiple of 128 columns (batched path: the MFMA kernels read it).
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* x, int x_stride,
+                                                           const uint16_t* gamma, float eps, int k,
+                                                           uint16_t* y, int y_stride) {
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const uint16_t* xr = x + (size_t)b * x_stride;
+  uint16_t* yr = y + (size_t)b * y_stride;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < k; i += 256) {
+    const float v = h2f(xr[i]);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float rs = 1.0f / sqrtf(tot / (float)k + eps);
+  const int kpad = (k + kGroup - 1) / kGroup * kGroup;
+  for (int i = threadIdx.x; i < kpad; i += 256)
+    yr[i] = i < k ? f2h(h2f(xr[i]) * rs * h2f(gamma[i])) : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const uint16_t* table,
+                                                    int vocab, int hidden, uint16_t* x,
+                                                    uint32_t* err) {
+  const int b = blockIdx.x;
+  int tok = tokens[b];
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0) atomicAdd(err, 1u);
+    tok = tok < 0 ? 0 : vocab - 1;
+  }
+  const uint16_t* src = table + (size_t)tok * hidden;
+  uint16_t* dst = x + (size_t)b * hidden;
+  for (int i = threadIdx.x * 8; i < hidden; i += 256 * 8)
+    *reinterpret_cast<u4_t*>(dst + i) = *reinterpret_cast<const u4_t*>(src + i);
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t count, uint32_t value) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int EPI>
+static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
+  if (a.batch == 1) {
+    constexpr int WAVES = 4;
+    const size_t lds = (size_t)a.groups * kGroup * 2 + (WAVES * 16 + 16 + WAVES) * sizeof(float);
+    hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, WAVES>), dim3(a.tiles), dim3(WAVES * 64), lds, s, a);
+  } else {
+    constexpr int WAVES = 4;
+    hipLaunchKernelGGL((w4_gemm_mfma_kernel<EPI, WAVES>), dim3(a.tiles), dim3(WAVES * 64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_w4_gemv(int epi, const GemvArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_w4_epi<EPI_STORE>(a, s);
+    case EPI_RESID: return launch_w4_epi<EPI_RESID>(a, s);
+    case EPI_SILU: return launch_w4_epi<EPI_SILU>(a, s);
+    case EPI_QKV: return launch_w4_epi<EPI_QKV>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s) {
+  constexpr int WAVES = 4;
+  const int grid = ceil_div(a.tiles, WAVES);
+  if (a.batch == 1) {
+    const size_t kpad = round_up((size_t)a.cblocks * 32, kGroup);
+    const size_t lds = kpad * 2 + WAVES * sizeof(float);
+    hipLaunchKernelGGL((f16_gemv_b1_kernel<WAVES>), dim3(grid), dim3(WAVES * 64), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((f16_gemm_mfma_kernel<WAVES>), dim3(grid), dim3(WAVES * 64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16_t* gamma, float eps,
+                               int32_t k, uint16_t* y, int32_t y_stride, int32_t batch,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(batch), dim3(256), 0, s, x, x_stride, gamma, eps, k,
+                     y, y_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const int32_t* tokens, const uint16_t* table, int32_t vocab, int32_t hidden,
+                        uint16_t* x, int32_t batch, uint32_t* err, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(batch), dim3(256), 0, s, tokens, table, vocab, hidden, x, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  const int grid = (int)std::min<size_t>(1024, (count + 255) / 256);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid), dim3(256), 0, s, p, count, value);
+  return hipGetLastError();
+}
+
+}  // namespace w4

@@ -1,0 +1,684 @@
+// Decode runtime of libw4a16: workspace carving, host validation, staging,
+// the per-layer kernel sequence, and hipGraph capture/replay of the step.
+//
+// Static preallocation: KV cache and activation buffers come from the caller
+// up front, nothing is allocated per step ("Building a Custom LLM Inference
+// Runtime on H100", Implementation Guide: Step-by-Step). Step inputs are
+// copied into fixed staging before a captured graph is launched, never inside
+// the capture (same page, The Three Critical Bugs, Bug 3), and every
+// sub-buffer is 256-byte aligned (Bug 2 there asks for aligned intermediate
+// buffers).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <tuple>
+#include <vector>
+
+#include "w4_internal.h"
+
+namespace w4 {
+
+struct WsLayout {
+  size_t err, counters, tokens, positions, ctx, pt, x, xn, q, o, h, partials, total;
+  int xn_stride, o_stride, h_stride, max_splits;
+};
+
+static WsLayout ws_layout(const w4_config& c, int max_batch, int max_pages) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  const int group = c.n_heads / c.n_kv_heads;
+  L.xn_stride = (int)round_up(c.hidden, kGroup);
+  L.o_stride = (int)round_up((size_t)c.n_heads * c.head_dim, kGroup);
+  L.h_stride = (int)round_up(c.ffn, kGroup);
+  L.max_splits = ceil_div(max_pages, 4);
+  L.err = take(256);
+  L.counters = take((size_t)max_batch * c.n_kv_heads * 4);
+  L.tokens = take((size_t)max_batch * 4);
+  L.positions = take((size_t)max_batch * 4);
+  L.ctx = take((size_t)max_batch * 4);
+  L.pt = take((size_t)max_batch * max_pages * 4);
+  L.x = take((size_t)max_batch * c.hidden * 2);
+  L.xn = take((size_t)max_batch * L.xn_stride * 2);
+  L.q = take((size_t)max_batch * c.n_heads * c.head_dim * 2);
+  L.o = take((size_t)max_batch * L.o_stride * 2);
+  L.h = take((size_t)max_batch * L.h_stride * 2);
+  L.partials = take(attention_partial_floats(max_batch, c.n_kv_heads, L.max_splits, group,
+                                             c.head_dim) * 4);
+  L.total = off;
+  return L;
+}
+
+static int check_config(const w4_config* c) {
+  if (!c) return fail(W4_EINVAL, "null config");
+  if (c->hidden <= 0 || c->hidden % 8 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
+      c->n_heads % c->n_kv_heads || c->ffn <= 0 || c->ffn % 8 || c->vocab <= 0 || c->n_layers <= 0)
+    return fail(W4_EINVAL, "unsupported config: hidden=%d (mult. of 8) heads=%d/%d ffn=%d (mult. of 8) "
+                "vocab=%d layers=%d", c->hidden, c->n_heads, c->n_kv_heads, c->ffn, c->vocab, c->n_layers);
+  if (!attention_supported(c->head_dim, c->n_heads / c->n_kv_heads))
+    return fail(W4_EINVAL, "unsupported head_dim %d / GQA group %d (head_dim 64 or 128, group 1, 2, 4, 7 or 8)",
+                c->head_dim, c->n_heads / c->n_kv_heads);
+  if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f))
+    return fail(W4_EINVAL, "bad rms_eps %g or rope_base %g", c->rms_eps, c->rope_base);
+  return W4_OK;
+}
+
+}  // namespace w4
+
+using namespace w4;
+
+struct w4_model {
+  w4_config cfg;
+  std::vector<w4_layer_weights> layers;
+  w4_weights weights;
+  uint16_t* kv = nullptr;
+  int32_t num_pages = 0, max_batch = 0, max_pages = 0;
+  uint8_t* ws = nullptr;
+  WsLayout L;
+  bool use_graph = true;
+  hipStream_t cap_stream = nullptr;
+  // key: batch, logits, device-input pointers (null for host inputs)
+  typedef std::tuple<int, const void*, const void*, const void*, const void*, const void*> Key;
+  std::map<Key, hipGraphExec_t> graphs;
+
+  template <class T>
+  T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
+  uint16_t* k_pool(int l) {
+    return kv + (size_t)(2 * l) * num_pages * cfg.n_kv_heads * kPage * cfg.head_dim;
+  }
+  uint16_t* v_pool(int l) {
+    return kv + (size_t)(2 * l + 1) * num_pages * cfg.n_kv_heads * kPage * cfg.head_dim;
+  }
+};
+
+namespace w4 {
+
+// Device-resident per-step inputs (staging or caller-provided).
+struct StepInputs {
+  const int32_t* tokens;
+  const int32_t* positions;
+  const int32_t* page_tables;
+  const int32_t* ctx_lens;
+};
+
+#define W4_LAUNCH(call)                                                                  \
+  do {                                                                                   \
+    hipError_t e_ = (call);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return ::w4::fail(W4_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));         \
+  } while (0)
+
+static GemvArgs gemv_args(const void* w, int n, int k, const uint16_t* x, int x_stride,
+                          const uint16_t* gamma, float eps, uint16_t* y, int y_stride,
+                          const uint16_t* resid, int batch) {
+  GemvArgs a{};
+  a.w = static_cast<const uint8_t*>(w);
+  a.n = n;
+  a.k = k;
+  a.tiles = w4_tiles(n);
+  a.groups = w4_groups(k);
+  a.x = x;
+  a.x_stride = x_stride;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.y = y;
+  a.y_stride = y_stride;
+  a.resid = resid;
+  a.batch = batch;
+  return a;
+}
+
+// Enqueues one operation of decoder layer l for `batch` sequences. The
+// residual stream goes x_in -> (o projection) x_out -> (down projection)
+// x_out; q, o and h live in the workspace.
+static int enqueue_op(w4_model* m, int op, int l, const uint16_t* x_in, uint16_t* x_out,
+                      const StepInputs& in, int batch, hipStream_t s) {
+  const w4_config& c = m->cfg;
+  const w4_layer_weights& W = m->layers[l];
+  const WsLayout& L = m->L;
+  uint32_t* err = m->at<uint32_t>(L.err);
+  uint16_t* xn = m->at<uint16_t>(L.xn);
+  uint16_t* q = m->at<uint16_t>(L.q);
+  uint16_t* o = m->at<uint16_t>(L.o);
+  uint16_t* h = m->at<uint16_t>(L.h);
+  const bool b1 = batch == 1;
+  switch (op) {
+    case W4_OP_QKV: {  // qkv projection (RMSNorm prologue at batch 1), RoPE, K/V page write
+      const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+      if (!b1) W4_LAUNCH(launch_rmsnorm_rows(x_in, c.hidden, W.attn_norm, c.rms_eps, c.hidden, xn,
+                                             L.xn_stride, batch, s));
+      GemvArgs a = b1 ? gemv_args(W.qkv, qkv_rows, c.hidden, x_in, c.hidden, W.attn_norm,
+                                  c.rms_eps, nullptr, 0, nullptr, 1)
+                      : gemv_args(W.qkv, qkv_rows, c.hidden, xn, L.xn_stride, nullptr, 0.f,
+                                  nullptr, 0, nullptr, batch);
+      if (b1) a.xn_out = xn;
+      a.qkv.q_out = q;
+      a.qkv.q_stride = c.n_heads * c.head_dim;
+      a.qkv.k_pool = m->k_pool(l);
+      a.qkv.v_pool = m->v_pool(l);
+      a.qkv.bias = W.qkv_bias;
+      a.qkv.positions = in.positions;
+      a.qkv.page_tables = in.page_tables;
+      a.qkv.max_pages = m->max_pages;
+      a.qkv.num_pages = m->num_pages;
+      a.qkv.n_heads = c.n_heads;
+      a.qkv.n_kv_heads = c.n_kv_heads;
+      a.qkv.head_dim = c.head_dim;
+      a.qkv.rope_base = c.rope_base;
+      a.qkv.err = err;
+      W4_LAUNCH(launch_w4_gemv(EPI_QKV, a, s));
+      return W4_OK;
+    }
+    case W4_OP_ATTN: {  // paged attention, split over pages, LSE merge by the last split
+      AttnArgs at{};
+      at.q = q;
+      at.q_stride = c.n_heads * c.head_dim;
+      at.k_pool = m->k_pool(l);
+      at.v_pool = m->v_pool(l);
+      at.page_tables = in.page_tables;
+      at.ctx_lens = in.ctx_lens;
+      at.batch = batch;
+      at.max_pages = m->max_pages;
+      at.num_pages = m->num_pages;
+      at.n_heads = c.n_heads;
+      at.n_kv_heads = c.n_kv_heads;
+      at.pages_per_split = attention_pages_per_split(batch, c.n_kv_heads, m->max_pages);
+      at.max_splits = ceil_div(m->max_pages, at.pages_per_split);
+      at.partials = m->at<float>(L.partials);
+      at.counters = m->at<uint32_t>(L.counters);
+      at.out = o;
+      at.out_stride = L.o_stride;
+      at.err = err;
+      W4_LAUNCH(launch_attention(at, c.head_dim, c.n_heads / c.n_kv_heads, s));
+      return W4_OK;
+    }
+    case W4_OP_OPROJ:  // o projection + residual
+      W4_LAUNCH(launch_w4_gemv(EPI_RESID, gemv_args(W.o, c.hidden, c.n_heads * c.head_dim, o,
+                                                    L.o_stride, nullptr, 0.f, x_out, c.hidden,
+                                                    x_in, batch), s));
+      return W4_OK;
+    case W4_OP_GATE_UP:  // gate/up (RMSNorm prologue at batch 1) with SiLU-mul
+      if (!b1) W4_LAUNCH(launch_rmsnorm_rows(x_out, c.hidden, W.mlp_norm, c.rms_eps, c.hidden, xn,
+                                             L.xn_stride, batch, s));
+      {
+        GemvArgs a = b1 ? gemv_args(W.gate_up, 2 * c.ffn, c.hidden, x_out, c.hidden, W.mlp_norm,
+                                    c.rms_eps, h, L.h_stride, nullptr, 1)
+                        : gemv_args(W.gate_up, 2 * c.ffn, c.hidden, xn, L.xn_stride, nullptr, 0.f,
+                                    h, L.h_stride, nullptr, batch);
+        if (b1) a.xn_out = xn;
+        W4_LAUNCH(launch_w4_gemv(EPI_SILU, a, s));
+      }
+      return W4_OK;
+    case W4_OP_DOWN:  // down projection + residual
+      W4_LAUNCH(launch_w4_gemv(EPI_RESID, gemv_args(W.down, c.hidden, c.ffn, h, L.h_stride,
+                                                    nullptr, 0.f, x_out, c.hidden, x_out, batch),
+                               s));
+      return W4_OK;
+  }
+  return fail(W4_EINVAL, "unknown layer op %d", op);
+}
+
+// Enqueues one decoder layer: x_out = layer(x_in) for `batch` sequences.
+static int enqueue_layer(w4_model* m, int l, const uint16_t* x_in, uint16_t* x_out,
+                         const StepInputs& in, int batch, hipStream_t s) {
+  for (int op = W4_OP_QKV; op <= W4_OP_DOWN; ++op) {
+    int rc = enqueue_op(m, op, l, x_in, x_out, in, batch, s);
+    if (rc) return rc;
+  }
+  return W4_OK;
+}
+
+static int enqueue_lm_head(w4_model* m, const uint16_t* x, int batch, uint16_t* logits,
+                           hipStream_t s) {
+  const w4_config& c = m->cfg;
+  F16GemvArgs f{};
+  f.w = static_cast<const uint8_t*>(m->weights.lm_head);
+  f.n = c.vocab;
+  f.k = c.hidden;
+  f.tiles = w4_tiles(c.vocab);
+  f.cblocks = ceil_div(c.hidden, 32);
+  f.y = logits;
+  f.y_stride = c.vocab;
+  f.batch = batch;
+  f.eps = c.rms_eps;
+  if (batch == 1) {
+    f.x = x;
+    f.x_stride = c.hidden;
+    f.gamma = m->weights.final_norm;
+    f.xn_out = m->at<uint16_t>(m->L.xn);
+  } else {
+    uint16_t* xn = m->at<uint16_t>(m->L.xn);
+    W4_LAUNCH(launch_rmsnorm_rows(x, c.hidden, m->weights.final_norm, c.rms_eps, c.hidden, xn,
+                                  m->L.xn_stride, batch, s));
+    f.x = xn;
+    f.x_stride = m->L.xn_stride;
+  }
+  W4_LAUNCH(launch_f16_gemv(f, s));
+  return W4_OK;
+}
+
+static int enqueue_step(w4_model* m, const StepInputs& in, int batch, uint16_t* logits,
+                        hipStream_t s) {
+  const w4_config& c = m->cfg;
+  uint16_t* x = m->at<uint16_t>(m->L.x);
+  W4_LAUNCH(launch_embed(in.tokens, m->weights.embed, c.vocab, c.hidden, x, batch,
+                         m->at<uint32_t>(m->L.err), s));
+  for (int l = 0; l < c.n_layers; ++l) {
+    int rc = enqueue_layer(m, l, x, x, in, batch, s);
+    if (rc) return rc;
+  }
+  return enqueue_lm_head(m, x, batch, logits, s);
+}
+
+// Host validation of one step's inputs; nothing is enqueued on failure.
+static int validate_step(int vocab, int num_pages, int max_pages, const int32_t* tokens,
+                         const int32_t* positions, const int32_t* page_tables,
+                         const int32_t* ctx_lens, int batch) {
+  for (int b = 0; b < batch; ++b) {
+    if (tokens && (tokens[b] < 0 || tokens[b] >= vocab))
+      return fail(W4_ERANGE, "tokens[%d] = %d outside [0, %d)", b, tokens[b], vocab);
+    const int ctx = ctx_lens[b];
+    if (ctx < 1 || ctx > max_pages * kPage)
+      return fail(W4_ERANGE, "ctx_lens[%d] = %d outside [1, %d]", b, ctx, max_pages * kPage);
+    if (positions[b] != ctx - 1)
+      return fail(W4_ERANGE, "positions[%d] = %d but ctx_lens[%d] - 1 = %d", b, positions[b], b,
+                  ctx - 1);
+    const int32_t* row = page_tables + (size_t)b * max_pages;
+    for (int p = 0; p < ceil_div(ctx, kPage); ++p)
+      if (row[p] < 0 || row[p] >= num_pages)
+        return fail(W4_ERANGE, "page_tables[%d][%d] = %d outside [0, %d)", b, p, row[p], num_pages);
+  }
+  // two sequences must not write the same (page, slot)
+  for (int b = 0; b < batch; ++b)
+    for (int b2 = b + 1; b2 < batch; ++b2) {
+      const int pb = page_tables[(size_t)b * max_pages + positions[b] / kPage];
+      const int pb2 = page_tables[(size_t)b2 * max_pages + positions[b2] / kPage];
+      if (pb == pb2 && positions[b] % kPage == positions[b2] % kPage)
+        return fail(W4_ERANGE, "sequences %d and %d write the same KV slot (page %d, slot %d)", b,
+                    b2, pb, positions[b] % kPage);
+    }
+  return W4_OK;
+}
+
+static int validate_inputs(const w4_model* m, const int32_t* tokens, const int32_t* positions,
+                           const int32_t* page_tables, const int32_t* ctx_lens, int batch) {
+  return validate_step(m->cfg.vocab, m->num_pages, m->max_pages, tokens, positions, page_tables,
+                       ctx_lens, batch);
+}
+
+static int stage_inputs(w4_model* m, const int32_t* tokens, const int32_t* positions,
+                        const int32_t* page_tables, const int32_t* ctx_lens, int batch,
+                        hipStream_t s) {
+  const WsLayout& L = m->L;
+  if (tokens) W4_HIP(hipMemcpyAsync(m->ws + L.tokens, tokens, batch * 4, hipMemcpyHostToDevice, s));
+  W4_HIP(hipMemcpyAsync(m->ws + L.positions, positions, batch * 4, hipMemcpyHostToDevice, s));
+  W4_HIP(hipMemcpyAsync(m->ws + L.ctx, ctx_lens, batch * 4, hipMemcpyHostToDevice, s));
+  W4_HIP(hipMemcpyAsync(m->ws + L.pt, page_tables, (size_t)batch * m->max_pages * 4,
+                        hipMemcpyHostToDevice, s));
+  return W4_OK;
+}
+
+static StepInputs staged(w4_model* m) {
+  return {m->at<int32_t>(m->L.tokens), m->at<int32_t>(m->L.positions), m->at<int32_t>(m->L.pt),
+          m->at<int32_t>(m->L.ctx)};
+}
+
+// Runs the step eagerly or through a graph captured once per key.
+static int run_step(w4_model* m, const StepInputs& in, int batch, uint16_t* logits,
+                    hipStream_t s, const void* key_inputs) {
+  if (!m->use_graph) return enqueue_step(m, in, batch, logits, s);
+  w4_model::Key key(batch, logits, key_inputs ? in.tokens : nullptr,
+                    key_inputs ? in.positions : nullptr, key_inputs ? in.page_tables : nullptr,
+                    key_inputs ? in.ctx_lens : nullptr);
+  auto it = m->graphs.find(key);
+  if (it == m->graphs.end()) {
+    hipGraph_t graph = nullptr;
+    W4_HIP(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
+    int rc = enqueue_step(m, in, batch, logits, m->cap_stream);
+    hipError_t e = hipStreamEndCapture(m->cap_stream, &graph);
+    if (rc) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) return fail(W4_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return fail(W4_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+    it = m->graphs.emplace(key, exec).first;
+  }
+  W4_HIP(hipGraphLaunch(it->second, s));
+  return W4_OK;
+}
+
+static int check_model(const w4_model* m, int batch) {
+  if (!m) return fail(W4_ESTATE, "null model");
+  if (batch < 1 || batch > m->max_batch)
+    return fail(W4_EINVAL, "batch %d outside [1, %d]", batch, m->max_batch);
+  return W4_OK;
+}
+
+}  // namespace w4
+
+W4_EXPORT int w4_validate_step(const w4_config* cfg, int32_t num_pages, int32_t max_batch,
+                               int32_t max_pages, const int32_t* tokens, const int32_t* positions,
+                               const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch) {
+  clear_error();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (batch < 1 || batch > max_batch || max_pages < 1 || num_pages < 1)
+    return fail(W4_EINVAL, "batch %d outside [1, %d] or max_pages=%d num_pages=%d", batch,
+                max_batch, max_pages, num_pages);
+  if (!positions || !page_tables || !ctx_lens) return fail(W4_EINVAL, "null input array");
+  return validate_step(cfg->vocab, num_pages, max_pages, tokens, positions, page_tables, ctx_lens,
+                       batch);
+}
+
+W4_EXPORT size_t w4_workspace_bytes(const w4_config* cfg, int32_t max_batch, int32_t max_pages) {
+  if (check_config(cfg) || max_batch < 1 || max_batch > 16 || max_pages < 1) return 0;
+  return ws_layout(*cfg, max_batch, max_pages).total;
+}
+
+W4_EXPORT int w4_model_create(const w4_config* cfg, const w4_weights* weights, void* kv_cache,
+                              int32_t num_pages, void* workspace, size_t ws_bytes,
+                              int32_t max_batch, int32_t max_pages, w4_model** out) {
+  clear_error();
+  if (!out || !weights || !weights->layers || !kv_cache || !workspace)
+    return fail(W4_EINVAL, "w4_model_create: null pointer");
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (max_batch < 1 || max_batch > 16 || max_pages < 1 || num_pages < 1)
+    return fail(W4_EINVAL, "w4_model_create: max_batch=%d (1..16) max_pages=%d num_pages=%d",
+                max_batch, max_pages, num_pages);
+  const WsLayout L = ws_layout(*cfg, max_batch, max_pages);
+  if (ws_bytes < L.total)
+    return fail(W4_EINVAL, "w4_model_create: workspace %zu bytes < %zu", ws_bytes, L.total);
+  if (!aligned256(kv_cache) || !aligned256(workspace))
+    return fail(W4_EALIGN, "w4_model_create: kv_cache/workspace not 256-byte aligned");
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const w4_layer_weights& W = weights->layers[l];
+    const void* ptrs[] = {W.qkv, W.o, W.gate_up, W.down, W.attn_norm, W.mlp_norm};
+    for (const void* p : ptrs) {
+      if (!p) return fail(W4_EINVAL, "w4_model_create: layer %d has a null weight", l);
+      if (!aligned256(p)) return fail(W4_EALIGN, "w4_model_create: layer %d weight not 256-byte aligned", l);
+    }
+    if (W.qkv_bias && !aligned256(W.qkv_bias))
+      return fail(W4_EALIGN, "w4_model_create: layer %d qkv_bias not 256-byte aligned", l);
+  }
+  const void* top[] = {weights->embed, weights->final_norm, weights->lm_head};
+  for (const void* p : top)
+    if (p && !aligned256(p)) return fail(W4_EALIGN, "w4_model_create: embed/final_norm/lm_head not 256-byte aligned");
+
+  auto* m = new w4_model;
+  m->cfg = *cfg;
+  m->layers.assign(weights->layers, weights->layers + cfg->n_layers);
+  m->weights = *weights;
+  m->weights.layers = nullptr;
+  m->kv = static_cast<uint16_t*>(kv_cache);
+  m->num_pages = num_pages;
+  m->max_batch = max_batch;
+  m->max_pages = max_pages;
+  m->ws = static_cast<uint8_t*>(workspace);
+  m->L = L;
+  hipError_t e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(m->ws), L.total / 4, 0u, m->cap_stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(m->cap_stream);
+  if (e != hipSuccess) {
+    if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+    delete m;
+    return fail(W4_EHIP, "w4_model_create: %s", hipGetErrorString(e));
+  }
+  *out = m;
+  return W4_OK;
+}
+
+W4_EXPORT void w4_model_destroy(w4_model* m) {
+  if (!m) return;
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  delete m;
+}
+
+W4_EXPORT int w4_set_graph(w4_model* m, int enabled) {
+  clear_error();
+  if (!m) return fail(W4_ESTATE, "null model");
+  m->use_graph = enabled != 0;
+  return W4_OK;
+}
+
+W4_EXPORT int decode_step(w4_model* m, const int32_t* tokens, const int32_t* positions,
+                          const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                          uint16_t* logits, void* stream) {
+  clear_error();
+  int rc = check_model(m, batch);
+  if (rc) return rc;
+  if (!tokens || !positions || !page_tables || !ctx_lens || !logits)
+    return fail(W4_EINVAL, "decode_step: null pointer");
+  if (!m->weights.embed || !m->weights.lm_head || !m->weights.final_norm)
+    return fail(W4_EINVAL, "decode_step: model has no embedding / final norm / lm_head");
+  if (!aligned256(logits)) return fail(W4_EALIGN, "decode_step: logits not 256-byte aligned");
+  rc = validate_inputs(m, tokens, positions, page_tables, ctx_lens, batch);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = stage_inputs(m, tokens, positions, page_tables, ctx_lens, batch, s);
+  if (rc) return rc;
+  return run_step(m, staged(m), batch, logits, s, nullptr);
+}
+
+W4_EXPORT int decode_step_device(w4_model* m, const int32_t* tokens, const int32_t* positions,
+                                 const int32_t* page_tables, const int32_t* ctx_lens,
+                                 int32_t batch, uint16_t* logits, void* stream) {
+  clear_error();
+  int rc = check_model(m, batch);
+  if (rc) return rc;
+  if (!tokens || !positions || !page_tables || !ctx_lens || !logits)
+    return fail(W4_EINVAL, "decode_step_device: null pointer");
+  if (!m->weights.embed || !m->weights.lm_head || !m->weights.final_norm)
+    return fail(W4_EINVAL, "decode_step_device: model has no embedding / final norm / lm_head");
+  const void* ptrs[] = {tokens, positions, page_tables, ctx_lens, logits};
+  for (const void* p : ptrs)
+    if (!aligned256(p)) return fail(W4_EALIGN, "decode_step_device: device pointer not 256-byte aligned");
+  StepInputs in{tokens, positions, page_tables, ctx_lens};
+  return run_step(m, in, batch, logits, static_cast<hipStream_t>(stream), tokens);
+}
+
+W4_EXPORT int64_t w4_device_errors(w4_model* m, void* stream) {
+  clear_error();
+  if (!m) return -1;
+  uint32_t v = 0;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return -1;
+  if (hipMemcpy(&v, m->ws + m->L.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  return v;
+}
+
+W4_EXPORT int decode_layer(w4_model* m, int32_t layer, const uint16_t* x_in, uint16_t* x_out,
+                           const int32_t* positions, const int32_t* page_tables,
+                           const int32_t* ctx_lens, int32_t batch, void* stream) {
+  clear_error();
+  int rc = check_model(m, batch);
+  if (rc) return rc;
+  if (layer < 0 || layer >= m->cfg.n_layers)
+    return fail(W4_EINVAL, "decode_layer: layer %d outside [0, %d)", layer, m->cfg.n_layers);
+  if (!x_in || !x_out || !positions || !page_tables || !ctx_lens)
+    return fail(W4_EINVAL, "decode_layer: null pointer");
+  if (!aligned256(x_in) || !aligned256(x_out))
+    return fail(W4_EALIGN, "decode_layer: x_in/x_out not 256-byte aligned");
+  rc = validate_inputs(m, nullptr, positions, page_tables, ctx_lens, batch);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = stage_inputs(m, nullptr, positions, page_tables, ctx_lens, batch, s);
+  if (rc) return rc;
+  return enqueue_layer(m, layer, x_in, x_out, staged(m), batch, s);
+}
+
+// ------------------------------------------------------- standalone kernels
+
+W4_EXPORT int w4_gemv(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
+                      int32_t batch, void* stream) {
+  clear_error();
+  if (!packed || !x || !y) return fail(W4_EINVAL, "w4_gemv: null pointer");
+  if (n <= 0 || k <= 0 || k % 8 || batch < 1 || batch > 16)
+    return fail(W4_EINVAL, "w4_gemv: n=%d k=%d (multiple of 8) batch=%d (1..16)", n, k, batch);
+  if (!aligned256(packed) || !aligned256(x) || !aligned256(y))
+    return fail(W4_EALIGN, "w4_gemv: pointer not 256-byte aligned");
+  GemvArgs a = gemv_args(packed, n, k, x, k, nullptr, 0.f, y, n, nullptr, batch);
+  W4_LAUNCH(launch_w4_gemv(EPI_STORE, a, static_cast<hipStream_t>(stream)));
+  return W4_OK;
+}
+
+W4_EXPORT int w4_gemv_f16(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
+                          int32_t batch, void* stream) {
+  clear_error();
+  if (!packed || !x || !y) return fail(W4_EINVAL, "w4_gemv_f16: null pointer");
+  if (n <= 0 || k <= 0 || k % 8 || batch < 1 || batch > 16)
+    return fail(W4_EINVAL, "w4_gemv_f16: n=%d k=%d (multiple of 8) batch=%d (1..16)", n, k, batch);
+  if (!aligned256(packed) || !aligned256(x) || !aligned256(y))
+    return fail(W4_EALIGN, "w4_gemv_f16: pointer not 256-byte aligned");
+  F16GemvArgs f{};
+  f.w = static_cast<const uint8_t*>(packed);
+  f.n = n;
+  f.k = k;
+  f.tiles = w4_tiles(n);
+  f.cblocks = ceil_div(k, 32);
+  f.x = x;
+  f.x_stride = k;
+  f.y = y;
+  f.y_stride = n;
+  f.batch = batch;
+  W4_LAUNCH(launch_f16_gemv(f, static_cast<hipStream_t>(stream)));
+  return W4_OK;
+}
+
+static size_t attn_ws_layout(int batch, int n_heads, int n_kv_heads, int head_dim, int max_pages,
+                             size_t* partials_off, int* max_splits, int* pps) {
+  *pps = attention_pages_per_split(batch, n_kv_heads, max_pages);
+  *max_splits = ceil_div(max_pages, *pps);
+  // counters [batch][Hkv] then one invalid-index counter
+  const size_t counters = round_up((size_t)batch * n_kv_heads * 4 + 4, 256);
+  *partials_off = counters;
+  return counters + round_up(attention_partial_floats(batch, n_kv_heads, *max_splits,
+                                                      n_heads / n_kv_heads, head_dim) * 4, 256);
+}
+
+W4_EXPORT size_t paged_attention_workspace_bytes(int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                                 int32_t head_dim, int32_t max_pages) {
+  if (batch < 1 || n_kv_heads < 1 || n_heads < 1 || n_heads % n_kv_heads || max_pages < 1 ||
+      !attention_supported(head_dim, n_heads / n_kv_heads))
+    return 0;
+  size_t off;
+  int ms, pps;
+  return attn_ws_layout(batch, n_heads, n_kv_heads, head_dim, max_pages, &off, &ms, &pps);
+}
+
+W4_EXPORT int paged_attention_decode(const uint16_t* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* page_tables, const int32_t* ctx_lens,
+                                     int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, int32_t num_pages, int32_t max_pages,
+                                     void* workspace, size_t ws_bytes, uint16_t* out,
+                                     void* stream) {
+  clear_error();
+  if (!q || !k_pool || !v_pool || !page_tables || !ctx_lens || !workspace || !out)
+    return fail(W4_EINVAL, "paged_attention_decode: null pointer");
+  const size_t need = paged_attention_workspace_bytes(batch, n_heads, n_kv_heads, head_dim, max_pages);
+  if (need == 0 || num_pages < 1)
+    return fail(W4_EINVAL, "paged_attention_decode: unsupported shape batch=%d heads=%d/%d "
+                "head_dim=%d max_pages=%d num_pages=%d", batch, n_heads, n_kv_heads, head_dim,
+                max_pages, num_pages);
+  if (ws_bytes < need)
+    return fail(W4_EINVAL, "paged_attention_decode: workspace %zu < %zu bytes", ws_bytes, need);
+  const void* ptrs[] = {q, k_pool, v_pool, page_tables, ctx_lens, workspace, out};
+  for (const void* p : ptrs)
+    if (!aligned256(p)) return fail(W4_EALIGN, "paged_attention_decode: pointer not 256-byte aligned");
+  size_t poff;
+  int max_splits, pps;
+  attn_ws_layout(batch, n_heads, n_kv_heads, head_dim, max_pages, &poff, &max_splits, &pps);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  // counters start at zero; a small fill kernel (no memset node) keeps the
+  // call safe inside a caller's graph capture
+  W4_LAUNCH(launch_fill_u32(reinterpret_cast<uint32_t*>(ws), (size_t)batch * n_kv_heads + 1, 0u, s));
+  AttnArgs at{};
+  at.q = q;
+  at.q_stride = n_heads * head_dim;
+  at.k_pool = static_cast<const uint16_t*>(k_pool);
+  at.v_pool = static_cast<const uint16_t*>(v_pool);
+  at.page_tables = page_tables;
+  at.ctx_lens = ctx_lens;
+  at.batch = batch;
+  at.max_pages = max_pages;
+  at.num_pages = num_pages;
+  at.n_heads = n_heads;
+  at.n_kv_heads = n_kv_heads;
+  at.pages_per_split = pps;
+  at.max_splits = max_splits;
+  at.partials = reinterpret_cast<float*>(ws + poff);
+  at.counters = reinterpret_cast<uint32_t*>(ws);
+  at.out = out;
+  at.out_stride = n_heads * head_dim;
+  at.err = reinterpret_cast<uint32_t*>(ws) + (size_t)batch * n_kv_heads;
+  W4_LAUNCH(launch_attention(at, head_dim, n_heads / n_kv_heads, s));
+  return W4_OK;
+}
+
+// ------------------------------------------------------ per-operation access
+
+W4_EXPORT int w4_model_stage(w4_model* m, const int32_t* tokens, const int32_t* positions,
+                             const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                             void* stream) {
+  clear_error();
+  int rc = check_model(m, batch);
+  if (rc) return rc;
+  if (!positions || !page_tables || !ctx_lens) return fail(W4_EINVAL, "w4_model_stage: null pointer");
+  rc = validate_inputs(m, tokens, positions, page_tables, ctx_lens, batch);
+  if (rc) return rc;
+  return stage_inputs(m, tokens, positions, page_tables, ctx_lens, batch,
+                      static_cast<hipStream_t>(stream));
+}
+
+W4_EXPORT int w4_model_run_op(w4_model* m, int32_t op, int32_t layer, int32_t batch,
+                              uint16_t* logits, void* stream) {
+  clear_error();
+  int rc = check_model(m, batch);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* x = m->at<uint16_t>(m->L.x);
+  if (op == W4_OP_EMBED) {
+    if (!m->weights.embed) return fail(W4_EINVAL, "w4_model_run_op: model has no embedding");
+    W4_LAUNCH(launch_embed(staged(m).tokens, m->weights.embed, m->cfg.vocab, m->cfg.hidden, x,
+                           batch, m->at<uint32_t>(m->L.err), s));
+    return W4_OK;
+  }
+  if (op == W4_OP_LM_HEAD) {
+    if (!m->weights.lm_head || !m->weights.final_norm || !logits)
+      return fail(W4_EINVAL, "w4_model_run_op: no lm_head / final norm / logits");
+    if (!aligned256(logits)) return fail(W4_EALIGN, "w4_model_run_op: logits not 256-byte aligned");
+    return enqueue_lm_head(m, x, batch, logits, s);
+  }
+  if (layer < 0 || layer >= m->cfg.n_layers)
+    return fail(W4_EINVAL, "w4_model_run_op: layer %d outside [0, %d)", layer, m->cfg.n_layers);
+  return enqueue_op(m, op, layer, x, x, staged(m), batch, s);
+}
+
+W4_EXPORT void* w4_model_buffer(w4_model* m, int32_t which, int32_t* row_stride) {
+  if (!m) return nullptr;
+  const WsLayout& L = m->L;
+  const w4_config& c = m->cfg;
+  size_t off;
+  int stride;
+  switch (which) {
+    case W4_BUF_X: off = L.x; stride = c.hidden; break;
+    case W4_BUF_Q: off = L.q; stride = c.n_heads * c.head_dim; break;
+    case W4_BUF_O: off = L.o; stride = L.o_stride; break;
+    case W4_BUF_H: off = L.h; stride = L.h_stride; break;
+    case W4_BUF_XN: off = L.xn; stride = L.xn_stride; break;
+    default: return nullptr;
+  }
+  if (row_stride) *row_stride = stride;
+  return m->ws + off;
+}

@@ -1,0 +1,135 @@
+// Internal declarations shared by the host runtime and the HIP kernels of
+// libw4a16. Nothing here is part of the C ABI (include/w4a16.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "w4a16.h"
+
+#define W4_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace w4 {
+
+// ----------------------------------------------------------------- errors
+// Sets the thread-local message returned by w4_last_error and returns code.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+#define W4_HIP(call)                                                                     \
+  do {                                                                                   \
+    hipError_t e_ = (call);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return ::w4::fail(W4_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));         \
+  } while (0)
+
+inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+constexpr int kPage = 16;       // tokens per KV page
+constexpr int kGroup = 128;     // input columns per INT4 scale group
+constexpr int kTileRows = 16;   // rows per packed tile
+
+// ----------------------------------------------------------- packed sizes
+inline int w4_tiles(int n) { return ceil_div(n, kTileRows); }
+inline int w4_groups(int k) { return ceil_div(k, kGroup); }
+inline size_t w4_nibble_bytes(int n, int k) { return (size_t)w4_tiles(n) * w4_groups(k) * 1024; }
+
+// --------------------------------------------------------- kernel arguments
+enum Epi : int {
+  EPI_STORE = 0,  // y[row] = fp16(acc)
+  EPI_RESID = 1,  // y[row] = fp16(resid[row] + acc)           (residual add)
+  EPI_SILU = 2,   // y[8t+i] = fp16(silu(acc_gate) * acc_up)    (GATE_UP role)
+  EPI_QKV = 3     // RoPE on q/k, q -> q_out, k/v -> KV pages    (QKV role)
+};
+
+// Everything the QKV epilogue needs: RoPE at the token's position and the
+// store of its K/V into the layer's pages.
+struct QkvEpilogue {
+  uint16_t* q_out;            // [B][q_stride] fp16, q heads in logical order
+  int32_t q_stride;
+  uint16_t* k_pool;           // [P][Hkv][16][D]
+  uint16_t* v_pool;
+  const uint16_t* bias;       // fp16 [(Hq+2Hkv)D] logical order, or nullptr
+  const int32_t* positions;   // device [B]
+  const int32_t* page_tables; // device [B][max_pages]
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t n_heads, n_kv_heads, head_dim;
+  float rope_base;
+  uint32_t* err;              // device error counter
+};
+
+struct GemvArgs {
+  const uint8_t* w;       // packed weights (nibble section, then scales)
+  int32_t n, k;           // logical rows / columns
+  int32_t tiles, groups;  // ceil(n/16), ceil(k/128)
+  const uint16_t* x;      // input fp16 [B][x_stride]
+  int32_t x_stride;
+  const uint16_t* gamma;  // RMSNorm weight applied to x first (batch-1 kernel), or nullptr
+  float eps;
+  uint16_t* y;            // output fp16 [B][y_stride]
+  int32_t y_stride;
+  const uint16_t* resid;  // EPI_RESID: residual input [B][y_stride] (may alias y)
+  uint16_t* xn_out;       // batch-1 kernel: workgroup 0 also stores the normalised x here, or nullptr
+  int32_t batch;
+  QkvEpilogue qkv;
+};
+
+struct F16GemvArgs {
+  const uint8_t* w;       // pack_weights_f16 layout
+  int32_t n, k;
+  int32_t tiles, cblocks; // ceil(n/16), ceil(k/32)
+  const uint16_t* x;
+  int32_t x_stride;
+  const uint16_t* gamma;  // optional RMSNorm (batch-1 kernel)
+  float eps;
+  uint16_t* y;
+  int32_t y_stride;
+  uint16_t* xn_out;       // batch-1 kernel: workgroup 0 also stores the normalised x here, or nullptr
+  int32_t batch;
+};
+
+struct AttnArgs {
+  const uint16_t* q;          // [B][q_stride], heads of D values
+  int32_t q_stride;
+  const uint16_t* k_pool;     // [P][Hkv][16][D]
+  const uint16_t* v_pool;
+  const int32_t* page_tables; // [B][max_pages]
+  const int32_t* ctx_lens;    // [B]
+  int32_t batch;
+  int32_t max_pages, num_pages;
+  int32_t n_heads, n_kv_heads;
+  int32_t pages_per_split, max_splits;
+  float* partials;            // [B][Hkv][max_splits][GQ][D + 2]
+  uint32_t* counters;         // [B][Hkv], zero between launches
+  uint16_t* out;              // [B][out_stride]
+  int32_t out_stride;
+  uint32_t* err;
+};
+
+// Launchers (return hipGetLastError of the launch).
+hipError_t launch_w4_gemv(int epi, const GemvArgs& a, hipStream_t s);
+hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16_t* gamma,
+                               float eps, int32_t k, uint16_t* y, int32_t y_stride,
+                               int32_t batch, hipStream_t s);
+hipError_t launch_embed(const int32_t* tokens, const uint16_t* table, int32_t vocab,
+                        int32_t hidden, uint16_t* x, int32_t batch, uint32_t* err,
+                        hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t s);
+bool attention_supported(int head_dim, int group);
+
+// Pages per attention split for a batch / context size: enough workgroups to
+// cover the chip, each split at least 4 pages (one per wavefront).
+int attention_pages_per_split(int batch, int n_kv_heads, int max_pages);
+inline size_t attention_partial_floats(int batch, int n_kv_heads, int max_splits, int group,
+                                       int head_dim) {
+  return (size_t)batch * n_kv_heads * max_splits * group * (head_dim + 2);
+}
+
+}  // namespace w4
