@@ -1,0 +1,252 @@
+"""Benchmark of the W4A16 paged-KV decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload step_b1]
+
+Default workload: the full 28-layer Qwen2.5-7B-shape decode step (random-init
+W4A16 weights, fp16 lm_head), batch 1, 2048-token context. One step = one
+decode_step over all layers + lm_head for the batch, inputs already resident
+in HBM. Prints one JSON line: ms/token, tokens/s, effective HBM GB/s against
+the 8 TB/s peak, the roofline of the dominant kernel and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+METRIC = "decode ms/token + effective HBM GB/s (% of peak), Qwen2.5-7B-shape W4A16"
+
+
+# ------------------------------------------------------------------ byte model
+
+def w4_bytes(n, k):
+    return n * k // 2 + n * ((k + 127) // 128) * 2
+
+
+def op_bytes(sh, batch, ctx_lens):
+    """Algorithmic HBM bytes of each operation type for one step (all layers):
+    weights read once, activations, KV read and written."""
+    H, F, D, Hq, Hkv, V = sh.hidden, sh.ffn, sh.head_dim, sh.n_heads, sh.n_kv_heads, sh.vocab
+    L, B = sh.n_layers, batch
+    qkv_n = (Hq + 2 * Hkv) * D
+    kv_tok = 2 * Hkv * D * 2                     # K and V bytes of one token, one layer
+    per = {
+        "embed": B * H * 2 * 2,
+        "qkv": L * (w4_bytes(qkv_n, H) + H * 2 + B * (H * 2 + Hq * D * 2 + kv_tok)),
+        "attn": L * (int(np.sum(ctx_lens)) * kv_tok + B * 2 * Hq * D * 2),
+        "oproj": L * (w4_bytes(H, Hq * D) + B * (Hq * D * 2 + 2 * H * 2)),
+        "gate_up": L * (w4_bytes(2 * F, H) + H * 2 + B * (H * 2 + F * 2)),
+        "down": L * (w4_bytes(H, F) + B * (F * 2 + 2 * H * 2)),
+        "lm_head": V * H * 2 + H * 2 + B * (H * 2 + V * 2),
+    }
+    return per
+
+
+def launches_per_step(name, sh):
+    return 1 if name in ("embed", "lm_head") else sh.n_layers
+
+
+# ------------------------------------------------------------------ helpers
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "w4a16_paged_kv_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, digest):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle as it stands, on host cores: whole decoder layers of the same
+    workload (weights already generated) plus a slice of the lm_head rows,
+    scaled to one full step."""
+    from threadpoolctl import threadpool_info
+    from oracle import decode as od
+    from oracle import runs
+    import workloads as wl
+    sh = w.shape
+    x = wl.embedding_rows(w.workload_id, sh, w.tokens()).astype(np.float64)
+    layer_s = []
+    t_all = time.perf_counter()
+    l = 0
+    while l < sh.n_layers and (not layer_s or time.perf_counter() - t_all < budget_s * 0.7):
+        lw = w.layer(l)
+        kp, vp = (a.astype(np.float64) for a in w.kv(l))
+        t0 = time.perf_counter()
+        x, _, _ = runs.layer_batch(w, l, x, pools=(kp, vp), weights=lw)
+        layer_s.append(time.perf_counter() - t0)
+        l += 1
+    rows = np.arange(min(sh.vocab, wl.ROW_CHUNK))
+    blk = wl.lm_head_chunk(w.workload_id, sh, 0)
+    gamma = w.final_norm()
+    t0 = time.perf_counter()
+    for b in range(w.batch):
+        od.lm_head(x[b], gamma, blk, sh.eps)
+    lm_s = (time.perf_counter() - t0) * sh.vocab / len(rows)
+    step_s = float(np.mean(layer_s)) * sh.n_layers + lm_s
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(step_s * 1e3 / w.batch, 1), "unit": "ms/token", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(layer_s)} of {sh.n_layers} decoder layers (float64 oracle, batch {w.batch}, "
+                      f"ctx {int(w.ctx_lens.max())}) + {len(rows)} of {sh.vocab} lm_head rows, scaled to one "
+                      f"step; {sum(layer_s) + lm_s * len(rows) / sh.vocab:.1f} s of CPU work"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="step_b1", choices=["step_b1", "step_b16"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--op-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step here is "
+              "single-GPU, see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w4a16_paged_kv_amd as w4
+    import workloads as wl
+    from workloads.device import DeviceModel
+
+    w = wl.WORKLOADS[args.workload]()
+    sh, B = w.shape, w.batch
+    t0 = time.time()
+    print(f"[bench] building {w.name} on the GPU ...", file=sys.stderr, flush=True)
+    dm = DeviceModel(w, progress=lambda l: print(f"[bench]   layer {l} uploaded", file=sys.stderr, flush=True)
+                     if l % 7 == 6 else None)
+    print(f"[bench] built in {time.time() - t0:.0f} s", file=sys.stderr, flush=True)
+    m = dm.model
+    tokens, pos, pt, ctx = dm.step_inputs()
+    dev = [torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda() for a in (tokens, pos, pt, ctx)]
+    logits = torch.empty((B, sh.vocab), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, iters):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters          # ms
+
+    # ---- the step: hipGraph replay, device-resident inputs
+    m.w4_set_graph(True)
+    step = lambda: m.decode_step_device(*dev, logits)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ms = timed(step, args.steps)
+    wall = time.perf_counter() - t_wall
+    assert m.w4_device_errors() == 0
+    # host-array inputs (includes the staging copies) and eager launches, for context
+    host_ms = timed(lambda: m.decode_step(tokens, pos, pt, ctx, logits), max(10, args.steps // 4))
+    m.w4_set_graph(False)
+    eager_ms = timed(lambda: m.decode_step_device(*dev, logits), max(10, args.steps // 4))
+    m.w4_set_graph(True)
+
+    per = op_bytes(sh, B, ctx)
+    step_bytes = sum(per.values())
+
+    # ---- per-operation timing: each op type's launches of one step, captured
+    # in a graph and replayed (same kernels and arguments as inside the step)
+    m.w4_model_stage(tokens, pos, pt, ctx)
+    ops = {"embed": (w4.OP_EMBED, [0]), "qkv": (w4.OP_QKV, range(sh.n_layers)),
+           "attn": (w4.OP_ATTN, range(sh.n_layers)), "oproj": (w4.OP_OPROJ, range(sh.n_layers)),
+           "gate_up": (w4.OP_GATE_UP, range(sh.n_layers)), "down": (w4.OP_DOWN, range(sh.n_layers)),
+           "lm_head": (w4.OP_LM_HEAD, [0])}
+    op_ms = {}
+    for name, (op, layers) in ops.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in layers:
+                m.w4_model_run_op(op, l, B, logits)
+        g.replay()
+        op_ms[name] = timed(g.replay, args.op_reps) / len(layers)     # per launch
+        del g
+    shares = {n: op_ms[n] * launches_per_step(n, sh) for n in op_ms}
+    dom = max(shares, key=shares.get)
+    dom_bytes = per[dom] / launches_per_step(dom, sh)
+    kernels = {"qkv": "gemv.hip", "oproj": "gemv.hip", "gate_up": "gemv.hip", "down": "gemv.hip",
+               "lm_head": "gemv.hip", "embed": "gemv.hip", "attn": "attention.hip"}
+    digest = source_digest(kernels[dom], "w4_internal.h")
+    achieved = dom_bytes / (op_ms[dom] * 1e-3)
+
+    cpu = None if args.no_cpu else cpu_baseline(w)
+
+    tok_s = B * 1e3 / ms
+    out = {
+        "metric": METRIC,
+        "value": round(ms / B, 4),
+        "unit": "ms/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded random-init weights and KV, no checkpoint)",
+        "config": {"workload": w.name, "layers": sh.n_layers, "hidden": sh.hidden, "heads": sh.n_heads,
+                   "kv_heads": sh.n_kv_heads, "head_dim": sh.head_dim, "ffn": sh.ffn, "vocab": sh.vocab,
+                   "batch": B, "ctx": [int(c) for c in ctx] if B <= 4 else
+                   {"min": int(ctx.min()), "max": int(ctx.max()), "sum": int(ctx.sum())},
+                   "weights": "int4 g128 symmetric, fp16 lm_head", "graph": True, "inputs": "device"},
+        "tokens_per_s": round(tok_s, 1),
+        "effective_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "pct_of_peak": round(100 * step_bytes / (ms * 1e-3) / PEAK_HBM, 2),
+        "bytes_per_step": int(step_bytes),
+        "ms_per_step_host_inputs": round(host_ms, 4),
+        "ms_per_step_eager": round(eager_ms, 4),
+        "wall_s_timed": round(wall, 3),
+        "ops": {n: {"us_per_launch": round(op_ms[n] * 1e3, 2), "launches": launches_per_step(n, sh),
+                    "GBps": round(per[n] / launches_per_step(n, sh) / (op_ms[n] * 1e-3) / 1e9, 1),
+                    "share_of_step": round(shares[n] / ms, 3)} for n in op_ms},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved / 1e9, 1),
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
+                     "traffic": read_traffic(dom, digest), "bytes_per_launch": int(dom_bytes),
+                     "us_per_launch": round(op_ms[dom] * 1e3, 2), "source_digest": digest},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

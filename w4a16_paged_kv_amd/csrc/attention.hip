@@ -39,6 +39,14 @@ __device__ __forceinline__ float dpp_xor2(float v) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Device-scope relaxed accesses: coherent across the XCDs' L2 caches.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int D, int GQ>
 __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
@@ -213,37 +221,65 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
         O += f * s_o[w][h][d];
       }
     }
-    part[h * (D + 2) + d] = O;
+    st_agent(&part[h * (D + 2) + d], O);
     if (d == 0) {
-      part[h * (D + 2) + D] = M;
-      part[h * (D + 2) + D + 1] = L;
+      st_agent(&part[h * (D + 2) + D], M);
+      st_agent(&part[h * (D + 2) + D + 1], L);
     }
   }
-  // the last split to arrive merges (log-sum-exp over splits)
-  __threadfence();
+  // The last split to arrive merges (log-sum-exp over splits). Partials move
+  // between workgroups, possibly on different XCDs, through device-scope
+  // (coherent) stores and loads, so no L2 writeback or invalidate is needed:
+  // each workgroup waits for its stores to complete before it counts itself.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   uint32_t* counter = a.counters + (size_t)b * a.n_kv_heads + kvh;
-  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1u) == (uint32_t)(nsplit - 1);
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(nsplit - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  // merge weights per (head, split): w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'
   const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * (D + 2);
+  float* s_w = &s_o[0][0][0];       // reuse: [GQ][nsplit] (nsplit <= 128 <= 2 D)
+  float* s_lm = s_w + GQ * nsplit;  //        [GQ][nsplit]
+  for (int idx = threadIdx.x; idx < GQ * nsplit; idx += 256) {
+    const int h = idx / nsplit, sp = idx % nsplit;
+    s_w[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D]);
+    s_lm[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D + 1]);
+  }
+  __syncthreads();
+  if (threadIdx.x < GQ) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_w[h * nsplit + sp]);
+    float L = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float f = M == -INFINITY ? 0.f : exp2f(s_w[h * nsplit + sp] - M);
+      L += f * s_lm[h * nsplit + sp];
+      s_w[h * nsplit + sp] = f;
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) s_w[h * nsplit + sp] *= inv;
+  }
+  __syncthreads();
   for (int idx = threadIdx.x; idx < GQ * D; idx += 256) {
     const int h = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, pb[((size_t)sp * GQ + h) * (D + 2) + D]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float* ps = pb + ((size_t)sp * GQ + h) * (D + 2);
-        const float f = exp2f(ps[D] - M);
-        L += f * ps[D + 1];
-        O += f * ps[d];
-      }
+    const float* ps = pb + (size_t)h * (D + 2) + d;
+    const float* wh = s_w + h * nsplit;
+    float O = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= nsplit; sp += 8) {   // eight independent loads in flight
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ld_agent(ps + (size_t)(sp + u) * GQ * (D + 2));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) O = fmaf(wh[sp + u], v[u], O);
     }
-    out[h * D + d] = f2h_a(L > 0.f ? O / L : 0.f);
+    for (; sp < nsplit; ++sp) O = fmaf(wh[sp], ld_agent(ps + (size_t)sp * GQ * (D + 2)), O);
+    out[h * D + d] = f2h_a(O);
   }
-  if (threadIdx.x == 0) *counter = 0u;
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 bool attention_supported(int head_dim, int group) {
@@ -256,6 +292,8 @@ int attention_pages_per_split(int batch, int n_kv_heads, int max_pages) {
   long pps = (units + 4095) / 4096;
   int p = 4;
   while (p < pps && p < 64) p <<= 1;
+  // the merge keeps two floats per (head, split) in LDS: at most 128 splits
+  while ((max_pages + p - 1) / p > 128) p <<= 1;
   return p;
 }
 

@@ -60,10 +60,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Copies x[0..k) (fp16, k % 8 == 0) into LDS xs[0..kpad), zero padded, and if
 // gamma is given replaces it by fp16(x * rsqrt(mean(x^2) + eps) * gamma)
-// (RMSNorm, kept in FP16). red needs NT/64 floats. Ends with a barrier.
-template <int NT>
+// (RMSNorm, kept in FP16). NT threads take part; red needs NT/64 floats.
+// Ends with a barrier.
 __device__ void stage_x(const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma,
-                        float eps, int k, int kpad, uint16_t* xs, float* red) {
+                        float eps, int k, int kpad, uint16_t* xs, float* red, const int NT) {
   const int tid = threadIdx.x;
   float ss = 0.f;
   for (int i = tid * 8; i < kpad; i += NT * 8) {
@@ -85,7 +85,6 @@ __device__ void stage_x(const uint16_t* __restrict__ x, const uint16_t* __restri
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     float tot = 0.f;
-#pragma unroll
     for (int w = 0; w < NT / 64; ++w) tot += red[w];
     const float rs = 1.0f / sqrtf(tot / (float)k + eps);
     for (int i = tid * 8; i < k; i += NT * 8) {
@@ -106,8 +105,7 @@ __device__ void stage_x(const uint16_t* __restrict__ x, const uint16_t* __restri
 }
 
 // Copies the staged (normalised) activations back to global memory.
-template <int NT>
-__device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* dst) {
+__device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* dst, const int NT) {
   for (int i = threadIdx.x * 8; i < k; i += NT * 8)
     *reinterpret_cast<u4_t*>(dst + i) = *reinterpret_cast<const u4_t*>(xs + i);
 }
@@ -191,71 +189,186 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i,
 }
 
 // ------------------------------------------------------------ batch 1, VALU
+// A workgroup of WAVES wavefronts covers WAVES/S tiles; the S wavefronts of a
+// tile take its 128-column groups round-robin (K split inside the workgroup),
+// so small matrices still put thousands of wavefronts on the chip and large
+// ones keep the activation prologue amortised over several tiles. Each
+// wavefront streams its blocks U at a time with the next U loads in flight.
 
-constexpr int kUnroll = 8;  // blocks in flight per wavefront
+constexpr int kUnroll = 4;  // blocks per batch; two batches in flight
 
-template <int EPI, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void w4_gemv_b1_kernel(GemvArgs a) {
+// A constant held in a VGPR, so v_and_or_b32 can pair it with an SGPR operand.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+// Sum over one lane's 32 columns of a block, exact dequant. For word j
+// (columns c = 8j..8j+7): w & 0x000F000F holds columns c, c+1 as 1024 + u;
+// w & 0x00F000F0 holds c+2, c+3 as 1024 + 16u (still exact: 16u < 1024), and
+// the same two masks of w >> 8 give c+4, c+5 and c+6, c+7. Subtracting 1032
+// (resp. 1152) leaves q (resp. 16 q) exactly; the 16 q partial sums are
+// scaled by 1/16 at the end. Four independent dot2 chains.
+__device__ __forceinline__ float dot_block_b1(const u4_t w, const uint16_t* __restrict__ xl,
+                                              uint32_t mlo, uint32_t mhi) {
+  const u4_t* xp = reinterpret_cast<const u4_t*>(xl);
+  const h2_t b1 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2_t b16 = {(_Float16)1152.0f, (_Float16)1152.0f};
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u4_t xv = xp[j];
+    const uint32_t w0 = w[j], w8 = w[j] >> 8;
+    s0 = __builtin_amdgcn_fdot2(as_h2((w0 & mlo) | 0x64006400u) - b1, as_h2(xv[0]), s0, false);
+    s1 = __builtin_amdgcn_fdot2(as_h2((w0 & mhi) | 0x64006400u) - b16, as_h2(xv[1]), s1, false);
+    s2 = __builtin_amdgcn_fdot2(as_h2((w8 & mlo) | 0x64006400u) - b1, as_h2(xv[2]), s2, false);
+    s3 = __builtin_amdgcn_fdot2(as_h2((w8 & mhi) | 0x64006400u) - b16, as_h2(xv[3]), s3, false);
+  }
+  return (s0 + s2) + (s1 + s3) * 0.0625f;
+}
+
+// Activation (and RMSNorm weight) chunks, 16 bytes per thread, loaded before
+// the weight prefetch and held in registers: the vector-memory counter is in
+// order, so the prologue then waits for these loads alone, not for the weight
+// blocks issued after them. The launcher guarantees kpad <= kXChunks * 8 * NT.
+constexpr int kXChunks = 4;
+
+// Stages x into LDS from xr[c] = x[(tid + c NT) 8 .. +8) and, if gamma is
+// given, replaces it by fp16(x * rsqrt(mean(x^2) + eps) * gamma) with
+// gr[c] = gamma[same range]. Ends with a barrier.
+__device__ void stage_x_held(const u4_t* xr, const u4_t* gr, bool norm, float eps, int k, int kpad,
+                             uint16_t* xs, float* red, const int NT) {
+  const int tid = threadIdx.x;
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kXChunks; ++c) {
+    const int i = (tid + c * NT) * 8;
+    if (i < kpad) {
+      *reinterpret_cast<u4_t*>(xs + i) = xr[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const h2_t h = as_h2(xr[c][e]);
+        ss = fmaf((float)h[0], (float)h[0], ss);
+        ss = fmaf((float)h[1], (float)h[1], ss);
+      }
+    }
+  }
+  if (norm) {
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < NT / 64; ++w) tot += red[w];
+    const float rs = 1.0f / sqrtf(tot / (float)k + eps);
+#pragma unroll
+    for (int c = 0; c < kXChunks; ++c) {
+      const int i = (tid + c * NT) * 8;
+      if (i < k) {
+        u4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2_t hv = as_h2(xr[c][e]), hg = as_h2(gr[c][e]);
+          h2_t r;
+          r[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
+          r[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
+          v[e] = __builtin_bit_cast(uint32_t, r);
+        }
+        *reinterpret_cast<u4_t*>(xs + i) = v;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int EPI, int S>
+__global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvArgs a) {
+  // S wavefronts per tile, TW tiles per workgroup
+  constexpr int TW = S < 4 ? 4 / S : 1;
+  constexpr int WAVES = S * TW;
   constexpr int NT = WAVES * 64;
   extern __shared__ __align__(16) uint8_t smem[];
   const int G = a.groups;
   const int kpad = G * kGroup;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);  // WAVES*16 + 16 + WAVES
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + (size_t)t * G * 64 + lane;
+  float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);  // [WAVES][16]
+  float* vals = red + WAVES * 16;                                   // [TW][16]
+  float* nred = vals + TW * 16;                                     // [WAVES]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x * TW + wave / S;  // this wavefront's tile
+  const int ks = wave % S;                   // first group; then every S-th
+  const bool live = t < a.tiles;
+  const int ng = live ? (G - ks + S - 1) / S : 0;  // groups of this wavefront
+  const int last = ng > 0 ? ng - 1 : 0;
+  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + ((size_t)(live ? t : 0) * G + ks) * 64 + lane;
   const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024) +
-                       (size_t)t * G * 16 + (lane & 15);
+                       ((size_t)(live ? t : 0) * G + ks) * 16 + (lane & 15);
+  const uint32_t mlo = vgpr_const(0x000F000Fu), mhi = vgpr_const(0x00F000F0u);
 
-  // weight loads of the first batch go out before the activation prologue
-  u4_t cur[kUnroll];
-  float csc[kUnroll];
+  // 1. activations (and RMSNorm weights) first
+  u4_t xr[kXChunks], gr[kXChunks];
+  const bool norm = a.gamma != nullptr;
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int g = wave + u * WAVES;
-    cur[u] = g < G ? __builtin_nontemporal_load(wb + (size_t)g * 64) : (u4_t){0u, 0u, 0u, 0u};
-    csc[u] = g < G ? h2f(sb[(size_t)g * 16]) : 0.f;
+  for (int c = 0; c < kXChunks; ++c) {
+    const int i = (threadIdx.x + c * NT) * 8;
+    const bool in = i < a.k;
+    xr[c] = in ? *reinterpret_cast<const u4_t*>(a.x + i) : (u4_t){0u, 0u, 0u, 0u};
+    gr[c] = (in && norm) ? *reinterpret_cast<const u4_t*>(a.gamma + i) : (u4_t){0u, 0u, 0u, 0u};
   }
-  stage_x<NT>(a.x, a.gamma, a.eps, a.k, kpad, xs, red + WAVES * 16 + 16);
-  if (a.xn_out && blockIdx.x == 0) store_xs<NT>(xs, a.k, a.xn_out);
-
-  const uint16_t* xl = xs + 32 * (lane >> 4);
+  // 2. weight blocks, two batches of kUnroll in flight. Loads are issued
+  // unconditionally (past the wavefront's last group they re-read that block)
+  // so the compiler's wait counts stay exact; scales stay fp16 until used.
+  u4_t bufA[kUnroll], bufB[kUnroll];
+  uint32_t scA[kUnroll], scB[kUnroll];  // one scale per register: no packing waits
+  auto load = [&](u4_t* buf, uint32_t* sc, int i0) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = min(i0 + u, last);
+      buf[u] = __builtin_nontemporal_load(wb + (size_t)i * S * 64);
+      sc[u] = sb[(size_t)i * S * 16];
+    }
+  };
+  const uint16_t* xl = xs + 32 * (lane >> 4) + ks * kGroup;
   float acc = 0.f;
-  for (int base = wave; base < G; base += kUnroll * WAVES) {
-    u4_t nxt[kUnroll];
-    float nsc[kUnroll];
+  auto compute = [&](const u4_t* buf, const uint32_t* sc, int i0) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int g = base + (kUnroll + u) * WAVES;
-      nxt[u] = g < G ? __builtin_nontemporal_load(wb + (size_t)g * 64) : (u4_t){0u, 0u, 0u, 0u};
-      nsc[u] = g < G ? h2f(sb[(size_t)g * 16]) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int g = base + u * WAVES;
-      if (g < G) acc = fmaf(dot_block(cur[u], xl + g * kGroup), csc[u], acc);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      cur[u] = nxt[u];
-      csc[u] = nsc[u];
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      if (i0 + u < ng)
+        acc = fmaf(dot_block_b1(buf[u], xl + (size_t)(i0 + u) * S * kGroup, mlo, mhi),
+                   h2f((uint16_t)sc[u]), acc);
+  };
+  load(bufA, scA, 0);
+  // 3. activation prologue (waits for the activation loads only)
+  stage_x_held(xr, gr, norm, a.eps, a.k, kpad, xs, nred, NT);
+  if (a.xn_out && blockIdx.x == 0) store_xs(xs, a.k, a.xn_out, NT);
+  // 4. stream
+  for (int i = 0; i < ng; i += 2 * kUnroll) {
+    load(bufB, scB, i + kUnroll);
+    compute(bufA, scA, i);
+    if (i + kUnroll >= ng) break;
+    load(bufA, scA, i + 2 * kUnroll);
+    compute(bufB, scB, i + kUnroll);
   }
   // lanes l, l+16, l+32, l+48 hold the same row
   acc += __shfl_xor(acc, 16);
   acc += __shfl_xor(acc, 32);
   if (lane < 16) red[wave * 16 + lane] = acc;
   __syncthreads();
-  float* vals = red + WAVES * 16;
-  if (threadIdx.x < 16) {
+  if (threadIdx.x < TW * 16) {
+    const int tl = threadIdx.x / 16, r = threadIdx.x % 16;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[w * 16 + threadIdx.x];
-    vals[threadIdx.x] = v;
+    for (int k = 0; k < S; ++k) v += red[(tl * S + k) * 16 + r];
+    vals[tl * 16 + r] = v;
   }
   __syncthreads();
-  if (threadIdx.x < epi_items<EPI>()) epilogue<EPI>(a, 0, t, threadIdx.x, vals);
+  constexpr int per = epi_items<EPI>();
+  if (threadIdx.x < TW * per) {
+    const int tl = threadIdx.x / per;
+    const int tt = blockIdx.x * TW + tl;
+    if (tt < a.tiles) epilogue<EPI>(a, 0, tt, threadIdx.x % per, vals + tl * 16);
+  }
 }
 
 // ------------------------------------------------------- batch 2..16, MFMA
@@ -347,8 +460,8 @@ __global__ __launch_bounds__(WAVES * 64) void f16_gemv_b1_kernel(F16GemvArgs a) 
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u)
     cur[u] = (live && u < C) ? __builtin_nontemporal_load(wb + (size_t)u * 64) : (u4_t){0u, 0u, 0u, 0u};
-  stage_x<NT>(a.x, a.gamma, a.eps, a.k, kpad, xs, red);
-  if (a.xn_out && blockIdx.x == 0) store_xs<NT>(xs, a.k, a.xn_out);
+  stage_x(a.x, a.gamma, a.eps, a.k, kpad, xs, red, NT);
+  if (a.xn_out && blockIdx.x == 0) store_xs(xs, a.k, a.xn_out, NT);
   if (!live) return;
   const uint16_t* xl = xs + 8 * (lane >> 4);
   float acc = 0.f;
@@ -459,12 +572,47 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t count, uint32_t value) {
 
 // ---------------------------------------------------------------- launchers
 
+// Batch-1 work split: S wavefronts per tile, each taking every S-th group, and
+// 4/S tiles per workgroup when S < 4. S is the largest choice that keeps every
+// wavefront of the launch resident on the chip at once (about 4K wavefronts)
+// with at least two groups each: then each wavefront streams one long,
+// double-buffered run of blocks and no second, partly empty round of
+// workgroups is needed.
+int w4_gemv_split(int tiles, int groups) {
+  const int opts[] = {16, 8, 7, 4, 3, 2, 1};
+  auto fits = [&](int s) {  // staged activations: kpad <= kXChunks * 8 * threads
+    const int waves = s < 4 ? 4 : s;
+    return groups * kGroup <= kXChunks * 8 * 64 * waves;
+  };
+  for (int s : opts)
+    if ((long)tiles * s <= 4096 && groups >= 2 * s && fits(s)) return s;
+  for (int s : {1, 2, 3, 4, 7, 8, 16})
+    if (fits(s)) return s;
+  return 0;  // activation row longer than one workgroup can stage
+}
+
+template <int EPI, int S>
+static void launch_b1(const GemvArgs& a, hipStream_t s) {
+  constexpr int TW = S < 4 ? 4 / S : 1;
+  constexpr int WAVES = S * TW;
+  const size_t lds = (size_t)a.groups * kGroup * 2 + (WAVES * 16 + TW * 16 + WAVES) * sizeof(float);
+  hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S>), dim3(ceil_div(a.tiles, TW)), dim3(WAVES * 64), lds, s,
+                     a);
+}
+
 template <int EPI>
 static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
   if (a.batch == 1) {
-    constexpr int WAVES = 4;
-    const size_t lds = (size_t)a.groups * kGroup * 2 + (WAVES * 16 + 16 + WAVES) * sizeof(float);
-    hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, WAVES>), dim3(a.tiles), dim3(WAVES * 64), lds, s, a);
+    switch (w4_gemv_split(a.tiles, a.groups)) {
+      case 16: launch_b1<EPI, 16>(a, s); break;
+      case 8: launch_b1<EPI, 8>(a, s); break;
+      case 7: launch_b1<EPI, 7>(a, s); break;
+      case 4: launch_b1<EPI, 4>(a, s); break;
+      case 3: launch_b1<EPI, 3>(a, s); break;
+      case 2: launch_b1<EPI, 2>(a, s); break;
+      case 1: launch_b1<EPI, 1>(a, s); break;
+      default: return hipErrorInvalidValue;
+    }
   } else {
     constexpr int WAVES = 4;
     hipLaunchKernelGGL((w4_gemm_mfma_kernel<EPI, WAVES>), dim3(a.tiles), dim3(WAVES * 64), 0, s, a);
