@@ -26,6 +26,7 @@ namespace w4 {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2_t as_h2a(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 __device__ __forceinline__ uint16_t f2h_a(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
@@ -47,20 +48,28 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time each
+
 template <int D, int GQ>
-__global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(GQ >= 1 && GQ <= 8, "group");
+  constexpr int W = kAttnWaves;
+  constexpr int NT = W * 64;
   constexpr int NI = D / 32;          // 8-column sub-chunks per lane for scores
   constexpr int LD = D / 8;           // lanes per token row for PV (8 columns each)
   constexpr int TPI = 64 / LD;        // token rows per PV load instruction
   constexpr int NTOK = kPage / TPI;   // tokens per lane for PV
-  __shared__ float s_m[4][8], s_l[4][8];
-  __shared__ float s_o[4][GQ][D];
+  __shared__ float s_m[W][8], s_l[W][8];
+  __shared__ __align__(16) float s_pb[W][kPage][8];  // per-wavefront softmax weights [token][head]
+  __shared__ __align__(16) float s_al[W][8];         // per-wavefront rescale factors [head]
+  __shared__ float s_o[W][GQ][D];
+  __shared__ __align__(16) uint16_t s_q[GQ * D];     // the group's query heads
   __shared__ int s_last;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int ctx = a.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * kPage ? a.max_pages * kPage : ctx);
   const int npages = (ctx + kPage - 1) / kPage;
@@ -68,7 +77,7 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
   uint16_t* out = a.out + (size_t)b * a.out_stride + (size_t)kvh * GQ * D;
   if (npages == 0) {  // empty context: zeros
     if (split == 0)
-      for (int i = threadIdx.x; i < GQ * D; i += 256) out[i] = 0;
+      for (int i = threadIdx.x; i < GQ * D; i += NT) out[i] = 0;
     return;
   }
   if (split >= nsplit) return;
@@ -76,14 +85,14 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
   const int p_end = min(npages, p_begin + a.pages_per_split);
   const int32_t* pt = a.page_tables + (size_t)b * a.max_pages;
 
-  // q fragments: lane (tk = lane >> 2, c = lane & 3) covers columns 8c + 32i .. +8
+  // the group's queries go to LDS (read per head per page: registers stay free
+  // for more wavefronts in flight); lane (tk = lane >> 2, c = lane & 3) covers
+  // columns 8c + 32i .. +8 of token tk for the scores
   const int tk = lane >> 2, c = lane & 3;
   const uint16_t* qb = a.q + (size_t)b * a.q_stride + (size_t)kvh * GQ * D;
-  u4_t qf[GQ][NI];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h)
-#pragma unroll
-    for (int i = 0; i < NI; ++i) qf[h][i] = *reinterpret_cast<const u4_t*>(qb + h * D + 8 * c + 32 * i);
+  for (int i = threadIdx.x * 8; i < GQ * D; i += NT * 8)
+    *reinterpret_cast<u4_t*>(&s_q[i]) = *reinterpret_cast<const u4_t*>(qb + i);
+  __syncthreads();
 
   const float scale = kLog2e / sqrtf((float)D);
   const int hA = c, hB = c + 4;            // heads whose softmax state this lane keeps
@@ -97,31 +106,46 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
   const int t0 = lane / LD;                // first PV token row of this lane
   const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
 
-  for (int p = p_begin + wave; p < p_end; p += 4) {
+  // K/V of this wavefront's next page are in flight while it computes the
+  // current one
+  auto page_of = [&](int p, int& valid) {
     int page = pt[p];
     const bool bad = page < 0 || page >= a.num_pages;
     if (bad) {
       if (lane == 0) atomicAdd(a.err, 1u);
       page = 0;
     }
-    const int valid = bad ? 0 : min(kPage, ctx - p * kPage);
+    valid = bad ? 0 : min(kPage, ctx - p * kPage);
+    return page;
+  };
+  u4_t kf[NI], vf[NTOK], kn[NI], vn[NTOK];
+  auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
     const uint16_t* kb = a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice;
     const uint16_t* vb = a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice;
-    u4_t kf[NI], vf[NTOK];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kf[i] = *reinterpret_cast<const u4_t*>(kb + tk * D + 8 * c + 32 * i);
+    for (int i = 0; i < NI; ++i) kk[i] = *reinterpret_cast<const u4_t*>(kb + tk * D + 8 * c + 32 * i);
 #pragma unroll
-    for (int i = 0; i < NTOK; ++i) vf[i] = *reinterpret_cast<const u4_t*>(vb + (t0 + TPI * i) * D + d0);
+    for (int i = 0; i < NTOK; ++i) vv[i] = *reinterpret_cast<const u4_t*>(vb + (t0 + TPI * i) * D + d0);
+  };
+  int valid_next = 0;
+  if (p_begin + wave < p_end) load_kv(page_of(p_begin + wave, valid_next), kf, vf);
+  for (int p = p_begin + wave; p < p_end; p += W) {
+    const int valid = valid_next;
+    if (p + W < p_end) {
+      load_kv(page_of(p + W, valid_next), kn, vn);
+    }
 
-    // scores of token tk for every head of the group
+    // scores of token tk for every head of the group (quad reduction over c)
     float s[GQ];
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+      for (int i = 0; i < NI; ++i) {
+        const u4_t qv = *reinterpret_cast<const u4_t*>(&s_q[h * D + 8 * c + 32 * i]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(as_h2a(qf[h][i][e]), as_h2a(kf[i][e]), acc, false);
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(as_h2a(qv[e]), as_h2a(kf[i][e]), acc, false);
+      }
       acc += dpp_xor1(acc);
       acc += dpp_xor2(acc);
       s[h] = acc * scale;
@@ -136,7 +160,7 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
       sA = -INFINITY;
       sB = -INFINITY;
     }
-    // page maximum over the 16 tokens (lanes sharing c)
+    // page maximum and sum over the 16 tokens (lanes sharing c)
     float pmA = sA, pmB = sB;
 #pragma unroll
     for (int off = 4; off < 64; off <<= 1) {
@@ -158,6 +182,17 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
     lB = lB * alB + sumB;
     mA = nA;
     mB = nB;
+    // broadcast weights and rescale factors to the PV lanes through LDS
+    // (wavefront-private rows; LDS operations of a wavefront stay in order)
+    s_pb[wave][tk][hA] = pA;
+    s_pb[wave][tk][hB] = pB;
+    if (lane < 4) {
+      s_al[wave][hA] = alA;
+      s_al[wave][hB] = alB;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // masked tokens contribute nothing even if their slots hold NaN
     if (valid < kPage) {
@@ -165,15 +200,21 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
       for (int i = 0; i < NTOK; ++i)
         if (t0 + TPI * i >= valid) vf[i] = (u4_t){0u, 0u, 0u, 0u};
     }
+    const f4v al0 = *reinterpret_cast<const f4v*>(&s_al[wave][0]);
+    const f4v al1 = *reinterpret_cast<const f4v*>(&s_al[wave][4]);
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      const int src = h & 3;
-      const float al = __shfl(h < 4 ? alA : alB, src);
+      const float al = h < 4 ? al0[h & 3] : al1[h & 3];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[h][e] *= al;
+    }
 #pragma unroll
-      for (int i = 0; i < NTOK; ++i) {
-        const float pv = __shfl(h < 4 ? pA : pB, 4 * (t0 + TPI * i) + src);
+    for (int i = 0; i < NTOK; ++i) {
+      const f4v p0 = *reinterpret_cast<const f4v*>(&s_pb[wave][t0 + TPI * i][0]);
+      const f4v p1 = *reinterpret_cast<const f4v*>(&s_pb[wave][t0 + TPI * i][4]);
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        const float pv = h < 4 ? p0[h & 3] : p1[h & 3];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const h2_t v2 = as_h2a(vf[i][e]);
@@ -182,6 +223,13 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kf[i] = kn[i];
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) vf[i] = vn[i];
   }
   // reduce o over the lanes holding other token rows of the same columns
 #pragma unroll
@@ -193,10 +241,8 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
   if (lane < 4) {
     s_m[wave][hA] = mA;
     s_l[wave][hA] = lA;
-    if (hB < 8) {
-      s_m[wave][hB] = mB;
-      s_l[wave][hB] = lB;
-    }
+    s_m[wave][hB] = mB;
+    s_l[wave][hB] = lB;
   }
   if (lane < LD)
 #pragma unroll
@@ -205,28 +251,33 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
       for (int e = 0; e < 8; ++e) s_o[wave][h][d0 + e] = o[h][e];
   __syncthreads();
 
-  // combine the four wavefronts into this split's partial
+  // combine the wavefronts: this split's (o, m, l), or the output if one split
   float* part = a.partials + (((size_t)b * a.n_kv_heads + kvh) * a.max_splits + split) * GQ * (D + 2);
-  for (int idx = threadIdx.x; idx < GQ * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < GQ * D; idx += NT) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][h]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float f = exp2f(s_m[w][h] - M);
         L += f * s_l[w][h];
         O += f * s_o[w][h][d];
       }
     }
-    st_agent(&part[h * (D + 2) + d], O);
-    if (d == 0) {
-      st_agent(&part[h * (D + 2) + D], M);
-      st_agent(&part[h * (D + 2) + D + 1], L);
+    if (nsplit == 1) {
+      out[h * D + d] = f2h_a(L > 0.f ? O / L : 0.f);
+    } else {
+      st_agent(&part[h * (D + 2) + d], O);
+      if (d == 0) {
+        st_agent(&part[h * (D + 2) + D], M);
+        st_agent(&part[h * (D + 2) + D + 1], L);
+      }
     }
   }
+  if (nsplit == 1) return;
   // The last split to arrive merges (log-sum-exp over splits). Partials move
   // between workgroups, possibly on different XCDs, through device-scope
   // (coherent) stores and loads, so no L2 writeback or invalidate is needed:
@@ -241,9 +292,9 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
   if (!s_last) return;
   // merge weights per (head, split): w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'
   const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * (D + 2);
-  float* s_w = &s_o[0][0][0];       // reuse: [GQ][nsplit] (nsplit <= 128 <= 2 D)
+  float* s_w = &s_o[0][0][0];       // reuse: [GQ][nsplit] (nsplit <= 128)
   float* s_lm = s_w + GQ * nsplit;  //        [GQ][nsplit]
-  for (int idx = threadIdx.x; idx < GQ * nsplit; idx += 256) {
+  for (int idx = threadIdx.x; idx < GQ * nsplit; idx += NT) {
     const int h = idx / nsplit, sp = idx % nsplit;
     s_w[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D]);
     s_lm[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D + 1]);
@@ -263,18 +314,18 @@ __global__ __launch_bounds__(256) void paged_attn_kernel(AttnArgs a) {
     for (int sp = 0; sp < nsplit; ++sp) s_w[h * nsplit + sp] *= inv;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < GQ * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < GQ * D; idx += NT) {
     const int h = idx / D, d = idx % D;
     const float* ps = pb + (size_t)h * (D + 2) + d;
     const float* wh = s_w + h * nsplit;
     float O = 0.f;
     int sp = 0;
-    for (; sp + 8 <= nsplit; sp += 8) {   // eight independent loads in flight
-      float v[8];
+    for (; sp + 16 <= nsplit; sp += 16) {   // sixteen independent loads in flight
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = ld_agent(ps + (size_t)(sp + u) * GQ * (D + 2));
+      for (int u = 0; u < 16; ++u) v[u] = ld_agent(ps + (size_t)(sp + u) * GQ * (D + 2));
 #pragma unroll
-      for (int u = 0; u < 8; ++u) O = fmaf(wh[sp + u], v[u], O);
+      for (int u = 0; u < 16; ++u) O = fmaf(wh[sp + u], v[u], O);
     }
     for (; sp < nsplit; ++sp) O = fmaf(wh[sp], ld_agent(ps + (size_t)sp * GQ * (D + 2)), O);
     out[h * D + d] = f2h_a(O);
@@ -287,20 +338,22 @@ bool attention_supported(int head_dim, int group) {
                                                  group == 7 || group == 8);
 }
 
+// Pages per split: one page per wavefront until the launch would exceed about
+// 2K workgroups, then up to four; at most 128 splits per sequence (the merge
+// keeps two floats per (head, split) in LDS).
 int attention_pages_per_split(int batch, int n_kv_heads, int max_pages) {
   const long units = (long)batch * n_kv_heads * max_pages;
-  long pps = (units + 4095) / 4096;
-  int p = 4;
-  while (p < pps && p < 64) p <<= 1;
-  // the merge keeps two floats per (head, split) in LDS: at most 128 splits
-  while ((max_pages + p - 1) / p > 128) p <<= 1;
-  return p;
+  int per_wave = 1;
+  while (per_wave < 4 && units / ((long)kAttnWaves * per_wave) > 2048) per_wave *= 2;
+  int pps = kAttnWaves * per_wave;
+  while ((max_pages + pps - 1) / pps > 128) pps *= 2;
+  return pps;
 }
 
 template <int D, int GQ>
 static hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((paged_attn_kernel<D, GQ>), dim3(a.max_splits, a.n_kv_heads, a.batch),
-                     dim3(256), 0, s, a);
+                     dim3(kAttnWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 
