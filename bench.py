@@ -131,6 +131,9 @@ def main():
     ap.add_argument("--workload", default="step_b1", choices=["step_b1", "step_b16"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--op-reps", type=int, default=20)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run three plain device copies of MIB MiB each, so that HBM byte "
+                         "counters taken over this run can be scaled by a copy of known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step here is "
@@ -141,6 +144,17 @@ def main():
     import w4a16_paged_kv_amd as w4
     import workloads as wl
     from workloads.device import DeviceModel
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n // 2, dtype=torch.float16, device="cuda").fill_(1)   # writes n bytes
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)                                              # reads n, writes n
+        torch.cuda.synchronize()
+        print(f"[bench] calibration: fill of {n} bytes, then 3 negating copies of {n} bytes",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     w = wl.WORKLOADS[args.workload]()
     sh, B = w.shape, w.batch

@@ -5,13 +5,12 @@
 // scratch", Architectural decisions and optimizations). lm_head and RMSNorm
 // stay in FP16 (same section).
 //
-// Batch 1 is a bandwidth-bound GEMV and runs on the vector ALUs: every lane
-// expands 32 nibbles of one row to fp16 in registers (OR into the exponent of
-// 1024.0, subtract 1032: exact), takes v_dot2_f32_f16 against the activation
-// pairs staged in LDS, scales the fp32 group sum once, and the four lanes
-// holding a row are reduced across the wavefront at the end.
-// Batches 2..16 turn each projection into a skinny dense contraction and run
-// the same packed blocks through v_mfma_f32_16x16x32_f16.
+// Batch 1 is a bandwidth-bound GEMV. It still runs on the matrix cores: the
+// packed block is laid out as the B operand of v_mfma_f32_16x16x32_f16, a
+// nibble turns into an exact fp16 (a subnormal) with one AND, and the MFMA
+// does the multiply-accumulate that would otherwise cost as many vector
+// instructions as the dequantisation. Batches 2..16 turn each projection
+// into a skinny dense contraction on the same instruction.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -188,7 +187,19 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i,
   }
 }
 
-// ------------------------------------------------------------ batch 1, VALU
+// ------------------------------------------------------------ batch 1, MFMA
+// The 16 bytes a lane holds of a packed block are already the B operand of
+// v_mfma_f32_16x16x32_f16 (weight row l & 15, eight k-slots per lane group
+// l >> 4), so batch 1 runs on the matrix cores too: A carries the activation
+// row (A rows 1..15 are don't-care) and D row 0 comes out in lanes 0..15.
+//
+// Dequantisation stays exact: 0x6400 | u is 1024 + u in fp16 (ulp 1), so
+// OR-ing a nibble pair masked with 0x000F000F into 0x64006400 and
+// subtracting 1032 gives (q, q'); the pair four bits higher (mask 0x00F000F0)
+// gives 16q after subtracting 1152, and the activations paired with those
+// slots are staged divided by 16. One AND-OR and one packed subtract per
+// weight pair; the multiply-accumulate runs on the matrix cores.
+//
 // A workgroup of WAVES wavefronts covers WAVES/S tiles; the S wavefronts of a
 // tile take its 128-column groups round-robin (K split inside the workgroup),
 // so small matrices still put thousands of wavefronts on the chip and large
@@ -197,6 +208,89 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i,
 
 constexpr int kUnroll = 4;  // blocks per batch; two batches in flight
 
+constexpr uint32_t kMaskLo = 0x000F000Fu;  // nibble offsets (0,1) / (4,5) of a word
+constexpr uint32_t kMaskHi = 0x00F000F0u;  // nibble offsets (2,3) / (6,7), as 16u
+
+// Column (0..31, inside a lane group's 32-column chunk) that feeds k-slot
+// 8r + s of MFMA r (0..3) of a block: MFMA r takes words 2(r/2) and
+// 2(r/2) + 1, masked with kMaskLo for even r and kMaskHi for odd r; each word
+// gives the pair (w & M) and ((w >> 8) & M).
+__device__ __forceinline__ constexpr int kslot_column(int r, int s) {
+  return 8 * (2 * (r >> 1) + (s >> 2)) + 2 * (r & 1) + (s & 1) + 4 * ((s >> 1) & 1);
+}
+
+// Stages one activation row for the MFMA path. Thread t owns 32-column chunk
+// t (xr = its columns in natural order, gr = the RMSNorm weights, zero past
+// k): with gamma, the row becomes fp16(x * rsqrt(mean(x^2) + eps) * gamma)
+// (RMSNorm in FP16). Chunk t is written to xs[32t..32t+32) in k-slot order,
+// odd-r slots divided by 16. The natural-order row also goes to xn_out if
+// given. Ends with a barrier. Requires kpad <= 32 * NT.
+__device__ void stage_row_mfma(const u4_t* xr, const u4_t* gr, bool norm, float eps, int k, int kpad,
+                               uint16_t* xs, float* red, uint16_t* xn_out, const int NT) {
+  const int tid = threadIdx.x;
+  const bool has = tid * 32 < kpad;
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const h2_t h = as_h2(xr[p][e]);
+      ss = fmaf((float)h[0], (float)h[0], ss);
+      ss = fmaf((float)h[1], (float)h[1], ss);
+    }
+  float rs = 1.f;
+  if (norm) {
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < NT / 64; ++w) tot += red[w];
+    rs = 1.0f / sqrtf(tot / (float)k + eps);
+  }
+  _Float16 v[32];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const h2_t hv = as_h2(xr[p][e]);
+      if (norm) {
+        const h2_t hg = as_h2(gr[p][e]);
+        v[8 * p + 2 * e] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
+        v[8 * p + 2 * e + 1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
+      } else {
+        v[8 * p + 2 * e] = hv[0];
+        v[8 * p + 2 * e + 1] = hv[1];
+      }
+    }
+  if (xn_out && has) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (tid * 32 + 8 * p < k) {
+        u4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = __builtin_bit_cast(uint32_t, (h2_t){v[8 * p + 2 * e], v[8 * p + 2 * e + 1]});
+        *reinterpret_cast<u4_t*>(xn_out + tid * 32 + 8 * p) = o;
+      }
+  }
+  u4_t o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int s = 0; s < 8; s += 2) {
+      _Float16 h0 = v[kslot_column(r, s)], h1 = v[kslot_column(r, s + 1)];
+      if (r & 1) {
+        h0 = (_Float16)((float)h0 * 0.0625f);
+        h1 = (_Float16)((float)h1 * 0.0625f);
+      }
+      o[r][s / 2] = __builtin_bit_cast(uint32_t, (h2_t){h0, h1});
+    }
+  if (has)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *reinterpret_cast<u4_t*>(xs + tid * 32 + 8 * r) = o[r];
+  __syncthreads();
+}
+
 // A constant held in a VGPR, so v_and_or_b32 can pair it with an SGPR operand.
 __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
   uint32_t r;
@@ -204,81 +298,26 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
   return r;
 }
 
-// Sum over one lane's 32 columns of a block, exact dequant. For word j
-// (columns c = 8j..8j+7): w & 0x000F000F holds columns c, c+1 as 1024 + u;
-// w & 0x00F000F0 holds c+2, c+3 as 1024 + 16u (still exact: 16u < 1024), and
-// the same two masks of w >> 8 give c+4, c+5 and c+6, c+7. Subtracting 1032
-// (resp. 1152) leaves q (resp. 16 q) exactly; the 16 q partial sums are
-// scaled by 1/16 at the end. Four independent dot2 chains.
-__device__ __forceinline__ float dot_block_b1(const u4_t w, const uint16_t* __restrict__ xl,
-                                              uint32_t mlo, uint32_t mhi) {
+// Sum over one block of q * x for weight row lane & 15: d[0] of lanes 0..15
+// after four chained MFMAs over the lane group's staged chunk xl.
+__device__ __forceinline__ float mfma_block_b1(const u4_t w, const uint16_t* __restrict__ xl, uint32_t mlo,
+                                               uint32_t mhi) {
   const u4_t* xp = reinterpret_cast<const u4_t*>(xl);
-  const h2_t b1 = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const h2_t b16 = {(_Float16)1152.0f, (_Float16)1152.0f};
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  f4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const u4_t xv = xp[j];
-    const uint32_t w0 = w[j], w8 = w[j] >> 8;
-    s0 = __builtin_amdgcn_fdot2(as_h2((w0 & mlo) | 0x64006400u) - b1, as_h2(xv[0]), s0, false);
-    s1 = __builtin_amdgcn_fdot2(as_h2((w0 & mhi) | 0x64006400u) - b16, as_h2(xv[1]), s1, false);
-    s2 = __builtin_amdgcn_fdot2(as_h2((w8 & mlo) | 0x64006400u) - b1, as_h2(xv[2]), s2, false);
-    s3 = __builtin_amdgcn_fdot2(as_h2((w8 & mhi) | 0x64006400u) - b16, as_h2(xv[3]), s3, false);
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t m = (r & 1) ? mhi : mlo;
+    const h2_t bias = (r & 1) ? (h2_t){(_Float16)1152.0f, (_Float16)1152.0f}
+                              : (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t w0 = w[2 * (r >> 1)], w1 = w[2 * (r >> 1) + 1];
+    auto q2 = [&](uint32_t v) {
+      return __builtin_bit_cast(uint32_t, as_h2((v & m) | 0x64006400u) - bias);
+    };
+    const u4_t b = {q2(w0), q2(w0 >> 8), q2(w1), q2(w1 >> 8)};
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xp[r]), __builtin_bit_cast(h8_t, b),
+                                               d, 0, 0, 0);
   }
-  return (s0 + s2) + (s1 + s3) * 0.0625f;
-}
-
-// Activation (and RMSNorm weight) chunks, 16 bytes per thread, loaded before
-// the weight prefetch and held in registers: the vector-memory counter is in
-// order, so the prologue then waits for these loads alone, not for the weight
-// blocks issued after them. The launcher guarantees kpad <= kXChunks * 8 * NT.
-constexpr int kXChunks = 4;
-
-// Stages x into LDS from xr[c] = x[(tid + c NT) 8 .. +8) and, if gamma is
-// given, replaces it by fp16(x * rsqrt(mean(x^2) + eps) * gamma) with
-// gr[c] = gamma[same range]. Ends with a barrier.
-__device__ void stage_x_held(const u4_t* xr, const u4_t* gr, bool norm, float eps, int k, int kpad,
-                             uint16_t* xs, float* red, const int NT) {
-  const int tid = threadIdx.x;
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < kXChunks; ++c) {
-    const int i = (tid + c * NT) * 8;
-    if (i < kpad) {
-      *reinterpret_cast<u4_t*>(xs + i) = xr[c];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const h2_t h = as_h2(xr[c][e]);
-        ss = fmaf((float)h[0], (float)h[0], ss);
-        ss = fmaf((float)h[1], (float)h[1], ss);
-      }
-    }
-  }
-  if (norm) {
-    ss = wave_sum(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
-    for (int w = 0; w < NT / 64; ++w) tot += red[w];
-    const float rs = 1.0f / sqrtf(tot / (float)k + eps);
-#pragma unroll
-    for (int c = 0; c < kXChunks; ++c) {
-      const int i = (tid + c * NT) * 8;
-      if (i < k) {
-        u4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const h2_t hv = as_h2(xr[c][e]), hg = as_h2(gr[c][e]);
-          h2_t r;
-          r[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
-          r[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
-          v[e] = __builtin_bit_cast(uint32_t, r);
-        }
-        *reinterpret_cast<u4_t*>(xs + i) = v;
-      }
-    }
-  }
-  __syncthreads();
+  return d[0];
 }
 
 template <int EPI, int S>
@@ -292,8 +331,8 @@ __global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvAr
   const int kpad = G * kGroup;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
   float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);  // [WAVES][16]
-  float* vals = red + WAVES * 16;                                   // [TW][16]
-  float* nred = vals + TW * 16;                                     // [WAVES]
+  float* vals = red + WAVES * 16;                                  // [TW][16]
+  float* nred = vals + TW * 16;                                    // [WAVES]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.x * TW + wave / S;  // this wavefront's tile
@@ -304,17 +343,16 @@ __global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvAr
   const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + ((size_t)(live ? t : 0) * G + ks) * 64 + lane;
   const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024) +
                        ((size_t)(live ? t : 0) * G + ks) * 16 + (lane & 15);
-  const uint32_t mlo = vgpr_const(0x000F000Fu), mhi = vgpr_const(0x00F000F0u);
 
-  // 1. activations (and RMSNorm weights) first
-  u4_t xr[kXChunks], gr[kXChunks];
+  // 1. this thread's activation chunk (and RMSNorm weights) first
+  u4_t xr[4], gr[4];
   const bool norm = a.gamma != nullptr;
 #pragma unroll
-  for (int c = 0; c < kXChunks; ++c) {
-    const int i = (threadIdx.x + c * NT) * 8;
+  for (int p = 0; p < 4; ++p) {
+    const int i = threadIdx.x * 32 + 8 * p;
     const bool in = i < a.k;
-    xr[c] = in ? *reinterpret_cast<const u4_t*>(a.x + i) : (u4_t){0u, 0u, 0u, 0u};
-    gr[c] = (in && norm) ? *reinterpret_cast<const u4_t*>(a.gamma + i) : (u4_t){0u, 0u, 0u, 0u};
+    xr[p] = in ? *reinterpret_cast<const u4_t*>(a.x + i) : (u4_t){0u, 0u, 0u, 0u};
+    gr[p] = (in && norm) ? *reinterpret_cast<const u4_t*>(a.gamma + i) : (u4_t){0u, 0u, 0u, 0u};
   }
   // 2. weight blocks, two batches of kUnroll in flight. Loads are issued
   // unconditionally (past the wavefront's last group they re-read that block)
@@ -330,18 +368,19 @@ __global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvAr
     }
   };
   const uint16_t* xl = xs + 32 * (lane >> 4) + ks * kGroup;
+  const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
   float acc = 0.f;
   auto compute = [&](const u4_t* buf, const uint32_t* sc, int i0) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      if (i0 + u < ng)
-        acc = fmaf(dot_block_b1(buf[u], xl + (size_t)(i0 + u) * S * kGroup, mlo, mhi),
-                   h2f((uint16_t)sc[u]), acc);
+      if (i0 + u < ng) {
+        const float d = mfma_block_b1(buf[u], xl + (size_t)(i0 + u) * S * kGroup, mlo, mhi);
+        acc = fmaf(d, h2f((uint16_t)sc[u]), acc);
+      }
   };
   load(bufA, scA, 0);
   // 3. activation prologue (waits for the activation loads only)
-  stage_x_held(xr, gr, norm, a.eps, a.k, kpad, xs, nred, NT);
-  if (a.xn_out && blockIdx.x == 0) store_xs(xs, a.k, a.xn_out, NT);
+  stage_row_mfma(xr, gr, norm, a.eps, a.k, kpad, xs, nred, (a.xn_out && blockIdx.x == 0) ? a.xn_out : nullptr, NT);
   // 4. stream
   for (int i = 0; i < ng; i += 2 * kUnroll) {
     load(bufB, scB, i + kUnroll);
@@ -350,9 +389,6 @@ __global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvAr
     load(bufA, scA, i + 2 * kUnroll);
     compute(bufB, scB, i + kUnroll);
   }
-  // lanes l, l+16, l+32, l+48 hold the same row
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 32);
   if (lane < 16) red[wave * 16 + lane] = acc;
   __syncthreads();
   if (threadIdx.x < TW * 16) {
@@ -580,9 +616,9 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t count, uint32_t value) {
 // workgroups is needed.
 int w4_gemv_split(int tiles, int groups) {
   const int opts[] = {16, 8, 7, 4, 3, 2, 1};
-  auto fits = [&](int s) {  // staged activations: kpad <= kXChunks * 8 * threads
-    const int waves = s < 4 ? 4 : s;
-    return groups * kGroup <= kXChunks * 8 * 64 * waves;
+  auto fits = [&](int s) {  // staged activations: one 32-column chunk per thread
+    const int waves = s * (s < 4 ? 4 / s : 1);
+    return groups * kGroup <= 32 * 64 * waves;
   };
   for (int s : opts)
     if ((long)tiles * s <= 4096 && groups >= 2 * s && fits(s)) return s;
