@@ -196,7 +196,8 @@ size_t w4_workspace_bytes(const w4_config* cfg, int32_t max_batch, int32_t max_p
 
 /* Bind weights, KV cache and workspace (all caller-owned device memory; the
  * pointers are kept, not copied) into a model. Zero-fills the workspace
- * with a kernel on the default stream and waits for it. */
+ * with a kernel on the default stream and waits for it. num_pages and
+ * max_pages_per_seq are at most 2^26 (W4_EINVAL otherwise). */
 int  w4_model_create(const w4_config* cfg, const w4_weights* weights, void* kv_cache,
                      int32_t num_pages, void* workspace, size_t ws_bytes, int32_t max_batch,
                      int32_t max_pages_per_seq, w4_model** out);

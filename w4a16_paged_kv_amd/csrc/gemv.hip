@@ -111,52 +111,46 @@ __device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* ds
 
 // ------------------------------------------------------------- epilogues
 
-__device__ __forceinline__ void kv_store(const QkvEpilogue& e, int m, uint16_t* pool, int kvh,
-                                         int dim0, int dim1, float v0, float v1) {
-  const int pos = e.positions[m];
-  if (pos < 0 || pos >= e.max_pages * kPage) {
-    atomicAdd(e.err, 1u);
-    return;
-  }
-  const int page = e.page_tables[(size_t)m * e.max_pages + (pos >> 4)];
-  if (page < 0 || page >= e.num_pages) {
-    atomicAdd(e.err, 1u);
-    return;
-  }
-  uint16_t* slot = pool + (((size_t)page * e.n_kv_heads + kvh) * kPage + (pos & 15)) * e.head_dim;
-  slot[dim0] = f2h(v0);
-  slot[dim1] = f2h(v1);
+__device__ __forceinline__ void kv_store(const QkvEpilogue& e, uint16_t* pool, int slot, int kvh, int dim0,
+                                         int dim1, float v0, float v1) {
+  if (slot < 0) return;  // invalid position or page: counted by the token plan
+  uint16_t* dst = pool + (((size_t)(slot >> 4) * e.n_kv_heads + kvh) * kPage + (slot & 15)) * e.head_dim;
+  dst[dim0] = f2h(v0);
+  dst[dim1] = f2h(v1);
 }
 
 // Rows i and i+8 of tile t hold the rotate-half RoPE pair (dim0, dim0 + D/2)
-// of one head (QKV packing role). q/k heads are rotated at the token's
-// position, theta = pos * base^(-2 dim0 / D), and rounded once to fp16; v
-// heads are rounded unrotated. k/v go to the token's page slot.
-__device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float y1) {
+// of one head (QKV packing role).
+__device__ __forceinline__ int qkv_head(const QkvEpilogue& e, int t) { return (kTileRows * t) / e.head_dim; }
+__device__ __forceinline__ int qkv_dim0(const QkvEpilogue& e, int t, int i) {
+  return 8 * (((kTileRows * t) % e.head_dim) / kTileRows) + i;
+}
+
+// q/k heads are rotated by (c, sn), the token plan's rotation of the pair
+// (angle pos * base^(-2 dim0 / D)), and rounded once to fp16; v heads are
+// rounded unrotated. k/v go to the token's page slot.
+__device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float y1, float c, float sn,
+                        int slot) {
   const QkvEpilogue& e = a.qkv;
   const int D = e.head_dim;
-  const int head = (kTileRows * t) / D;
-  const int p = ((kTileRows * t) % D) / kTileRows;
-  const int dim0 = 8 * p + i, dim1 = D / 2 + 8 * p + i;
+  const int head = qkv_head(e, t);
+  const int dim0 = qkv_dim0(e, t, i), dim1 = D / 2 + dim0;
   if (e.bias) {
     y0 += h2f(e.bias[head * D + dim0]);
     y1 += h2f(e.bias[head * D + dim1]);
   }
   if (head < e.n_heads + e.n_kv_heads) {
-    int pos = e.positions[m];
-    const double th = (double)pos * pow((double)e.rope_base, -2.0 * (double)dim0 / (double)D);
-    const float c = (float)cos(th), s = (float)sin(th);
-    const float r0 = y0 * c - y1 * s;
-    const float r1 = y1 * c + y0 * s;
+    const float r0 = y0 * c - y1 * sn;
+    const float r1 = y1 * c + y0 * sn;
     if (head < e.n_heads) {
       uint16_t* q = e.q_out + (size_t)m * e.q_stride + head * D;
       q[dim0] = f2h(r0);
       q[dim1] = f2h(r1);
     } else {
-      kv_store(e, m, e.k_pool, head - e.n_heads, dim0, dim1, r0, r1);
+      kv_store(e, e.k_pool, slot, head - e.n_heads, dim0, dim1, r0, r1);
     }
   } else {
-    kv_store(e, m, e.v_pool, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
+    kv_store(e, e.v_pool, slot, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
   }
 }
 
@@ -170,7 +164,9 @@ __device__ __forceinline__ constexpr int epi_items() {
 template <int EPI>
 __device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i, const float* vals) {
   if (EPI == EPI_QKV) {
-    epi_qkv(a, m, t, i, vals[i], vals[i + 8]);
+    const int pair = qkv_dim0(a.qkv, t, i);
+    const float* cs = a.qkv.rope + ((size_t)m * (a.qkv.head_dim / 2) + pair) * 2;
+    epi_qkv(a, m, t, i, vals[i], vals[i + 8], cs[0], cs[1], a.qkv.slot[m]);
   } else if (EPI == EPI_SILU) {
     const int o = 8 * t + i;
     if (o < a.n / 2) {
@@ -211,83 +207,108 @@ constexpr int kUnroll = 4;  // blocks per batch; two batches in flight
 constexpr uint32_t kMaskLo = 0x000F000Fu;  // nibble offsets (0,1) / (4,5) of a word
 constexpr uint32_t kMaskHi = 0x00F000F0u;  // nibble offsets (2,3) / (6,7), as 16u
 
-// Column (0..31, inside a lane group's 32-column chunk) that feeds k-slot
-// 8r + s of MFMA r (0..3) of a block: MFMA r takes words 2(r/2) and
-// 2(r/2) + 1, masked with kMaskLo for even r and kMaskHi for odd r; each word
-// gives the pair (w & M) and ((w >> 8) & M).
-__device__ __forceinline__ constexpr int kslot_column(int r, int s) {
-  return 8 * (2 * (r >> 1) + (s >> 2)) + 2 * (r & 1) + (s & 1) + 4 * ((s >> 1) & 1);
+// Activation staging for the MFMA path works in slot groups: slot group sg
+// is the 8 k-slots of MFMA r = sg % 4 in 32-column chunk c = sg / 4, i.e.
+// xs[8 sg .. 8 sg + 8). Its columns sit in the two 8-column words
+// j0 = 2 (r / 2) and j0 + 1 of the chunk, at offsets 2 (r % 2) + {0, 1, 4, 5}:
+// 32-bit pairs e = r % 2 and e + 2 of each word. A thread loads natural
+// 8-column word wd = tid + it * NT (it < IT) of x (and of the RMSNorm
+// weights) ahead of the weight stream, normalises it and builds slot group
+// sg = wd from the words of its own 4-lane quad (the quad of lanes 4c..4c+3
+// holds chunk c) with DPP quad permutes.
+
+template <int IT, bool NORM>
+struct StageRegs {
+  u4_t x[IT], g[NORM ? IT : 1];
+};
+
+template <int IT, bool NORM>
+__device__ __forceinline__ void stage_load(StageRegs<IT, NORM>& r, const uint16_t* __restrict__ x,
+                                           const uint16_t* __restrict__ gamma, int k, int NT) {
+  // unconditional loads from clamped addresses (a branch around a load makes
+  // the compiler wait for it on the spot); words past k are zeroed after the
+  // wait, in stage_row_mfma
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = min(8 * (threadIdx.x + it * NT), k - 8);
+    r.x[it] = *reinterpret_cast<const u4_t*>(x + c);
+    if (NORM) r.g[it] = *reinterpret_cast<const u4_t*>(gamma + c);
+  }
 }
 
-// Stages one activation row for the MFMA path. Thread t owns 32-column chunk
-// t (xr = its columns in natural order, gr = the RMSNorm weights, zero past
-// k): with gamma, the row becomes fp16(x * rsqrt(mean(x^2) + eps) * gamma)
-// (RMSNorm in FP16). Chunk t is written to xs[32t..32t+32) in k-slot order,
-// odd-r slots divided by 16. The natural-order row also goes to xn_out if
-// given. Ends with a barrier. Requires kpad <= 32 * NT.
-__device__ void stage_row_mfma(const u4_t* xr, const u4_t* gr, bool norm, float eps, int k, int kpad,
-                               uint16_t* xs, float* red, uint16_t* xn_out, const int NT) {
+__device__ __forceinline__ uint32_t quad_perm(uint32_t v, int ctrl_is_odd) {
+  // quad_perm [0,0,2,2] (0xA0) or [1,1,3,3] (0xF5)
+  return ctrl_is_odd ? (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xF5, 0xF, 0xF, false)
+                     : (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xA0, 0xF, 0xF, false);
+}
+
+// Stages the row: with NORM it becomes fp16(x * rsqrt(mean(x^2) + eps) *
+// gamma) (RMSNorm in FP16); the slots of odd r are divided by 16 (exact
+// fp16 scaling). The natural-order (normalised) row also goes to xn_out if
+// given. Ends with a barrier. Requires kpad <= 8 * IT * NT.
+template <int IT, bool NORM>
+__device__ void stage_row_mfma(const StageRegs<IT, NORM>& r, float eps, int k, int kpad, uint16_t* xs,
+                               float* red, uint16_t* xn_out, const int NT) {
+  // every use of the loaded words comes first, in straight-line code: a
+  // branch here would make the compiler wait for all loads in flight,
+  // weights included
   const int tid = threadIdx.x;
-  const bool has = tid * 32 < kpad;
-  float ss = 0.f;
+  const int e = tid & 1;                      // r % 2 of this lane's slot groups (NT % 4 == 0)
+  u4_t xv[IT];
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
+  for (int it = 0; it < IT; ++it) {
+    const bool in = 8 * (tid + it * NT) < k;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const h2_t h = as_h2(xr[p][e]);
-      ss = fmaf((float)h[0], (float)h[0], ss);
-      ss = fmaf((float)h[1], (float)h[1], ss);
-    }
+    for (int d = 0; d < 4; ++d) xv[it][d] = in ? r.x[it][d] : 0u;
+  }
   float rs = 1.f;
-  if (norm) {
+  if (NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const h2_t v = as_h2(xv[it][d]);
+        ss = fmaf((float)v[0], (float)v[0], ss);
+        ss = fmaf((float)v[1], (float)v[1], ss);
+      }
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     float tot = 0.f;
     for (int w = 0; w < NT / 64; ++w) tot += red[w];
     rs = 1.0f / sqrtf(tot / (float)k + eps);
-  }
-  _Float16 v[32];
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
+    for (int it = 0; it < IT; ++it)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const h2_t hv = as_h2(xr[p][e]);
-      if (norm) {
-        const h2_t hg = as_h2(gr[p][e]);
-        v[8 * p + 2 * e] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
-        v[8 * p + 2 * e + 1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
-      } else {
-        v[8 * p + 2 * e] = hv[0];
-        v[8 * p + 2 * e + 1] = hv[1];
-      }
-    }
-  if (xn_out && has) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      if (tid * 32 + 8 * p < k) {
-        u4_t o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = __builtin_bit_cast(uint32_t, (h2_t){v[8 * p + 2 * e], v[8 * p + 2 * e + 1]});
-        *reinterpret_cast<u4_t*>(xn_out + tid * 32 + 8 * p) = o;
+      for (int d = 0; d < 4; ++d) {
+        const h2_t hv = as_h2(xv[it][d]), hg = as_h2(r.g[it][d]);
+        h2_t v;
+        v[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
+        v[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
+        xv[it][d] = __builtin_bit_cast(uint32_t, v);
       }
   }
-  u4_t o[4];
+  const h2_t sc = e ? (h2_t){(_Float16)0.0625f, (_Float16)0.0625f} : (h2_t){(_Float16)1.0f, (_Float16)1.0f};
+  u4_t o[IT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int it = 0; it < IT; ++it) {
+    // words j0 (lanes {0,0,2,2} of the quad) and j0 + 1 (lanes {1,1,3,3})
+    const uint32_t a0 = quad_perm(xv[it][0], 0), a1 = quad_perm(xv[it][1], 0);
+    const uint32_t a2 = quad_perm(xv[it][2], 0), a3 = quad_perm(xv[it][3], 0);
+    const uint32_t b0 = quad_perm(xv[it][0], 1), b1 = quad_perm(xv[it][1], 1);
+    const uint32_t b2 = quad_perm(xv[it][2], 1), b3 = quad_perm(xv[it][3], 1);
+    o[it][0] = __builtin_bit_cast(uint32_t, as_h2(e ? a1 : a0) * sc);
+    o[it][1] = __builtin_bit_cast(uint32_t, as_h2(e ? a3 : a2) * sc);
+    o[it][2] = __builtin_bit_cast(uint32_t, as_h2(e ? b1 : b0) * sc);
+    o[it][3] = __builtin_bit_cast(uint32_t, as_h2(e ? b3 : b2) * sc);
+  }
 #pragma unroll
-    for (int s = 0; s < 8; s += 2) {
-      _Float16 h0 = v[kslot_column(r, s)], h1 = v[kslot_column(r, s + 1)];
-      if (r & 1) {
-        h0 = (_Float16)((float)h0 * 0.0625f);
-        h1 = (_Float16)((float)h1 * 0.0625f);
-      }
-      o[r][s / 2] = __builtin_bit_cast(uint32_t, (h2_t){h0, h1});
-    }
-  if (has)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) *reinterpret_cast<u4_t*>(xs + tid * 32 + 8 * r) = o[r];
+  for (int it = 0; it < IT; ++it) {
+    const int wd = tid + it * NT;
+    if (8 * wd < kpad) *reinterpret_cast<u4_t*>(xs + 8 * wd) = o[it];
+    if (xn_out && 8 * wd < k) *reinterpret_cast<u4_t*>(xn_out + 8 * wd) = xv[it];
+  }
   __syncthreads();
 }
 
@@ -320,12 +341,13 @@ __device__ __forceinline__ float mfma_block_b1(const u4_t w, const uint16_t* __r
   return d[0];
 }
 
-template <int EPI, int S>
-__global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvArgs a) {
-  // S wavefronts per tile, TW tiles per workgroup
-  constexpr int TW = S < 4 ? 4 / S : 1;
-  constexpr int WAVES = S * TW;
-  constexpr int NT = WAVES * 64;
+template <int EPI, int S, int IT>
+__global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a) {
+  // S wavefronts per tile, TW tiles per workgroup (blockDim.x = 64 S TW);
+  // IT activation words per thread
+  const int NT = blockDim.x;
+  const int WAVES = NT / 64;
+  const int TW = WAVES / S;
   extern __shared__ __align__(16) uint8_t smem[];
   const int G = a.groups;
   const int kpad = G * kGroup;
@@ -344,15 +366,23 @@ __global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvAr
   const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024) +
                        ((size_t)(live ? t : 0) * G + ks) * 16 + (lane & 15);
 
-  // 1. this thread's activation chunk (and RMSNorm weights) first
-  u4_t xr[4], gr[4];
-  const bool norm = a.gamma != nullptr;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int i = threadIdx.x * 32 + 8 * p;
-    const bool in = i < a.k;
-    xr[p] = in ? *reinterpret_cast<const u4_t*>(a.x + i) : (u4_t){0u, 0u, 0u, 0u};
-    gr[p] = (in && norm) ? *reinterpret_cast<const u4_t*>(a.gamma + i) : (u4_t){0u, 0u, 0u, 0u};
+  // 1. this thread's activation slot groups (and RMSNorm weights) first
+  constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SILU;  // batch 1: RMSNorm prologue
+  StageRegs<IT, NORM> st;
+  stage_load(st, a.x, a.gamma, a.k, NT);
+  // QKV: the epilogue threads' RoPE rotations and the token's K/V slot, also
+  // ahead of the weights
+  float rc = 1.f, rsn = 0.f;
+  int slot = -1;
+  if (EPI == EPI_QKV && threadIdx.x < TW * 8) {
+    const int tt = blockIdx.x * TW + threadIdx.x / 8;
+    if (tt < a.tiles) {
+      const int pair = qkv_dim0(a.qkv, tt, threadIdx.x % 8);
+      const float2 cs = *reinterpret_cast<const float2*>(a.qkv.rope + 2 * pair);
+      rc = cs.x;
+      rsn = cs.y;
+      slot = a.qkv.slot[0];
+    }
   }
   // 2. weight blocks, two batches of kUnroll in flight. Loads are issued
   // unconditionally (past the wavefront's last group they re-read that block)
@@ -379,8 +409,9 @@ __global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvAr
       }
   };
   load(bufA, scA, 0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the prologue's arithmetic behind the first weight loads
   // 3. activation prologue (waits for the activation loads only)
-  stage_row_mfma(xr, gr, norm, a.eps, a.k, kpad, xs, nred, (a.xn_out && blockIdx.x == 0) ? a.xn_out : nullptr, NT);
+  stage_row_mfma(st, a.eps, a.k, kpad, xs, nred, (a.xn_out && blockIdx.x == 0) ? a.xn_out : nullptr, NT);
   // 4. stream
   for (int i = 0; i < ng; i += 2 * kUnroll) {
     load(bufB, scB, i + kUnroll);
@@ -403,7 +434,13 @@ __global__ __launch_bounds__((S < 4 ? 4 : S) * 64) void w4_gemv_b1_kernel(GemvAr
   if (threadIdx.x < TW * per) {
     const int tl = threadIdx.x / per;
     const int tt = blockIdx.x * TW + tl;
-    if (tt < a.tiles) epilogue<EPI>(a, 0, tt, threadIdx.x % per, vals + tl * 16);
+    if (tt < a.tiles) {
+      const int i = threadIdx.x % per;
+      if (EPI == EPI_QKV)
+        epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], rc, rsn, slot);
+      else
+        epilogue<EPI>(a, 0, tt, i, vals + tl * 16);
+    }
   }
 }
 
@@ -585,19 +622,35 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* x, in
     yr[i] = i < k ? f2h(h2f(xr[i]) * rs * h2f(gamma[i])) : (uint16_t)0;
 }
 
-__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, const uint16_t* table,
-                                                    int vocab, int hidden, uint16_t* x,
-                                                    uint32_t* err) {
+__global__ __launch_bounds__(256) void embed_plan_kernel(TokenPlanArgs a) {
   const int b = blockIdx.x;
-  int tok = tokens[b];
-  if (tok < 0 || tok >= vocab) {
-    if (threadIdx.x == 0) atomicAdd(err, 1u);
-    tok = tok < 0 ? 0 : vocab - 1;
+  if (a.tokens) {
+    int tok = a.tokens[b];
+    if (tok < 0 || tok >= a.vocab) {
+      if (threadIdx.x == 0) atomicAdd(a.err, 1u);
+      tok = tok < 0 ? 0 : a.vocab - 1;
+    }
+    const uint16_t* src = a.table + (size_t)tok * a.hidden;
+    uint16_t* dst = a.x + (size_t)b * a.hidden;
+    for (int i = threadIdx.x * 8; i < a.hidden; i += 256 * 8)
+      *reinterpret_cast<u4_t*>(dst + i) = *reinterpret_cast<const u4_t*>(src + i);
   }
-  const uint16_t* src = table + (size_t)tok * hidden;
-  uint16_t* dst = x + (size_t)b * hidden;
-  for (int i = threadIdx.x * 8; i < hidden; i += 256 * 8)
-    *reinterpret_cast<u4_t*>(dst + i) = *reinterpret_cast<const u4_t*>(src + i);
+  if (threadIdx.x >= 64) return;
+  const int pos = a.positions[b];
+  if (threadIdx.x == 0) {
+    const bool pos_ok = pos >= 0 && pos < a.max_pages * kPage;
+    const int page = pos_ok ? a.page_tables[(size_t)b * a.max_pages + (pos >> 4)] : -1;
+    const bool ok = pos_ok && page >= 0 && page < a.num_pages;
+    a.slot[b] = ok ? page * kPage + (pos & 15) : -1;
+    if (!ok) atomicAdd(a.err, 1u);
+  }
+  const int half = a.head_dim / 2;
+  for (int i = threadIdx.x; i < half; i += 64) {
+    const double th = (double)pos * pow((double)a.rope_base, -2.0 * (double)i / (double)a.head_dim);
+    float* r = a.rope + ((size_t)b * half + i) * 2;
+    r[0] = (float)cos(th);
+    r[1] = (float)sin(th);
+  }
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t count, uint32_t value) {
@@ -608,47 +661,62 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t count, uint32_t value) {
 
 // ---------------------------------------------------------------- launchers
 
-// Batch-1 work split: S wavefronts per tile, each taking every S-th group, and
-// 4/S tiles per workgroup when S < 4. S is the largest choice that keeps every
-// wavefront of the launch resident on the chip at once (about 4K wavefronts)
-// with at least two groups each: then each wavefront streams one long,
-// double-buffered run of blocks and no second, partly empty round of
-// workgroups is needed.
-int w4_gemv_split(int tiles, int groups) {
-  const int opts[] = {16, 8, 7, 4, 3, 2, 1};
-  auto fits = [&](int s) {  // staged activations: one 32-column chunk per thread
-    const int waves = s * (s < 4 ? 4 / s : 1);
-    return groups * kGroup <= 32 * 64 * waves;
-  };
-  for (int s : opts)
-    if ((long)tiles * s <= 4096 && groups >= 2 * s && fits(s)) return s;
-  for (int s : {1, 2, 3, 4, 7, 8, 16})
-    if (fits(s)) return s;
-  return 0;  // activation row longer than one workgroup can stage
+// Batch-1 work split. TW = ceil(tiles / 256) tiles per workgroup, so a
+// matrix of up to 256 x 16 tiles runs as at most one workgroup per CU: each
+// CU then stages the activation row once, and no second workgroup on a CU
+// waits for its activations behind the first one's weight stream. The S
+// wavefronts of a tile split its groups (S <= groups / 2, S * TW <= 16), so
+// small matrices still put thousands of wavefronts in flight.
+struct B1Split {
+  int s, tw, it;
+};
+
+static B1Split w4_b1_split(int tiles, int groups) {
+  const int tw = std::min(16, ceil_div(tiles, 256));
+  int s = 1;
+  for (int c : {16, 8, 4, 2})
+    if (groups >= 2 * c && c * tw <= 16) {
+      s = c;
+      break;
+    }
+  const int nt = 64 * s * tw;
+  const int it = ceil_div(groups * kGroup, 8 * nt);  // activation words per thread
+  return {s, tw, it};
+}
+
+template <int EPI, int S, int IT>
+static void launch_b1(const GemvArgs& a, int tw, hipStream_t s) {
+  const int waves = S * tw;
+  const size_t lds = (size_t)a.groups * kGroup * 2 + (waves * 16 + tw * 16 + waves) * sizeof(float);
+  hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S, IT>), dim3(ceil_div(a.tiles, tw)), dim3(waves * 64), lds, s,
+                     a);
 }
 
 template <int EPI, int S>
-static void launch_b1(const GemvArgs& a, hipStream_t s) {
-  constexpr int TW = S < 4 ? 4 / S : 1;
-  constexpr int WAVES = S * TW;
-  const size_t lds = (size_t)a.groups * kGroup * 2 + (WAVES * 16 + TW * 16 + WAVES) * sizeof(float);
-  hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S>), dim3(ceil_div(a.tiles, TW)), dim3(WAVES * 64), lds, s,
-                     a);
+static hipError_t launch_b1_it(const GemvArgs& a, const B1Split& sp, hipStream_t s) {
+  switch (sp.it) {
+    case 1: launch_b1<EPI, S, 1>(a, sp.tw, s); return hipSuccess;
+    case 2: launch_b1<EPI, S, 2>(a, sp.tw, s); return hipSuccess;
+    case 3: launch_b1<EPI, S, 3>(a, sp.tw, s); return hipSuccess;
+  }
+  return hipErrorInvalidValue;  // activation row longer than one workgroup can stage
 }
 
 template <int EPI>
 static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
   if (a.batch == 1) {
-    switch (w4_gemv_split(a.tiles, a.groups)) {
-      case 16: launch_b1<EPI, 16>(a, s); break;
-      case 8: launch_b1<EPI, 8>(a, s); break;
-      case 7: launch_b1<EPI, 7>(a, s); break;
-      case 4: launch_b1<EPI, 4>(a, s); break;
-      case 3: launch_b1<EPI, 3>(a, s); break;
-      case 2: launch_b1<EPI, 2>(a, s); break;
-      case 1: launch_b1<EPI, 1>(a, s); break;
-      default: return hipErrorInvalidValue;
+    // the batch-1 kernel applies RMSNorm exactly for the QKV and gate/up epilogues
+    if ((a.gamma != nullptr) != (EPI == EPI_QKV || EPI == EPI_SILU)) return hipErrorInvalidValue;
+    const B1Split sp = w4_b1_split(a.tiles, a.groups);
+    hipError_t e = hipErrorInvalidValue;
+    switch (sp.s) {
+      case 16: e = launch_b1_it<EPI, 16>(a, sp, s); break;
+      case 8: e = launch_b1_it<EPI, 8>(a, sp, s); break;
+      case 4: e = launch_b1_it<EPI, 4>(a, sp, s); break;
+      case 2: e = launch_b1_it<EPI, 2>(a, sp, s); break;
+      case 1: e = launch_b1_it<EPI, 1>(a, sp, s); break;
     }
+    if (e != hipSuccess) return e;
   } else {
     constexpr int WAVES = 4;
     hipLaunchKernelGGL((w4_gemm_mfma_kernel<EPI, WAVES>), dim3(a.tiles), dim3(WAVES * 64), 0, s, a);
@@ -687,9 +755,8 @@ hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16
   return hipGetLastError();
 }
 
-hipError_t launch_embed(const int32_t* tokens, const uint16_t* table, int32_t vocab, int32_t hidden,
-                        uint16_t* x, int32_t batch, uint32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(batch), dim3(256), 0, s, tokens, table, vocab, hidden, x, err);
+hipError_t launch_embed_plan(const TokenPlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(embed_plan_kernel, dim3(a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

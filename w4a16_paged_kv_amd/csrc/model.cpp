@@ -21,7 +21,7 @@
 namespace w4 {
 
 struct WsLayout {
-  size_t err, counters, tokens, positions, ctx, pt, x, xn, q, o, h, partials, total;
+  size_t err, counters, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, total;
   int xn_stride, o_stride, h_stride, max_splits;
 };
 
@@ -44,6 +44,8 @@ static WsLayout ws_layout(const w4_config& c, int max_batch, int max_pages) {
   L.positions = take((size_t)max_batch * 4);
   L.ctx = take((size_t)max_batch * 4);
   L.pt = take((size_t)max_batch * max_pages * 4);
+  L.slot = take((size_t)max_batch * 4);
+  L.rope = take((size_t)max_batch * (c.head_dim / 2) * 2 * 4);
   L.x = take((size_t)max_batch * c.hidden * 2);
   L.xn = take((size_t)max_batch * L.xn_stride * 2);
   L.q = take((size_t)max_batch * c.n_heads * c.head_dim * 2);
@@ -163,15 +165,11 @@ static int enqueue_op(w4_model* m, int op, int l, const uint16_t* x_in, uint16_t
       a.qkv.k_pool = m->k_pool(l);
       a.qkv.v_pool = m->v_pool(l);
       a.qkv.bias = W.qkv_bias;
-      a.qkv.positions = in.positions;
-      a.qkv.page_tables = in.page_tables;
-      a.qkv.max_pages = m->max_pages;
-      a.qkv.num_pages = m->num_pages;
+      a.qkv.slot = m->at<int32_t>(L.slot);
+      a.qkv.rope = m->at<float>(L.rope);
       a.qkv.n_heads = c.n_heads;
       a.qkv.n_kv_heads = c.n_kv_heads;
       a.qkv.head_dim = c.head_dim;
-      a.qkv.rope_base = c.rope_base;
-      a.qkv.err = err;
       W4_LAUNCH(launch_w4_gemv(EPI_QKV, a, s));
       return W4_OK;
     }
@@ -263,12 +261,37 @@ static int enqueue_lm_head(w4_model* m, const uint16_t* x, int batch, uint16_t* 
   return W4_OK;
 }
 
+// Embedding lookup (if tokens is given) and the step's token plan: every
+// layer's QKV epilogue reads the token's K/V slot and RoPE rotations from it.
+static int enqueue_plan(w4_model* m, const int32_t* tokens, const StepInputs& in, int batch,
+                        hipStream_t s) {
+  const w4_config& c = m->cfg;
+  TokenPlanArgs p{};
+  p.tokens = tokens;
+  p.table = m->weights.embed;
+  p.vocab = c.vocab;
+  p.hidden = c.hidden;
+  p.x = m->at<uint16_t>(m->L.x);
+  p.positions = in.positions;
+  p.page_tables = in.page_tables;
+  p.max_pages = m->max_pages;
+  p.num_pages = m->num_pages;
+  p.head_dim = c.head_dim;
+  p.rope_base = c.rope_base;
+  p.slot = m->at<int32_t>(m->L.slot);
+  p.rope = m->at<float>(m->L.rope);
+  p.batch = batch;
+  p.err = m->at<uint32_t>(m->L.err);
+  W4_LAUNCH(launch_embed_plan(p, s));
+  return W4_OK;
+}
+
 static int enqueue_step(w4_model* m, const StepInputs& in, int batch, uint16_t* logits,
                         hipStream_t s) {
   const w4_config& c = m->cfg;
   uint16_t* x = m->at<uint16_t>(m->L.x);
-  W4_LAUNCH(launch_embed(in.tokens, m->weights.embed, c.vocab, c.hidden, x, batch,
-                         m->at<uint32_t>(m->L.err), s));
+  int rc0 = enqueue_plan(m, in.tokens, in, batch, s);
+  if (rc0) return rc0;
   for (int l = 0; l < c.n_layers; ++l) {
     int rc = enqueue_layer(m, l, x, x, in, batch, s);
     if (rc) return rc;
@@ -393,8 +416,9 @@ W4_EXPORT int w4_model_create(const w4_config* cfg, const w4_weights* weights, v
     return fail(W4_EINVAL, "w4_model_create: null pointer");
   int rc = check_config(cfg);
   if (rc) return rc;
-  if (max_batch < 1 || max_batch > 16 || max_pages < 1 || num_pages < 1)
-    return fail(W4_EINVAL, "w4_model_create: max_batch=%d (1..16) max_pages=%d num_pages=%d",
+  if (max_batch < 1 || max_batch > 16 || max_pages < 1 || num_pages < 1 || num_pages > (1 << 26) ||
+      max_pages > (1 << 26))
+    return fail(W4_EINVAL, "w4_model_create: max_batch=%d (1..16) max_pages=%d num_pages=%d (pages at most 2^26)",
                 max_batch, max_pages, num_pages);
   const WsLayout L = ws_layout(*cfg, max_batch, max_pages);
   if (ws_bytes < L.total)
@@ -513,6 +537,8 @@ W4_EXPORT int decode_layer(w4_model* m, int32_t layer, const uint16_t* x_in, uin
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = stage_inputs(m, nullptr, positions, page_tables, ctx_lens, batch, s);
+  if (rc) return rc;
+  rc = enqueue_plan(m, nullptr, staged(m), batch, s);
   if (rc) return rc;
   return enqueue_layer(m, layer, x_in, x_out, staged(m), batch, s);
 }
@@ -637,8 +663,10 @@ W4_EXPORT int w4_model_stage(w4_model* m, const int32_t* tokens, const int32_t* 
   if (!positions || !page_tables || !ctx_lens) return fail(W4_EINVAL, "w4_model_stage: null pointer");
   rc = validate_inputs(m, tokens, positions, page_tables, ctx_lens, batch);
   if (rc) return rc;
-  return stage_inputs(m, tokens, positions, page_tables, ctx_lens, batch,
-                      static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = stage_inputs(m, tokens, positions, page_tables, ctx_lens, batch, s);
+  if (rc) return rc;
+  return enqueue_plan(m, nullptr, staged(m), batch, s);
 }
 
 W4_EXPORT int w4_model_run_op(w4_model* m, int32_t op, int32_t layer, int32_t batch,
@@ -650,9 +678,7 @@ W4_EXPORT int w4_model_run_op(w4_model* m, int32_t op, int32_t layer, int32_t ba
   uint16_t* x = m->at<uint16_t>(m->L.x);
   if (op == W4_OP_EMBED) {
     if (!m->weights.embed) return fail(W4_EINVAL, "w4_model_run_op: model has no embedding");
-    W4_LAUNCH(launch_embed(staged(m).tokens, m->weights.embed, m->cfg.vocab, m->cfg.hidden, x,
-                           batch, m->at<uint32_t>(m->L.err), s));
-    return W4_OK;
+    return enqueue_plan(m, staged(m).tokens, staged(m), batch, s);
   }
   if (op == W4_OP_LM_HEAD) {
     if (!m->weights.lm_head || !m->weights.final_norm || !logits)

@@ -47,20 +47,38 @@ enum Epi : int {
 };
 
 // Everything the QKV epilogue needs: RoPE at the token's position and the
-// store of its K/V into the layer's pages.
+// store of its K/V into the layer's pages. The per-token parts (slot and
+// rotation) are the same in every layer and come from the token plan.
 struct QkvEpilogue {
   uint16_t* q_out;            // [B][q_stride] fp16, q heads in logical order
   int32_t q_stride;
   uint16_t* k_pool;           // [P][Hkv][16][D]
   uint16_t* v_pool;
   const uint16_t* bias;       // fp16 [(Hq+2Hkv)D] logical order, or nullptr
-  const int32_t* positions;   // device [B]
-  const int32_t* page_tables; // device [B][max_pages]
-  int32_t max_pages;
-  int32_t num_pages;
+  const int32_t* slot;        // token plan: [B] page * 16 + position % 16, or -1 (no K/V store)
+  const float* rope;          // token plan: [B][D/2][2] cos, sin of pair i's angle
   int32_t n_heads, n_kv_heads, head_dim;
+};
+
+// Embedding lookup and the token plan of one step, one workgroup per
+// sequence: x[b] = E[tokens[b]] (skipped without tokens); slot[b] = the K/V
+// slot of the token at positions[b] (page from the page table), -1 and one
+// error count if the position or its page is invalid; rope[b][i] = cos, sin
+// of positions[b] * rope_base^(-2i/D), computed in double.
+struct TokenPlanArgs {
+  const int32_t* tokens;      // [B] or nullptr
+  const uint16_t* table;      // [vocab][hidden]
+  int32_t vocab, hidden;
+  uint16_t* x;                // [B][hidden]
+  const int32_t* positions;   // [B]
+  const int32_t* page_tables; // [B][max_pages]
+  int32_t max_pages, num_pages;
+  int32_t head_dim;
   float rope_base;
-  uint32_t* err;              // device error counter
+  int32_t* slot;              // [B]
+  float* rope;                // [B][head_dim / 2][2]
+  int32_t batch;
+  uint32_t* err;
 };
 
 struct GemvArgs {
@@ -117,9 +135,7 @@ hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16_t* gamma,
                                float eps, int32_t k, uint16_t* y, int32_t y_stride,
                                int32_t batch, hipStream_t s);
-hipError_t launch_embed(const int32_t* tokens, const uint16_t* table, int32_t vocab,
-                        int32_t hidden, uint16_t* x, int32_t batch, uint32_t* err,
-                        hipStream_t s);
+hipError_t launch_embed_plan(const TokenPlanArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t s);
 bool attention_supported(int head_dim, int group);
