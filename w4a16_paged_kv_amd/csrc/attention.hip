@@ -50,6 +50,42 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 
 constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time each
 
+__device__ __forceinline__ int f_bits(float v) { return __builtin_bit_cast(int, v); }
+__device__ __forceinline__ float bits_f(int v) { return __builtin_bit_cast(float, v); }
+
+// Cross-lane reductions on the VALU rather than through LDS permutes:
+// DPP row rotates inside a 16-lane row, v_permlane16_swap / v_permlane32_swap
+// across rows. row4: lanes i, i+4, i+8, i+12 of a row; rows: lanes i, i^16,
+// i^32, i^48; ror8 alone pairs lanes i and i^8 of a row.
+__device__ __forceinline__ float ror4(float v) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float ror8(float v) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
+  v = fmaxf(bits_f(a[0]), bits_f(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
+  return fmaxf(bits_f(b[0]), bits_f(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
+  v = bits_f(a[0]) + bits_f(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
+  return bits_f(b[0]) + bits_f(b[1]);
+}
+__device__ __forceinline__ float page_max(float v) {  // over the 16 tokens of a page (same lane % 4)
+  v = fmaxf(v, ror4(v));
+  v = fmaxf(v, ror8(v));
+  return rows_max(v);
+}
+__device__ __forceinline__ float page_sum(float v) {
+  v += ror4(v);
+  v += ror8(v);
+  return rows_sum(v);
+}
+
 template <int D, int GQ>
 __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
@@ -70,7 +106,20 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t* pt = a.page_tables + (size_t)b * a.max_pages;
+  // the context length, this wavefront's first two page ids and the queries
+  // are independent: issue them together (page ids are validated below)
+  const int pw0 = split * a.pages_per_split + wave;
+  int pid_cur = pt[min(pw0, a.max_pages - 1)];
+  int pid_nxt = pt[min(pw0 + W, a.max_pages - 1)];
   int ctx = a.ctx_lens[b];
+  const uint16_t* qb = a.q + (size_t)b * a.q_stride + (size_t)kvh * GQ * D;
+  u4_t qv[(GQ * D + NT * 8 - 1) / (NT * 8)];
+#pragma unroll
+  for (int r = 0; r < (GQ * D + NT * 8 - 1) / (NT * 8); ++r) {
+    const int i = min((int)(threadIdx.x + r * NT) * 8, GQ * D - 8);
+    qv[r] = *reinterpret_cast<const u4_t*>(qb + i);
+  }
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * kPage ? a.max_pages * kPage : ctx);
   const int npages = (ctx + kPage - 1) / kPage;
   const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
@@ -83,16 +132,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
   if (split >= nsplit) return;
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(npages, p_begin + a.pages_per_split);
-  const int32_t* pt = a.page_tables + (size_t)b * a.max_pages;
 
-  // the group's queries go to LDS (read per head per page: registers stay free
-  // for more wavefronts in flight); lane (tk = lane >> 2, c = lane & 3) covers
-  // columns 8c + 32i .. +8 of token tk for the scores
-  const int tk = lane >> 2, c = lane & 3;
-  const uint16_t* qb = a.q + (size_t)b * a.q_stride + (size_t)kvh * GQ * D;
-  for (int i = threadIdx.x * 8; i < GQ * D; i += NT * 8)
-    *reinterpret_cast<u4_t*>(&s_q[i]) = *reinterpret_cast<const u4_t*>(qb + i);
+  // the group's queries go to LDS (read per head per page); lane
+  // (tk = lane >> 2, c = lane & 3) covers columns 8c + 32i .. +8 of token tk
+#pragma unroll
+  for (int r = 0; r < (GQ * D + NT * 8 - 1) / (NT * 8); ++r) {
+    const int i = (int)(threadIdx.x + r * NT) * 8;
+    if (i < GQ * D) *reinterpret_cast<u4_t*>(&s_q[i]) = qv[r];
+  }
   __syncthreads();
+  const int tk = lane >> 2, c = lane & 3;
 
   const float scale = kLog2e / sqrtf((float)D);
   const int hA = c, hB = c + 4;            // heads whose softmax state this lane keeps
@@ -106,17 +155,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
   const int t0 = lane / LD;                // first PV token row of this lane
   const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
 
-  // K/V of this wavefront's next page are in flight while it computes the
-  // current one
-  auto page_of = [&](int p, int& valid) {
-    int page = pt[p];
-    const bool bad = page < 0 || page >= a.num_pages;
-    if (bad) {
-      if (lane == 0) atomicAdd(a.err, 1u);
-      page = 0;
-    }
+  // page p's id, validated (an invalid id is counted and read as page 0,
+  // with no valid tokens)
+  auto checked = [&](int p, int id, int& valid) {
+    const bool bad = id < 0 || id >= a.num_pages;
+    if (bad && lane == 0) atomicAdd(a.err, 1u);
     valid = bad ? 0 : min(kPage, ctx - p * kPage);
-    return page;
+    return bad ? 0 : id;
   };
   u4_t kf[NI], vf[NTOK], kn[NI], vn[NTOK];
   auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
@@ -127,12 +172,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
 #pragma unroll
     for (int i = 0; i < NTOK; ++i) vv[i] = *reinterpret_cast<const u4_t*>(vb + (t0 + TPI * i) * D + d0);
   };
-  int valid_next = 0;
-  if (p_begin + wave < p_end) load_kv(page_of(p_begin + wave, valid_next), kf, vf);
-  for (int p = p_begin + wave; p < p_end; p += W) {
-    const int valid = valid_next;
+  int valid_cur = 0, valid_nxt = 0;
+  if (pw0 < p_end) load_kv(checked(pw0, pid_cur, valid_cur), kf, vf);
+  for (int p = pw0; p < p_end; p += W) {
+    const int valid = valid_cur;
     if (p + W < p_end) {
-      load_kv(page_of(p + W, valid_next), kn, vn);
+      load_kv(checked(p + W, pid_nxt, valid_nxt), kn, vn);
+      pid_nxt = pt[min(p + 2 * W, a.max_pages - 1)];  // the page after, one step ahead
     }
 
     // scores of token tk for every head of the group (quad reduction over c)
@@ -142,9 +188,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const u4_t qv = *reinterpret_cast<const u4_t*>(&s_q[h * D + 8 * c + 32 * i]);
+        const u4_t qq = *reinterpret_cast<const u4_t*>(&s_q[h * D + 8 * c + 32 * i]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(as_h2a(qv[e]), as_h2a(kf[i][e]), acc, false);
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(as_h2a(qq[e]), as_h2a(kf[i][e]), acc, false);
       }
       acc += dpp_xor1(acc);
       acc += dpp_xor2(acc);
@@ -161,25 +207,14 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
       sB = -INFINITY;
     }
     // page maximum and sum over the 16 tokens (lanes sharing c)
-    float pmA = sA, pmB = sB;
-#pragma unroll
-    for (int off = 4; off < 64; off <<= 1) {
-      pmA = fmaxf(pmA, __shfl_xor(pmA, off));
-      pmB = fmaxf(pmB, __shfl_xor(pmB, off));
-    }
+    const float pmA = page_max(sA), pmB = page_max(sB);
     const float nA = fmaxf(mA, pmA), nB = fmaxf(mB, pmB);
     const float alA = nA == -INFINITY ? 1.f : exp2f(mA - nA);
     const float alB = nB == -INFINITY ? 1.f : exp2f(mB - nB);
     const float pA = nA == -INFINITY ? 0.f : exp2f(sA - nA);
     const float pB = nB == -INFINITY ? 0.f : exp2f(sB - nB);
-    float sumA = pA, sumB = pB;
-#pragma unroll
-    for (int off = 4; off < 64; off <<= 1) {
-      sumA += __shfl_xor(sumA, off);
-      sumB += __shfl_xor(sumB, off);
-    }
-    lA = lA * alA + sumA;
-    lB = lB * alB + sumB;
+    lA = lA * alA + page_sum(pA);
+    lB = lB * alB + page_sum(pB);
     mA = nA;
     mB = nB;
     // broadcast weights and rescale factors to the PV lanes through LDS
@@ -230,14 +265,18 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
     for (int i = 0; i < NI; ++i) kf[i] = kn[i];
 #pragma unroll
     for (int i = 0; i < NTOK; ++i) vf[i] = vn[i];
+    valid_cur = valid_nxt;
   }
   // reduce o over the lanes holding other token rows of the same columns
+  // (lanes d apart by multiples of LD: 16 for D = 128, 8 for D = 64)
 #pragma unroll
-  for (int off = LD; off < 64; off <<= 1)
+  for (int h = 0; h < GQ; ++h)
 #pragma unroll
-    for (int h = 0; h < GQ; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], off);
+    for (int e = 0; e < 8; ++e) {
+      float v = o[h][e];
+      if (LD == 8) v += ror8(v);
+      o[h][e] = rows_sum(v);
+    }
   if (lane < 4) {
     s_m[wave][hA] = mA;
     s_l[wave][hA] = lA;
@@ -290,45 +329,56 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
              (uint32_t)(nsplit - 1);
   __syncthreads();
   if (!s_last) return;
-  // merge weights per (head, split): w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'
+  // One pass: (m, l) of every (head, split) go to LDS while each thread's
+  // first sixteen partial outputs are already in flight; every thread then
+  // forms the merge weights of its own head from LDS.
   const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * (D + 2);
-  float* s_w = &s_o[0][0][0];       // reuse: [GQ][nsplit] (nsplit <= 128)
-  float* s_lm = s_w + GQ * nsplit;  //        [GQ][nsplit]
+  float* s_ms = &s_o[0][0][0];        // reuse: [GQ][nsplit] (nsplit <= 128)
+  float* s_ls = s_ms + GQ * nsplit;   //        [GQ][nsplit]
   for (int idx = threadIdx.x; idx < GQ * nsplit; idx += NT) {
     const int h = idx / nsplit, sp = idx % nsplit;
-    s_w[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D]);
-    s_lm[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D + 1]);
+    s_ms[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D]);
+    s_ls[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D + 1]);
+  }
+  constexpr int kFirst = 16;
+  constexpr int kItems = (GQ * D + NT - 1) / NT;
+  float v0[kItems][kFirst];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int idx = min((int)threadIdx.x + r * NT, GQ * D - 1);
+    const float* ps = pb + (size_t)(idx / D) * (D + 2) + idx % D;
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u)
+      v0[r][u] = ld_agent(ps + (size_t)min(u, nsplit - 1) * GQ * (D + 2));
   }
   __syncthreads();
-  if (threadIdx.x < GQ) {
-    const int h = threadIdx.x;
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_w[h * nsplit + sp]);
-    float L = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float f = M == -INFINITY ? 0.f : exp2f(s_w[h * nsplit + sp] - M);
-      L += f * s_lm[h * nsplit + sp];
-      s_w[h * nsplit + sp] = f;
-    }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) s_w[h * nsplit + sp] *= inv;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < GQ * D; idx += NT) {
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int idx = threadIdx.x + r * NT;
+    if (idx >= GQ * D) break;
     const int h = idx / D, d = idx % D;
-    const float* ps = pb + (size_t)h * (D + 2) + d;
-    const float* wh = s_w + h * nsplit;
-    float O = 0.f;
-    int sp = 0;
-    for (; sp + 16 <= nsplit; sp += 16) {   // sixteen independent loads in flight
-      float v[16];
+    const float* ms = s_ms + h * nsplit;
+    const float* ls = s_ls + h * nsplit;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ms[sp]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = ld_agent(ps + (size_t)(sp + u) * GQ * (D + 2));
-#pragma unroll
-      for (int u = 0; u < 16; ++u) O = fmaf(wh[sp + u], v[u], O);
+      for (int u = 0; u < kFirst; ++u) {
+        if (u < nsplit) {
+          const float f = exp2f(ms[u] - M);
+          L += f * ls[u];
+          O = fmaf(f, v0[r][u], O);
+        }
+      }
+      const float* ps = pb + (size_t)h * (D + 2) + d;
+      for (int sp = kFirst; sp < nsplit; ++sp) {
+        const float f = exp2f(ms[sp] - M);
+        L += f * ls[sp];
+        O = fmaf(f, ld_agent(ps + (size_t)sp * GQ * (D + 2)), O);
+      }
     }
-    for (; sp < nsplit; ++sp) O = fmaf(wh[sp], ld_agent(ps + (size_t)sp * GQ * (D + 2)), O);
-    out[h * D + d] = f2h_a(O);
+    out[h * D + d] = f2h_a(L > 0.f ? O / L : 0.f);
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
