@@ -67,6 +67,20 @@ def test_ragged_contexts_all_tails(d, hq, hkv):
     assert_close(got, runs.attention_batch(w, q, k, v), f"ragged d={d} gqa={hq // hkv}")
 
 
+@pytest.mark.parametrize("ctx", [300, 4000, 16384])
+def test_many_splits_reach_the_merge(ctx):
+    """One sequence, one KV head: the context is split into 3, 32 and 128
+    splits of 8 pages, so the merging workgroup combines every count of
+    partials up to its limit (128), with a partial last page."""
+    sh = wl.Shape(hidden=896, n_heads=7, n_kv_heads=1, head_dim=128, ffn=8, vocab=8, n_layers=1)
+    w = wl.custom("splits", 66, sh, [ctx - 5])
+    q = w.attn_q()
+    k, v = w.kv(0)
+    poison(k, v, w.page_tables, w.ctx_lens)
+    got = run_attn(q, k, v, w.page_tables, w.ctx_lens, 7, 1, 128)
+    assert_close(got, runs.attention_batch(w, q, k, v), f"{ctx - 5} tokens")
+
+
 def test_tail_poison_does_not_change_the_result():
     w = wl.custom("tails", 61, wl.QWEN7B, [17, 31, 200, 333, 1000], 0)
     q = w.attn_q()

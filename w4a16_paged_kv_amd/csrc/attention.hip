@@ -329,16 +329,22 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
              (uint32_t)(nsplit - 1);
   __syncthreads();
   if (!s_last) return;
-  // One pass: (m, l) of every (head, split) go to LDS while each thread's
-  // first sixteen partial outputs are already in flight; every thread then
-  // forms the merge weights of its own head from LDS.
+  // One pass: wavefront h loads (m, l) of head h for every split while each
+  // thread's first sixteen partial outputs are already in flight; the
+  // wavefront reduces them on the VALU and leaves the merge weights
+  // w[h][s] = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s' in LDS.
   const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * (D + 2);
-  float* s_ms = &s_o[0][0][0];        // reuse: [GQ][nsplit] (nsplit <= 128)
-  float* s_ls = s_ms + GQ * nsplit;   //        [GQ][nsplit]
-  for (int idx = threadIdx.x; idx < GQ * nsplit; idx += NT) {
-    const int h = idx / nsplit, sp = idx % nsplit;
-    s_ms[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D]);
-    s_ls[idx] = ld_agent(&pb[((size_t)sp * GQ + h) * (D + 2) + D + 1]);
+  float* s_w = &s_o[0][0][0];  // reuse: [GQ][nsplit] (nsplit <= 128)
+  float mm[2] = {-INFINITY, -INFINITY}, ll[2] = {0.f, 0.f};
+  if (wave < GQ) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sp = lane + 64 * r;
+      if (sp < nsplit) {
+        mm[r] = ld_agent(&pb[((size_t)sp * GQ + wave) * (D + 2) + D]);
+        ll[r] = ld_agent(&pb[((size_t)sp * GQ + wave) * (D + 2) + D + 1]);
+      }
+    }
   }
   constexpr int kFirst = 16;
   constexpr int kItems = (GQ * D + NT - 1) / NT;
@@ -351,34 +357,42 @@ __global__ __launch_bounds__(kAttnWaves * 64) void paged_attn_kernel(AttnArgs a)
     for (int u = 0; u < kFirst; ++u)
       v0[r][u] = ld_agent(ps + (size_t)min(u, nsplit - 1) * GQ * (D + 2));
   }
+  if (wave < GQ) {
+    float M = fmaxf(mm[0], mm[1]);
+    M = fmaxf(M, ror4(M));
+    M = fmaxf(M, ror8(M));
+    M = fmaxf(M, bits_f(__builtin_amdgcn_update_dpp(0, f_bits(M), 0xB1, 0xF, 0xF, false)));
+    M = fmaxf(M, bits_f(__builtin_amdgcn_update_dpp(0, f_bits(M), 0x4E, 0xF, 0xF, false)));
+    M = rows_max(M);
+    const float f0 = M == -INFINITY ? 0.f : exp2f(mm[0] - M);
+    const float f1 = M == -INFINITY ? 0.f : exp2f(mm[1] - M);
+    float L = f0 * ll[0] + f1 * ll[1];
+    L += ror4(L);
+    L += ror8(L);
+    L += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(L), 0xB1, 0xF, 0xF, false));
+    L += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(L), 0x4E, 0xF, 0xF, false));
+    L = rows_sum(L);
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sp = lane + 64 * r;
+      if (sp < nsplit) s_w[wave * nsplit + sp] = (r ? f1 : f0) * inv;
+    }
+  }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const int idx = threadIdx.x + r * NT;
     if (idx >= GQ * D) break;
     const int h = idx / D, d = idx % D;
-    const float* ms = s_ms + h * nsplit;
-    const float* ls = s_ls + h * nsplit;
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ms[sp]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
+    const float* wh = s_w + h * nsplit;
+    float O = 0.f;
 #pragma unroll
-      for (int u = 0; u < kFirst; ++u) {
-        if (u < nsplit) {
-          const float f = exp2f(ms[u] - M);
-          L += f * ls[u];
-          O = fmaf(f, v0[r][u], O);
-        }
-      }
-      const float* ps = pb + (size_t)h * (D + 2) + d;
-      for (int sp = kFirst; sp < nsplit; ++sp) {
-        const float f = exp2f(ms[sp] - M);
-        L += f * ls[sp];
-        O = fmaf(f, ld_agent(ps + (size_t)sp * GQ * (D + 2)), O);
-      }
-    }
-    out[h * D + d] = f2h_a(L > 0.f ? O / L : 0.f);
+    for (int u = 0; u < kFirst; ++u)
+      if (u < nsplit) O = fmaf(wh[u], v0[r][u], O);
+    const float* ps = pb + (size_t)h * (D + 2) + d;
+    for (int sp = kFirst; sp < nsplit; ++sp) O = fmaf(wh[sp], ld_agent(ps + (size_t)sp * GQ * (D + 2)), O);
+    out[h * D + d] = f2h_a(O);
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
