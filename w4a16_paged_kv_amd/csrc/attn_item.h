@@ -1,0 +1,410 @@
+// Paged-attention decode as device code (one work item on one workgroup),
+// shared by the attention kernel and the persistent layer kernel.
+//
+// The KV cache is split into 16-token pages addressed through a page table
+// ("Building a Custom LLM Inference Runtime on H100", The KV Cache and
+// PagedAttention; "How to build your own LLM runtime from scratch",
+// Architectural decisions and optimizations: 16-token pages, 4 KiB per head
+// slice, GQA 7:1). Logical token t of sequence b lives in page
+// page_tables[b][t / 16], slot t % 16 (same page, The Three Critical Bugs,
+// Bug 1).
+//
+// A work item is (split of consecutive pages, KV head, sequence). Each of
+// eight wavefronts streams whole pages: one (page, KV head) K slice and V
+// slice is read from HBM once and used for all GQ query heads of the group.
+// Softmax is online, in fp32 and base 2. The item writes its un-normalised
+// (o, m, l) partial; the last item of a (sequence, KV head) to finish merges
+// all partials with a log-sum-exp reduction and writes fp16 o. Every barrier
+// sits in uniform control flow (the same page's Bug list warns against
+// barriers inside divergent branches).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "gemv_b1.h"
+
+namespace w4 {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2_t as_h2a(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+__device__ __forceinline__ uint16_t f2h_a(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Device-scope relaxed accesses: coherent across the XCDs' L2 caches.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time each
+
+__device__ __forceinline__ int f_bits(float v) { return __builtin_bit_cast(int, v); }
+__device__ __forceinline__ float bits_f(int v) { return __builtin_bit_cast(float, v); }
+
+// Cross-lane reductions on the VALU rather than through LDS permutes:
+// DPP row rotates inside a 16-lane row, v_permlane16_swap / v_permlane32_swap
+// across rows. row4: lanes i, i+4, i+8, i+12 of a row; rows: lanes i, i^16,
+// i^32, i^48; ror8 alone pairs lanes i and i^8 of a row.
+__device__ __forceinline__ float ror4(float v) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float ror8(float v) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
+  v = fmaxf(bits_f(a[0]), bits_f(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
+  return fmaxf(bits_f(b[0]), bits_f(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
+  v = bits_f(a[0]) + bits_f(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
+  return bits_f(b[0]) + bits_f(b[1]);
+}
+__device__ __forceinline__ float page_max(float v) {  // over the 16 tokens of a page (same lane % 4)
+  v = fmaxf(v, ror4(v));
+  v = fmaxf(v, ror8(v));
+  return rows_max(v);
+}
+__device__ __forceinline__ float page_sum(float v) {
+  v += ror4(v);
+  v += ror8(v);
+  return rows_sum(v);
+}
+
+// One work item (split of pages, KV head, sequence) on one workgroup of NT
+// threads. The first kAttnWaves wavefronts stream pages; any further
+// wavefronts only take part in the cooperative loops and the barriers, so
+// every barrier stays in workgroup-uniform control flow (the item decides
+// every early return). Queries and K/V are read coherently (they may have
+// been written earlier in the same launch), outputs and partials are stored
+// coherently.
+template <int D, int GQ, int NT>
+__device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(GQ >= 1 && GQ <= 8, "group");
+  static_assert(NT >= kAttnWaves * 64 && NT % 64 == 0, "threads");
+  constexpr int W = kAttnWaves;
+  constexpr int NI = D / 32;          // 8-column sub-chunks per lane for scores
+  constexpr int LD = D / 8;           // lanes per token row for PV (8 columns each)
+  constexpr int TPI = 64 / LD;        // token rows per PV load instruction
+  constexpr int NTOK = kPage / TPI;   // tokens per lane for PV
+  __shared__ float s_m[W][8], s_l[W][8];
+  __shared__ __align__(16) float s_pb[W][kPage][8];  // per-wavefront softmax weights [token][head]
+  __shared__ __align__(16) float s_al[W][8];         // per-wavefront rescale factors [head]
+  __shared__ float s_o[W][GQ][D];
+  __shared__ __align__(16) uint16_t s_q[GQ * D];     // the group's query heads
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool pager = wave < W;  // this wavefront streams pages
+  const int32_t* pt = a.page_tables + (size_t)b * a.max_pages;
+  // the context length, this wavefront's first two page ids and the queries
+  // are independent: issue them together (page ids are validated below)
+  const int pw0 = split * a.pages_per_split + wave;
+  int pid_cur = pt[min(pw0, a.max_pages - 1)];
+  int pid_nxt = pt[min(pw0 + W, a.max_pages - 1)];
+  int ctx = a.ctx_lens[b];
+  const __amdgpu_buffer_rsrc_t rq = coherent_rsrc(a.q + (size_t)b * a.q_stride + (size_t)kvh * GQ * D);
+  u4_t qv[(GQ * D + NT * 8 - 1) / (NT * 8)];
+#pragma unroll
+  for (int r = 0; r < (GQ * D + NT * 8 - 1) / (NT * 8); ++r) {
+    const int i = min((int)(threadIdx.x + r * NT) * 8, GQ * D - 8);
+    qv[r] = ld128_agent(rq, 2 * i);
+  }
+  ctx = ctx < 0 ? 0 : (ctx > a.max_pages * kPage ? a.max_pages * kPage : ctx);
+  const int npages = (ctx + kPage - 1) / kPage;
+  const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
+  uint16_t* out = a.out + (size_t)b * a.out_stride + (size_t)kvh * GQ * D;
+  if (npages == 0) {  // empty context: zeros
+    if (split == 0)
+      for (int i = threadIdx.x; i < GQ * D; i += NT) st16_agent(out + i, 0);
+    return;
+  }
+  if (split >= nsplit) return;
+  const int p_begin = split * a.pages_per_split;
+  const int p_end = min(npages, p_begin + a.pages_per_split);
+
+  // the group's queries go to LDS (read per head per page); lane
+  // (tk = lane >> 2, c = lane & 3) covers columns 8c + 32i .. +8 of token tk
+#pragma unroll
+  for (int r = 0; r < (GQ * D + NT * 8 - 1) / (NT * 8); ++r) {
+    const int i = (int)(threadIdx.x + r * NT) * 8;
+    if (i < GQ * D) *reinterpret_cast<u4_t*>(&s_q[i]) = qv[r];
+  }
+  __syncthreads();
+  const int tk = lane >> 2, c = lane & 3;
+
+  const float scale = kLog2e / sqrtf((float)D);
+  const int hA = c, hB = c + 4;            // heads whose softmax state this lane keeps
+  float mA = -INFINITY, mB = -INFINITY, lA = 0.f, lB = 0.f;
+  float o[GQ][8];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  const int d0 = 8 * (lane % LD);          // PV columns of this lane
+  const int t0 = lane / LD;                // first PV token row of this lane
+  const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
+
+  // page p's id, validated (an invalid id is counted and read as page 0,
+  // with no valid tokens)
+  auto checked = [&](int p, int id, int& valid) {
+    const bool bad = id < 0 || id >= a.num_pages;
+    if (bad && lane == 0) atomicAdd(a.err, 1u);
+    valid = bad ? 0 : min(kPage, ctx - p * kPage);
+    return bad ? 0 : id;
+  };
+  u4_t kf[NI], vf[NTOK], kn[NI], vn[NTOK];
+  auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
+    page = __builtin_amdgcn_readfirstlane(page);  // one page per wavefront: keeps the resources scalar
+    const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
+    const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kk[i] = ld128_agent(rk, 2 * (tk * D + 8 * c + 32 * i));
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) vv[i] = ld128_agent(rv, 2 * ((t0 + TPI * i) * D + d0));
+  };
+  int valid_cur = 0, valid_nxt = 0;
+  const int p_stop = pager ? p_end : pw0;  // non-page wavefronts skip the loop
+  if (pw0 < p_stop) load_kv(checked(pw0, pid_cur, valid_cur), kf, vf);
+  for (int p = pw0; p < p_stop; p += W) {
+    const int valid = valid_cur;
+    if (p + W < p_stop) {
+      load_kv(checked(p + W, pid_nxt, valid_nxt), kn, vn);
+      pid_nxt = pt[min(p + 2 * W, a.max_pages - 1)];  // the page after, one step ahead
+    }
+
+    // scores of token tk for every head of the group (quad reduction over c)
+    float s[GQ];
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const u4_t qq = *reinterpret_cast<const u4_t*>(&s_q[h * D + 8 * c + 32 * i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(as_h2a(qq[e]), as_h2a(kf[i][e]), acc, false);
+      }
+      acc += dpp_xor1(acc);
+      acc += dpp_xor2(acc);
+      s[h] = acc * scale;
+    }
+    float sA = -INFINITY, sB = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      if (h == hA) sA = s[h];
+      if (h == hB) sB = s[h];
+    }
+    if (tk >= valid) {
+      sA = -INFINITY;
+      sB = -INFINITY;
+    }
+    // page maximum and sum over the 16 tokens (lanes sharing c)
+    const float pmA = page_max(sA), pmB = page_max(sB);
+    const float nA = fmaxf(mA, pmA), nB = fmaxf(mB, pmB);
+    const float alA = nA == -INFINITY ? 1.f : exp2f(mA - nA);
+    const float alB = nB == -INFINITY ? 1.f : exp2f(mB - nB);
+    const float pA = nA == -INFINITY ? 0.f : exp2f(sA - nA);
+    const float pB = nB == -INFINITY ? 0.f : exp2f(sB - nB);
+    lA = lA * alA + page_sum(pA);
+    lB = lB * alB + page_sum(pB);
+    mA = nA;
+    mB = nB;
+    // broadcast weights and rescale factors to the PV lanes through LDS
+    // (wavefront-private rows; LDS operations of a wavefront stay in order)
+    s_pb[wave][tk][hA] = pA;
+    s_pb[wave][tk][hB] = pB;
+    if (lane < 4) {
+      s_al[wave][hA] = alA;
+      s_al[wave][hB] = alB;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // masked tokens contribute nothing even if their slots hold NaN
+    if (valid < kPage) {
+#pragma unroll
+      for (int i = 0; i < NTOK; ++i)
+        if (t0 + TPI * i >= valid) vf[i] = (u4_t){0u, 0u, 0u, 0u};
+    }
+    const f4v al0 = *reinterpret_cast<const f4v*>(&s_al[wave][0]);
+    const f4v al1 = *reinterpret_cast<const f4v*>(&s_al[wave][4]);
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      const float al = h < 4 ? al0[h & 3] : al1[h & 3];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= al;
+    }
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+      const f4v p0 = *reinterpret_cast<const f4v*>(&s_pb[wave][t0 + TPI * i][0]);
+      const f4v p1 = *reinterpret_cast<const f4v*>(&s_pb[wave][t0 + TPI * i][4]);
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        const float pv = h < 4 ? p0[h & 3] : p1[h & 3];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2_t v2 = as_h2a(vf[i][e]);
+          o[h][2 * e] = fmaf(pv, (float)v2[0], o[h][2 * e]);
+          o[h][2 * e + 1] = fmaf(pv, (float)v2[1], o[h][2 * e + 1]);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kf[i] = kn[i];
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) vf[i] = vn[i];
+    valid_cur = valid_nxt;
+  }
+  // reduce o over the lanes holding other token rows of the same columns
+  // (lanes d apart by multiples of LD: 16 for D = 128, 8 for D = 64)
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = o[h][e];
+      if (LD == 8) v += ror8(v);
+      o[h][e] = rows_sum(v);
+    }
+  if (pager && lane < 4) {
+    s_m[wave][hA] = mA;
+    s_l[wave][hA] = lA;
+    s_m[wave][hB] = mB;
+    s_l[wave][hB] = lB;
+  }
+  if (pager && lane < LD)
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[wave][h][d0 + e] = o[h][e];
+  __syncthreads();
+
+  // combine the wavefronts: this split's (o, m, l), or the output if one split
+  float* part = a.partials + (((size_t)b * a.n_kv_heads + kvh) * a.max_splits + split) * GQ * (D + 2);
+  for (int idx = threadIdx.x; idx < GQ * D; idx += NT) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float f = exp2f(s_m[w][h] - M);
+        L += f * s_l[w][h];
+        O += f * s_o[w][h][d];
+      }
+    }
+    if (nsplit == 1) {
+      st16_agent(out + h * D + d, f2h_a(L > 0.f ? O / L : 0.f));
+    } else {
+      st_agent(&part[h * (D + 2) + d], O);
+      if (d == 0) {
+        st_agent(&part[h * (D + 2) + D], M);
+        st_agent(&part[h * (D + 2) + D + 1], L);
+      }
+    }
+  }
+  if (nsplit == 1) return;
+  // The last split to arrive merges (log-sum-exp over splits). Partials move
+  // between workgroups, possibly on different XCDs, through device-scope
+  // (coherent) stores and loads, so no L2 writeback or invalidate is needed:
+  // each workgroup waits for its stores to complete before it counts itself.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* counter = a.counters + (size_t)b * a.n_kv_heads + kvh;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(nsplit - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // One pass: wavefront h loads (m, l) of head h for every split while each
+  // thread's first sixteen partial outputs are already in flight; the
+  // wavefront reduces them on the VALU and leaves the merge weights
+  // w[h][s] = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s' in LDS.
+  const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * (D + 2);
+  float* s_w = &s_o[0][0][0];  // reuse: [GQ][nsplit] (nsplit <= 128)
+  float mm[2] = {-INFINITY, -INFINITY}, ll[2] = {0.f, 0.f};
+  if (wave < GQ) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sp = lane + 64 * r;
+      if (sp < nsplit) {
+        mm[r] = ld_agent(&pb[((size_t)sp * GQ + wave) * (D + 2) + D]);
+        ll[r] = ld_agent(&pb[((size_t)sp * GQ + wave) * (D + 2) + D + 1]);
+      }
+    }
+  }
+  constexpr int kFirst = 16;
+  constexpr int kItems = (GQ * D + NT - 1) / NT;
+  float v0[kItems][kFirst];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int idx = min((int)threadIdx.x + r * NT, GQ * D - 1);
+    const float* ps = pb + (size_t)(idx / D) * (D + 2) + idx % D;
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u)
+      v0[r][u] = ld_agent(ps + (size_t)min(u, nsplit - 1) * GQ * (D + 2));
+  }
+  if (wave < GQ) {
+    float M = fmaxf(mm[0], mm[1]);
+    M = fmaxf(M, ror4(M));
+    M = fmaxf(M, ror8(M));
+    M = fmaxf(M, bits_f(__builtin_amdgcn_update_dpp(0, f_bits(M), 0xB1, 0xF, 0xF, false)));
+    M = fmaxf(M, bits_f(__builtin_amdgcn_update_dpp(0, f_bits(M), 0x4E, 0xF, 0xF, false)));
+    M = rows_max(M);
+    const float f0 = M == -INFINITY ? 0.f : exp2f(mm[0] - M);
+    const float f1 = M == -INFINITY ? 0.f : exp2f(mm[1] - M);
+    float L = f0 * ll[0] + f1 * ll[1];
+    L += ror4(L);
+    L += ror8(L);
+    L += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(L), 0xB1, 0xF, 0xF, false));
+    L += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(L), 0x4E, 0xF, 0xF, false));
+    L = rows_sum(L);
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int sp = lane + 64 * r;
+      if (sp < nsplit) s_w[wave * nsplit + sp] = (r ? f1 : f0) * inv;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int idx = threadIdx.x + r * NT;
+    if (idx >= GQ * D) break;
+    const int h = idx / D, d = idx % D;
+    const float* wh = s_w + h * nsplit;
+    float O = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFirst; ++u)
+      if (u < nsplit) O = fmaf(wh[u], v0[r][u], O);
+    const float* ps = pb + (size_t)h * (D + 2) + d;
+    for (int sp = kFirst; sp < nsplit; ++sp) O = fmaf(wh[sp], ld_agent(ps + (size_t)sp * GQ * (D + 2)), O);
+    st16_agent(out + h * D + d, f2h_a(O));
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace w4

@@ -1,0 +1,416 @@
+// Batch-1 W4A16 GEMV as device code: the pieces the per-projection kernel
+// and the persistent layer kernel share (activation staging, the MFMA block
+// product, fused epilogues and the per-wavefront streaming worker).
+//
+// Weights: symmetric group-wise INT4, group 128 along the input dimension,
+// dequantised value q * s ("How to build your own LLM runtime from
+// scratch", Architectural decisions and optimizations). RMSNorm stays in
+// FP16 (same section).
+//
+// Activations and outputs cross workgroups (and XCDs, whose L2 caches are
+// not coherent with each other): every activation load and every output
+// store here is device-coherent (sc1), which costs nothing measurable for
+// these few kilobytes and lets the same code run inside one launch that
+// spans several operations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "w4_internal.h"
+
+namespace w4 {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h2f(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
+__device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+// Nibbles at bits 4i and 16+4i of a packed word -> the exact fp16 pair
+// (q_{2i}, q_{2i+1}). 0x6400 is 1024.0; its ulp is 1, so 0x6400|u == 1024+u.
+__device__ __forceinline__ h2_t nib_pair(uint32_t word, int i) {
+  const uint32_t v = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+  return __builtin_bit_cast(h2_t, v) - (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+}
+
+__device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Device-coherent accesses: 16-bit stores and loads through the atomic
+// builtins, 16-byte loads through a buffer resource with the sc1 policy bit.
+__device__ __forceinline__ void st16_agent(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint16_t ld16_agent(const uint16_t* p) {
+  return __hip_atomic_load(const_cast<uint16_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+constexpr int kPolicySc1 = 16;  // buffer instruction cache-policy operand: sc1
+__device__ __forceinline__ u4_t ld128_agent(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kPolicySc1));
+}
+
+// ------------------------------------------------------------- epilogues
+
+__device__ __forceinline__ void kv_store(const QkvEpilogue& e, uint16_t* pool, int slot, int kvh, int dim0,
+                                         int dim1, float v0, float v1) {
+  if (slot < 0) return;  // invalid position or page: counted by the token plan
+  uint16_t* dst = pool + (((size_t)(slot >> 4) * e.n_kv_heads + kvh) * kPage + (slot & 15)) * e.head_dim;
+  st16_agent(dst + dim0, f2h(v0));
+  st16_agent(dst + dim1, f2h(v1));
+}
+
+// Rows i and i+8 of tile t hold the rotate-half RoPE pair (dim0, dim0 + D/2)
+// of one head (QKV packing role).
+__device__ __forceinline__ int qkv_head(const QkvEpilogue& e, int t) { return (kTileRows * t) / e.head_dim; }
+__device__ __forceinline__ int qkv_dim0(const QkvEpilogue& e, int t, int i) {
+  return 8 * (((kTileRows * t) % e.head_dim) / kTileRows) + i;
+}
+
+// q/k heads are rotated by (c, sn), the token plan's rotation of the pair
+// (angle pos * base^(-2 dim0 / D)), and rounded once to fp16; v heads are
+// rounded unrotated. k/v go to the token's page slot.
+__device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float y1, float c, float sn,
+                        int slot) {
+  const QkvEpilogue& e = a.qkv;
+  const int D = e.head_dim;
+  const int head = qkv_head(e, t);
+  const int dim0 = qkv_dim0(e, t, i), dim1 = D / 2 + dim0;
+  if (e.bias) {
+    y0 += h2f(e.bias[head * D + dim0]);
+    y1 += h2f(e.bias[head * D + dim1]);
+  }
+  if (head < e.n_heads + e.n_kv_heads) {
+    const float r0 = y0 * c - y1 * sn;
+    const float r1 = y1 * c + y0 * sn;
+    if (head < e.n_heads) {
+      uint16_t* q = e.q_out + (size_t)m * e.q_stride + head * D;
+      st16_agent(q + dim0, f2h(r0));
+      st16_agent(q + dim1, f2h(r1));
+    } else {
+      kv_store(e, e.k_pool, slot, head - e.n_heads, dim0, dim1, r0, r1);
+    }
+  } else {
+    kv_store(e, e.v_pool, slot, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ constexpr int epi_items() {
+  return (EPI == EPI_SILU || EPI == EPI_QKV) ? 8 : 16;
+}
+
+// Applies the epilogue to item i of tile t for batch row m; vals[16] are the
+// fp32 results of the tile's 16 physical rows.
+template <int EPI>
+__device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i, const float* vals) {
+  if (EPI == EPI_QKV) {
+    const int pair = qkv_dim0(a.qkv, t, i);
+    const float* cs = a.qkv.rope + ((size_t)m * (a.qkv.head_dim / 2) + pair) * 2;
+    epi_qkv(a, m, t, i, vals[i], vals[i + 8], cs[0], cs[1], a.qkv.slot[m]);
+  } else if (EPI == EPI_SILU) {
+    const int o = 8 * t + i;
+    if (o < a.n / 2) {
+      const float g = vals[i], u = vals[i + 8];
+      st16_agent(a.y + (size_t)m * a.y_stride + o, f2h(g / (1.0f + expf(-g)) * u));
+    }
+  } else {
+    const int row = kTileRows * t + i;
+    if (row < a.n) {
+      float v = vals[i];
+      if (EPI == EPI_RESID) v += h2f(ld16_agent(a.resid + (size_t)m * a.y_stride + row));
+      st16_agent(a.y + (size_t)m * a.y_stride + row, f2h(v));
+    }
+  }
+}
+
+// ------------------------------------------------------------ batch 1, MFMA
+// The 16 bytes a lane holds of a packed block are already the B operand of
+// v_mfma_f32_16x16x32_f16 (weight row l & 15, eight k-slots per lane group
+// l >> 4), so batch 1 runs on the matrix cores too: A carries the activation
+// row (A rows 1..15 are don't-care) and D row 0 comes out in lanes 0..15.
+//
+// Dequantisation stays exact: 0x6400 | u is 1024 + u in fp16 (ulp 1), so
+// OR-ing a nibble pair masked with 0x000F000F into 0x64006400 and
+// subtracting 1032 gives (q, q'); the pair four bits higher (mask 0x00F000F0)
+// gives 16q after subtracting 1152, and the activations paired with those
+// slots are staged divided by 16. One AND-OR and one packed subtract per
+// weight pair; the multiply-accumulate runs on the matrix cores.
+//
+// A workgroup of WAVES wavefronts covers WAVES/S tiles; the S wavefronts of a
+// tile take its 128-column groups round-robin (K split inside the workgroup),
+// so small matrices still put thousands of wavefronts on the chip and large
+// ones keep the activation prologue amortised over several tiles. Each
+// wavefront streams its blocks U at a time with the next U loads in flight.
+
+constexpr int kUnroll = 4;  // blocks per batch; two batches in flight
+
+constexpr uint32_t kMaskLo = 0x000F000Fu;  // nibble offsets (0,1) / (4,5) of a word
+constexpr uint32_t kMaskHi = 0x00F000F0u;  // nibble offsets (2,3) / (6,7), as 16u
+
+// Activation staging for the MFMA path works in slot groups: slot group sg
+// is the 8 k-slots of MFMA r = sg % 4 in 32-column chunk c = sg / 4, i.e.
+// xs[8 sg .. 8 sg + 8). Its columns sit in the two 8-column words
+// j0 = 2 (r / 2) and j0 + 1 of the chunk, at offsets 2 (r % 2) + {0, 1, 4, 5}:
+// 32-bit pairs e = r % 2 and e + 2 of each word. A thread loads natural
+// 8-column word wd = tid + it * NT (it < IT) of x (and of the RMSNorm
+// weights) ahead of the weight stream, normalises it and builds slot group
+// sg = wd from the words of its own 4-lane quad (the quad of lanes 4c..4c+3
+// holds chunk c) with DPP quad permutes.
+
+template <int IT, bool NORM>
+struct StageRegs {
+  u4_t x[IT], g[NORM ? IT : 1];
+};
+
+template <int IT, bool NORM>
+__device__ __forceinline__ void stage_load(StageRegs<IT, NORM>& r, const uint16_t* __restrict__ x,
+                                           const uint16_t* __restrict__ gamma, int k, int NT) {
+  // unconditional loads from clamped addresses (a branch around a load makes
+  // the compiler wait for it on the spot); words past k are zeroed after the
+  // wait, in stage_row_mfma. x may have been written by other workgroups of
+  // the same launch, so it is read coherently.
+  const __amdgpu_buffer_rsrc_t rx = coherent_rsrc(x);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int c = min(8 * (threadIdx.x + it * NT), k - 8);
+    r.x[it] = ld128_agent(rx, 2 * c);
+    if (NORM) r.g[it] = *reinterpret_cast<const u4_t*>(gamma + c);
+  }
+}
+
+__device__ __forceinline__ uint32_t quad_perm(uint32_t v, int ctrl_is_odd) {
+  // quad_perm [0,0,2,2] (0xA0) or [1,1,3,3] (0xF5)
+  return ctrl_is_odd ? (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xF5, 0xF, 0xF, false)
+                     : (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xA0, 0xF, 0xF, false);
+}
+
+// Stages the row: with NORM it becomes fp16(x * rsqrt(mean(x^2) + eps) *
+// gamma) (RMSNorm in FP16); the slots of odd r are divided by 16 (exact
+// fp16 scaling). The natural-order (normalised) row also goes to xn_out if
+// given. Ends with a barrier. Requires kpad <= 8 * IT * NT.
+template <int IT, bool NORM>
+__device__ void stage_row_mfma(const StageRegs<IT, NORM>& r, float eps, int k, int kpad, uint16_t* xs,
+                               float* red, uint16_t* xn_out, const int NT) {
+  // every use of the loaded words comes first, in straight-line code: a
+  // branch here would make the compiler wait for all loads in flight,
+  // weights included
+  const int tid = threadIdx.x;
+  const int e = tid & 1;                      // r % 2 of this lane's slot groups (NT % 4 == 0)
+  u4_t xv[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const bool in = 8 * (tid + it * NT) < k;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) xv[it][d] = in ? r.x[it][d] : 0u;
+  }
+  float rs = 1.f;
+  if (NORM) {
+    float ss = 0.f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const h2_t v = as_h2(xv[it][d]);
+        ss = fmaf((float)v[0], (float)v[0], ss);
+        ss = fmaf((float)v[1], (float)v[1], ss);
+      }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < NT / 64; ++w) tot += red[w];
+    rs = 1.0f / sqrtf(tot / (float)k + eps);
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const h2_t hv = as_h2(xv[it][d]), hg = as_h2(r.g[it][d]);
+        h2_t v;
+        v[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
+        v[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
+        xv[it][d] = __builtin_bit_cast(uint32_t, v);
+      }
+  }
+  const h2_t sc = e ? (h2_t){(_Float16)0.0625f, (_Float16)0.0625f} : (h2_t){(_Float16)1.0f, (_Float16)1.0f};
+  u4_t o[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    // words j0 (lanes {0,0,2,2} of the quad) and j0 + 1 (lanes {1,1,3,3})
+    const uint32_t a0 = quad_perm(xv[it][0], 0), a1 = quad_perm(xv[it][1], 0);
+    const uint32_t a2 = quad_perm(xv[it][2], 0), a3 = quad_perm(xv[it][3], 0);
+    const uint32_t b0 = quad_perm(xv[it][0], 1), b1 = quad_perm(xv[it][1], 1);
+    const uint32_t b2 = quad_perm(xv[it][2], 1), b3 = quad_perm(xv[it][3], 1);
+    o[it][0] = __builtin_bit_cast(uint32_t, as_h2(e ? a1 : a0) * sc);
+    o[it][1] = __builtin_bit_cast(uint32_t, as_h2(e ? a3 : a2) * sc);
+    o[it][2] = __builtin_bit_cast(uint32_t, as_h2(e ? b1 : b0) * sc);
+    o[it][3] = __builtin_bit_cast(uint32_t, as_h2(e ? b3 : b2) * sc);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int wd = tid + it * NT;
+    if (8 * wd < kpad) *reinterpret_cast<u4_t*>(xs + 8 * wd) = o[it];
+    if (xn_out && 8 * wd < k) *reinterpret_cast<u4_t*>(xn_out + 8 * wd) = xv[it];
+  }
+  __syncthreads();
+}
+
+// A constant held in a VGPR, so v_and_or_b32 can pair it with an SGPR operand.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+// Sum over one block of q * x for weight row lane & 15: d[0] of lanes 0..15
+// after four chained MFMAs over the lane group's staged chunk xl.
+__device__ __forceinline__ float mfma_block_b1(const u4_t w, const uint16_t* __restrict__ xl, uint32_t mlo,
+                                               uint32_t mhi) {
+  const u4_t* xp = reinterpret_cast<const u4_t*>(xl);
+  f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t m = (r & 1) ? mhi : mlo;
+    const h2_t bias = (r & 1) ? (h2_t){(_Float16)1152.0f, (_Float16)1152.0f}
+                              : (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t w0 = w[2 * (r >> 1)], w1 = w[2 * (r >> 1) + 1];
+    auto q2 = [&](uint32_t v) {
+      return __builtin_bit_cast(uint32_t, as_h2((v & m) | 0x64006400u) - bias);
+    };
+    const u4_t b = {q2(w0), q2(w0 >> 8), q2(w1), q2(w1 >> 8)};
+    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xp[r]), __builtin_bit_cast(h8_t, b),
+                                               d, 0, 0, 0);
+  }
+  return d[0];
+}
+
+// The QKV epilogue's per-thread RoPE rotation and the token's K/V slot
+// (token plan, written by an earlier launch): thread i < tw * 8 of virtual
+// workgroup vb rotates pair i % 8 of tile vb * tw + i / 8.
+struct QkvPre {
+  float c, s;
+  int slot;
+};
+
+template <int EPI>
+__device__ __forceinline__ QkvPre qkv_pre(const GemvArgs& a, int vb, int tw) {
+  QkvPre p{1.f, 0.f, -1};
+  if (EPI == EPI_QKV && (int)threadIdx.x < tw * 8) {
+    const int tt = vb * tw + threadIdx.x / 8;
+    if (tt < a.tiles) {
+      const int pair = qkv_dim0(a.qkv, tt, threadIdx.x % 8);
+      const float2 cs = *reinterpret_cast<const float2*>(a.qkv.rope + 2 * pair);
+      p.c = cs.x;
+      p.s = cs.y;
+      p.slot = a.qkv.slot[0];
+    }
+  }
+  return p;
+}
+
+// LDS of one batch-1 GEMV: the staged activation row, then reductions.
+__host__ __device__ constexpr size_t gemv_b1_lds_bytes(int groups, int waves, int tw) {
+  return (size_t)groups * kGroup * 2 + (size_t)(waves * 16 + tw * 16 + waves) * 4;
+}
+
+// One wavefront's share of a batch-1 GEMV. Virtual workgroup vb covers tiles
+// vb * tw .. vb * tw + tw - 1; its working wavefront w takes tile
+// vb * tw + w / S and the 128-column groups w % S, w % S + S, ... (waves at or
+// past S * tw, and tiles past the end, take none). Weight blocks stream two
+// batches of kUnroll ahead; loads are issued unconditionally (past the
+// wavefront's last group they re-read that block) so the compiler's wait
+// counts stay exact, and scales stay fp16 in their own registers until used.
+template <int EPI, int S, int IT>
+struct GemvB1 {
+  static constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SILU;  // batch 1: RMSNorm prologue
+  int t, ks, ng, last;
+  const u4_t* wb;
+  const uint16_t* sb;
+  u4_t bufA[kUnroll], bufB[kUnroll];
+  uint32_t scA[kUnroll], scB[kUnroll];
+
+  __device__ __forceinline__ void assign(const GemvArgs& a, int vb, int tw, int w) {
+    const int lane = threadIdx.x & 63;
+    t = vb * tw + w / S;
+    ks = w % S;
+    const bool live = w >= 0 && w < S * tw && t < a.tiles;
+    ng = live ? (a.groups - ks + S - 1) / S : 0;
+    last = ng > 0 ? ng - 1 : 0;
+    const size_t base = (size_t)(live ? t : 0) * a.groups + ks;
+    wb = reinterpret_cast<const u4_t*>(a.w) + base * 64 + lane;
+    sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * a.groups * 1024) + base * 16 + (lane & 15);
+  }
+  __device__ __forceinline__ void load(u4_t* buf, uint32_t* sc, int i0) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = min(i0 + u, last);
+      buf[u] = __builtin_nontemporal_load(wb + (size_t)i * S * 64);
+      sc[u] = sb[(size_t)i * S * 16];
+    }
+  }
+  // the first batch of weight blocks: needs nothing the previous operation writes
+  __device__ __forceinline__ void prefetch() { load(bufA, scA, 0); }
+
+  // After the activation row is staged in LDS (xs): stream the remaining
+  // blocks, reduce the S wavefronts of each tile in LDS, apply the epilogue.
+  // All nt threads of the workgroup take part (the barriers are uniform).
+  __device__ void finish(const GemvArgs& a, int vb, int tw, int w, uint8_t* smem, const QkvPre& pre) {
+    const int lane = threadIdx.x & 63;
+    const int kpad = a.groups * kGroup;
+    const int waves = blockDim.x / 64;
+    const uint16_t* xs = reinterpret_cast<const uint16_t*>(smem);
+    float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);  // [waves][16]
+    float* vals = red + waves * 16;                                  // [tw][16]
+    const uint16_t* xl = xs + 32 * (lane >> 4) + ks * kGroup;
+    const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
+    float acc = 0.f;
+    auto compute = [&](const u4_t* buf, const uint32_t* sc, int i0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (i0 + u < ng) {
+          const float d = mfma_block_b1(buf[u], xl + (size_t)(i0 + u) * S * kGroup, mlo, mhi);
+          acc = fmaf(d, h2f((uint16_t)sc[u]), acc);
+        }
+    };
+    for (int i = 0; i < ng; i += 2 * kUnroll) {
+      load(bufB, scB, i + kUnroll);
+      compute(bufA, scA, i);
+      if (i + kUnroll >= ng) break;
+      load(bufA, scA, i + 2 * kUnroll);
+      compute(bufB, scB, i + kUnroll);
+    }
+    if (w >= 0 && w < S * tw && lane < 16) red[w * 16 + lane] = acc;
+    __syncthreads();
+    if ((int)threadIdx.x < tw * 16) {
+      const int tl = threadIdx.x / 16, r = threadIdx.x % 16;
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < S; ++k) v += red[(tl * S + k) * 16 + r];
+      vals[tl * 16 + r] = v;
+    }
+    __syncthreads();
+    constexpr int per = epi_items<EPI>();
+    if ((int)threadIdx.x < tw * per) {
+      const int tl = threadIdx.x / per;
+      const int tt = vb * tw + tl;
+      if (tt < a.tiles) {
+        const int i = threadIdx.x % per;
+        if (EPI == EPI_QKV)
+          epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], pre.c, pre.s, pre.slot);
+        else
+          epilogue<EPI>(a, 0, tt, i, vals + tl * 16);
+      }
+    }
+  }
+};
+
+}  // namespace w4
