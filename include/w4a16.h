@@ -206,6 +206,18 @@ void w4_model_destroy(w4_model* model);
  * (per batch size and output/input pointers) and replays it afterwards
  * [H100-graph]; 0: launch kernel by kernel. Default 1. */
 int  w4_set_graph(w4_model* model, int enabled);
+/* 1: batch-1 decode_step runs each decoder layer as one persistent launch
+ * (one 1024-thread workgroup per CU; the layer's five operations meet at
+ * grid barriers, the next operation's first weight loads issued before each
+ * barrier), with the per-operation kernels' device code and work split, so
+ * the results are bit-identical to mode 0; batch > 1 and decode_layer always
+ * use the per-operation kernels. Replaces the step's CUDA-graph capture
+ * (the step is then 30 launches). W4_EINVAL if this configuration has no
+ * persistent instantiation or the device cannot keep one such workgroup on
+ * every CU. Default 0. A barrier wait is bounded: a launch whose workgroups
+ * lose each other counts one device error (w4_device_errors) instead of
+ * hanging. */
+int  w4_set_persistent(w4_model* model, int enabled);
 
 /* One decode step for `batch` sequences. tokens, positions, ctx_lens: host
  * int32 [batch]; page_tables: host int32 [batch * max_pages_per_seq].

@@ -70,6 +70,7 @@ _SIGS = {
                                 c_size_t, c_int32, c_int32, POINTER(c_void_p)]),
     "w4_model_destroy": (None, [c_void_p]),
     "w4_set_graph": (c_int, [c_void_p, c_int]),
+    "w4_set_persistent": (c_int, [c_void_p, c_int]),
     "decode_step": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     "decode_step_device": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     "w4_device_errors": (c_int64, [c_void_p, c_void_p]),
@@ -267,6 +268,9 @@ class Model:
 
     def w4_set_graph(self, enabled: bool) -> None:
         _check(lib().w4_set_graph(self.handle, int(enabled)))
+
+    def w4_set_persistent(self, enabled: bool) -> None:
+        _check(lib().w4_set_persistent(self.handle, int(enabled)))
 
     def decode_step(self, tokens, positions, page_tables, ctx_lens, logits, stream=None) -> None:
         """Host int32 arrays (tokens/positions/ctx_lens [B], page_tables [B, max_pages]) -> logits."""

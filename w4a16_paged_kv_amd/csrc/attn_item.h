@@ -76,15 +76,9 @@ __device__ __forceinline__ float rows_sum(float v) {
   const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
   return bits_f(b[0]) + bits_f(b[1]);
 }
-__device__ __forceinline__ float page_max(float v) {  // over the 16 tokens of a page (same lane % 4)
-  v = fmaxf(v, ror4(v));
-  v = fmaxf(v, ror8(v));
-  return rows_max(v);
-}
-__device__ __forceinline__ float page_sum(float v) {
-  v += ror4(v);
-  v += ror8(v);
-  return rows_sum(v);
+__device__ __forceinline__ float half_sum(float v) {  // lanes i and i^32
+  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
+  return bits_f(b[0]) + bits_f(b[1]);
 }
 
 // One work item (split of pages, KV head, sequence) on one workgroup of NT
@@ -94,14 +88,16 @@ __device__ __forceinline__ float page_sum(float v) {
 // every early return). Queries and K/V are read coherently (they may have
 // been written earlier in the same launch), outputs and partials are stored
 // coherently.
-template <int D, int GQ, int NT>
+// PF: keep the next page's K/V in flight while the current page is processed
+// (two K/V register sets; without it the kernel fits a 1024-thread launch).
+template <int D, int GQ, int NT, bool PF = true>
 __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(GQ >= 1 && GQ <= 8, "group");
   static_assert(NT >= kAttnWaves * 64 && NT % 64 == 0, "threads");
   constexpr int W = kAttnWaves;
-  constexpr int NI = D / 32;          // 8-column sub-chunks per lane for scores
-  constexpr int LD = D / 8;           // lanes per token row for PV (8 columns each)
+  constexpr int CW = 4;               // PV columns per lane
+  constexpr int LD = D / CW;          // lanes per token row for PV
   constexpr int TPI = 64 / LD;        // token rows per PV load instruction
   constexpr int NTOK = kPage / TPI;   // tokens per lane for PV
   __shared__ float s_m[W][8], s_l[W][8];
@@ -141,25 +137,29 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   const int p_begin = split * a.pages_per_split;
   const int p_end = min(npages, p_begin + a.pages_per_split);
 
-  // the group's queries go to LDS (read per head per page); lane
-  // (tk = lane >> 2, c = lane & 3) covers columns 8c + 32i .. +8 of token tk
+  // Scores on the matrix cores: S^T = K q^T with v_mfma_f32_16x16x32_f16, A =
+  // the page's K (lane l: token l & 15, columns 32 kk + 8 (l >> 4) .. +8), B =
+  // the group's queries (lane l: head l & 15, same columns; heads past GQ are
+  // zero), so lane l ends with S[token 4 (l >> 4) + j][head l & 15], j < 4.
+  // The queries pass through LDS once into that operand layout.
 #pragma unroll
   for (int r = 0; r < (GQ * D + NT * 8 - 1) / (NT * 8); ++r) {
     const int i = (int)(threadIdx.x + r * NT) * 8;
     if (i < GQ * D) *reinterpret_cast<u4_t*>(&s_q[i]) = qv[r];
   }
   __syncthreads();
-  const int tk = lane >> 2, c = lane & 3;
+  constexpr int NK = D / 32;               // MFMA k-steps per page
+  const int qh = lane & 15, kc = 8 * (lane >> 4);
+  const int qrow = min(qh, GQ - 1);        // heads past GQ read a real row and are zeroed
 
   const float scale = kLog2e / sqrtf((float)D);
-  const int hA = c, hB = c + 4;            // heads whose softmax state this lane keeps
-  float mA = -INFINITY, mB = -INFINITY, lA = 0.f, lB = 0.f;
-  float o[GQ][8];
+  float m_h = -INFINITY, l_h = 0.f;        // softmax state of head qh
+  float o[GQ][CW];
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-  const int d0 = 8 * (lane % LD);          // PV columns of this lane
+    for (int e = 0; e < CW; ++e) o[h][e] = 0.f;
+  const int d0 = CW * (lane % LD);         // PV columns of this lane
   const int t0 = lane / LD;                // first PV token row of this lane
   const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
 
@@ -171,69 +171,55 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     valid = bad ? 0 : min(kPage, ctx - p * kPage);
     return bad ? 0 : id;
   };
-  u4_t kf[NI], vf[NTOK], kn[NI], vn[NTOK];
-  auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
+  u4_t kf[NK], kn[PF ? NK : 1];
+  u2_t vf[NTOK], vn[PF ? NTOK : 1];
+  auto load_kv = [&](int page, u4_t* kk, u2_t* vv) {
     page = __builtin_amdgcn_readfirstlane(page);  // one page per wavefront: keeps the resources scalar
     const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
     const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kk[i] = ld128_agent(rk, 2 * (tk * D + 8 * c + 32 * i));
+    for (int i = 0; i < NK; ++i) kk[i] = ld128_agent(rk, 2 * (qh * D + 32 * i + kc));
 #pragma unroll
-    for (int i = 0; i < NTOK; ++i) vv[i] = ld128_agent(rv, 2 * ((t0 + TPI * i) * D + d0));
+    for (int i = 0; i < NTOK; ++i) vv[i] = ld64_agent(rv, 2 * ((t0 + TPI * i) * D + d0));
   };
   int valid_cur = 0, valid_nxt = 0;
   const int p_stop = pager ? p_end : pw0;  // non-page wavefronts skip the loop
   if (pw0 < p_stop) load_kv(checked(pw0, pid_cur, valid_cur), kf, vf);
   for (int p = pw0; p < p_stop; p += W) {
     const int valid = valid_cur;
-    if (p + W < p_stop) {
+    if (PF && p + W < p_stop) {
       load_kv(checked(p + W, pid_nxt, valid_nxt), kn, vn);
       pid_nxt = pt[min(p + 2 * W, a.max_pages - 1)];  // the page after, one step ahead
     }
 
-    // scores of token tk for every head of the group (quad reduction over c)
-    float s[GQ];
+    f4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const u4_t qq = *reinterpret_cast<const u4_t*>(&s_q[h * D + 8 * c + 32 * i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_fdot2(as_h2a(qq[e]), as_h2a(kf[i][e]), acc, false);
-      }
-      acc += dpp_xor1(acc);
-      acc += dpp_xor2(acc);
-      s[h] = acc * scale;
+    for (int kk = 0; kk < NK; ++kk) {
+      // the query operand is re-read from LDS per page (registers stay free)
+      u4_t qb = *reinterpret_cast<const u4_t*>(&s_q[qrow * D + 32 * kk + kc]);
+      if (qh >= GQ) qb = (u4_t){0u, 0u, 0u, 0u};
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, kf[kk]), __builtin_bit_cast(h8_t, qb), sc,
+                                                  0, 0, 0);
     }
-    float sA = -INFINITY, sB = -INFINITY;
+    // tokens past the context (and their NaN-poisoned slots) score -inf
+    float sv[4];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      if (h == hA) sA = s[h];
-      if (h == hB) sB = s[h];
-    }
-    if (tk >= valid) {
-      sA = -INFINITY;
-      sB = -INFINITY;
-    }
-    // page maximum and sum over the 16 tokens (lanes sharing c)
-    const float pmA = page_max(sA), pmB = page_max(sB);
-    const float nA = fmaxf(mA, pmA), nB = fmaxf(mB, pmB);
-    const float alA = nA == -INFINITY ? 1.f : exp2f(mA - nA);
-    const float alB = nB == -INFINITY ? 1.f : exp2f(mB - nB);
-    const float pA = nA == -INFINITY ? 0.f : exp2f(sA - nA);
-    const float pB = nB == -INFINITY ? 0.f : exp2f(sB - nB);
-    lA = lA * alA + page_sum(pA);
-    lB = lB * alB + page_sum(pB);
-    mA = nA;
-    mB = nB;
+    for (int j = 0; j < 4; ++j) sv[j] = 4 * (lane >> 4) + j < valid ? sc[j] * scale : -INFINITY;
+    // page maximum and sum per head: four tokens in the lane, then the rows
+    const float pm = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    const float n_h = fmaxf(m_h, pm);
+    const float al = n_h == -INFINITY ? 1.f : exp2f(m_h - n_h);
+    float pj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pj[j] = n_h == -INFINITY ? 0.f : exp2f(sv[j] - n_h);
+    l_h = l_h * al + rows_sum((pj[0] + pj[1]) + (pj[2] + pj[3]));
+    m_h = n_h;
     // broadcast weights and rescale factors to the PV lanes through LDS
     // (wavefront-private rows; LDS operations of a wavefront stay in order)
-    s_pb[wave][tk][hA] = pA;
-    s_pb[wave][tk][hB] = pB;
-    if (lane < 4) {
-      s_al[wave][hA] = alA;
-      s_al[wave][hB] = alB;
+    if (qh < 8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_pb[wave][4 * (lane >> 4) + j][qh] = pj[j];
+      if (lane < 8) s_al[wave][qh] = al;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -243,7 +229,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     if (valid < kPage) {
 #pragma unroll
       for (int i = 0; i < NTOK; ++i)
-        if (t0 + TPI * i >= valid) vf[i] = (u4_t){0u, 0u, 0u, 0u};
+        if (t0 + TPI * i >= valid) vf[i] = (u2_t){0u, 0u};
     }
     const f4v al0 = *reinterpret_cast<const f4v*>(&s_al[wave][0]);
     const f4v al1 = *reinterpret_cast<const f4v*>(&s_al[wave][4]);
@@ -251,7 +237,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     for (int h = 0; h < GQ; ++h) {
       const float al = h < 4 ? al0[h & 3] : al1[h & 3];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] *= al;
+      for (int e = 0; e < CW; ++e) o[h][e] *= al;
     }
 #pragma unroll
     for (int i = 0; i < NTOK; ++i) {
@@ -261,7 +247,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
       for (int h = 0; h < GQ; ++h) {
         const float pv = h < 4 ? p0[h & 3] : p1[h & 3];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < CW / 2; ++e) {
           const h2_t v2 = as_h2a(vf[i][e]);
           o[h][2 * e] = fmaf(pv, (float)v2[0], o[h][2 * e]);
           o[h][2 * e + 1] = fmaf(pv, (float)v2[1], o[h][2 * e + 1]);
@@ -271,33 +257,32 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (PF) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kf[i] = kn[i];
+      for (int i = 0; i < NK; ++i) kf[i] = kn[PF ? i : 0];
 #pragma unroll
-    for (int i = 0; i < NTOK; ++i) vf[i] = vn[i];
-    valid_cur = valid_nxt;
+      for (int i = 0; i < NTOK; ++i) vf[i] = vn[PF ? i : 0];
+      valid_cur = valid_nxt;
+    } else if (p + W < p_stop) {
+      load_kv(checked(p + W, pid_nxt, valid_cur), kf, vf);
+      pid_nxt = pt[min(p + 2 * W, a.max_pages - 1)];
+    }
   }
   // reduce o over the lanes holding other token rows of the same columns
-  // (lanes d apart by multiples of LD: 16 for D = 128, 8 for D = 64)
+  // (lanes apart by multiples of LD: 32 for D = 128, 16 for D = 64)
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = o[h][e];
-      if (LD == 8) v += ror8(v);
-      o[h][e] = rows_sum(v);
-    }
-  if (pager && lane < 4) {
-    s_m[wave][hA] = mA;
-    s_l[wave][hA] = lA;
-    s_m[wave][hB] = mB;
-    s_l[wave][hB] = lB;
+    for (int e = 0; e < CW; ++e) o[h][e] = LD == 32 ? half_sum(o[h][e]) : rows_sum(o[h][e]);
+  if (pager && lane < 8) {
+    s_m[wave][lane] = m_h;
+    s_l[wave][lane] = l_h;
   }
   if (pager && lane < LD)
 #pragma unroll
     for (int h = 0; h < GQ; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[wave][h][d0 + e] = o[h][e];
+      for (int e = 0; e < CW; ++e) s_o[wave][h][d0 + e] = o[h][e];
   __syncthreads();
 
   // combine the wavefronts: this split's (o, m, l), or the output if one split
@@ -371,16 +356,16 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     float M = fmaxf(mm[0], mm[1]);
     M = fmaxf(M, ror4(M));
     M = fmaxf(M, ror8(M));
-    M = fmaxf(M, bits_f(__builtin_amdgcn_update_dpp(0, f_bits(M), 0xB1, 0xF, 0xF, false)));
-    M = fmaxf(M, bits_f(__builtin_amdgcn_update_dpp(0, f_bits(M), 0x4E, 0xF, 0xF, false)));
+    M = fmaxf(M, dpp_xor1(M));
+    M = fmaxf(M, dpp_xor2(M));
     M = rows_max(M);
     const float f0 = M == -INFINITY ? 0.f : exp2f(mm[0] - M);
     const float f1 = M == -INFINITY ? 0.f : exp2f(mm[1] - M);
     float L = f0 * ll[0] + f1 * ll[1];
     L += ror4(L);
     L += ror8(L);
-    L += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(L), 0xB1, 0xF, 0xF, false));
-    L += bits_f(__builtin_amdgcn_update_dpp(0, f_bits(L), 0x4E, 0xF, 0xF, false));
+    L += dpp_xor1(L);
+    L += dpp_xor2(L);
     L = rows_sum(L);
     const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll

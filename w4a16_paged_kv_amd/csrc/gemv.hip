@@ -72,15 +72,17 @@ __device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* ds
 }
 
 // ------------------------------------------------------------ batch 1
-// One launch per projection: S wavefronts per tile, TW tiles per workgroup
-// (blockDim.x = 64 S TW), IT activation words per thread. The activation
-// loads go out first, then the first weight batch, so the prologue waits for
-// the activations only (the vector-memory counter is in order).
+// One launch per projection: 1024 threads per workgroup, S wavefronts per
+// tile on TW tiles (S TW <= 16; the other wavefronts only help stage the
+// activations), IT activation words per thread: the same decomposition and
+// arithmetic as the projection phases of the persistent layer kernel. The
+// activation loads go out first, then the first weight batch, so the
+// prologue waits for the activations only (the vector-memory counter is in
+// order).
 template <int EPI, int S, int IT>
-__global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a) {
+__global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
   constexpr bool NORM = GemvB1<EPI, S, IT>::NORM;
   const int NT = blockDim.x;
-  const int TW = NT / 64 / S;
   extern __shared__ __align__(16) uint8_t smem[];
   const int kpad = a.groups * kGroup;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -314,17 +316,8 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t count, uint32_t value) {
 
 // ---------------------------------------------------------------- launchers
 
-// Batch-1 work split. TW = ceil(tiles / 256) tiles per workgroup, so a
-// matrix of up to 256 x 16 tiles runs as at most one workgroup per CU: each
-// CU then stages the activation row once, and no second workgroup on a CU
-// waits for its activations behind the first one's weight stream. The S
-// wavefronts of a tile split its groups (S <= groups / 2, S * TW <= 16), so
-// small matrices still put thousands of wavefronts in flight.
-struct B1Split {
-  int s, tw, it;
-};
-
-static B1Split w4_b1_split(int tiles, int groups) {
+// (the batch-1 split policy is described with B1Split in gemv_b1.h)
+B1Split w4_b1_split(int tiles, int groups) {
   const int tw = std::min(16, ceil_div(tiles, 256));
   int s = 1;
   for (int c : {16, 8, 4, 2})
@@ -332,17 +325,15 @@ static B1Split w4_b1_split(int tiles, int groups) {
       s = c;
       break;
     }
-  const int nt = 64 * s * tw;
-  const int it = ceil_div(groups * kGroup, 8 * nt);  // activation words per thread
+  const int it = ceil_div(groups * kGroup, 8 * kB1Threads);  // activation words per thread
   return {s, tw, it};
 }
 
 template <int EPI, int S, int IT>
 static void launch_b1(const GemvArgs& a, int tw, hipStream_t s) {
-  const int waves = S * tw;
-  const size_t lds = gemv_b1_lds_bytes(a.groups, waves, tw);
-  hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S, IT>), dim3(ceil_div(a.tiles, tw)), dim3(waves * 64), lds, s,
-                     a);
+  const size_t lds = gemv_b1_lds_bytes(a.groups, kB1Threads / 64, tw);
+  hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S, IT>), dim3(ceil_div(a.tiles, tw)), dim3(kB1Threads), lds, s,
+                     a, tw);
 }
 
 template <int EPI, int S>

@@ -24,6 +24,7 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float h2f(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
 __device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
@@ -57,6 +58,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base
 constexpr int kPolicySc1 = 16;  // buffer instruction cache-policy operand: sc1
 __device__ __forceinline__ u4_t ld128_agent(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kPolicySc1));
+}
+__device__ __forceinline__ u2_t ld64_agent(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kPolicySc1));
 }
 
 // ------------------------------------------------------------- epilogues
@@ -317,6 +321,17 @@ __device__ __forceinline__ QkvPre qkv_pre(const GemvArgs& a, int vb, int tw) {
   return p;
 }
 
+// Threads of a batch-1 GEMV workgroup, in its own launch and as a phase of
+// the persistent layer kernel (identical decomposition, identical results).
+constexpr int kB1Threads = 1024;
+
+// Batch-1 work split. TW = ceil(tiles / 256) tiles per workgroup, so a
+// matrix of up to 256 x 16 tiles runs as at most one workgroup per CU: each
+// CU then stages the activation row once, and no second workgroup on a CU
+// waits for its activations behind the first one's weight stream. The S
+// wavefronts of a tile split its groups (S <= groups / 2, S * TW <= 16), so
+// small matrices still put thousands of wavefronts in flight. IT activation
+// words per thread (at most 3). (B1Split, w4_b1_split: w4_internal.h.)
 // LDS of one batch-1 GEMV: the staged activation row, then reductions.
 __host__ __device__ constexpr size_t gemv_b1_lds_bytes(int groups, int waves, int tw) {
   return (size_t)groups * kGroup * 2 + (size_t)(waves * 16 + tw * 16 + waves) * 4;

@@ -21,7 +21,7 @@
 namespace w4 {
 
 struct WsLayout {
-  size_t err, counters, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, total;
+  size_t err, counters, bar, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, total;
   int xn_stride, o_stride, h_stride, max_splits;
 };
 
@@ -40,6 +40,7 @@ static WsLayout ws_layout(const w4_config& c, int max_batch, int max_pages) {
   L.max_splits = ceil_div(max_pages, 4);
   L.err = take(256);
   L.counters = take((size_t)max_batch * c.n_kv_heads * 4);
+  L.bar = take(persistent_bar_words(kMaxPersistGrid) * 4);
   L.tokens = take((size_t)max_batch * 4);
   L.positions = take((size_t)max_batch * 4);
   L.ctx = take((size_t)max_batch * 4);
@@ -84,6 +85,8 @@ struct w4_model {
   uint8_t* ws = nullptr;
   WsLayout L;
   bool use_graph = true;
+  int persist_grid = 0;        // workgroups of the persistent layer kernel (0: unavailable)
+  bool use_persistent = false;
   hipStream_t cap_stream = nullptr;
   // key: batch, logits, device-input pointers (null for host inputs)
   typedef std::tuple<int, const void*, const void*, const void*, const void*, const void*> Key;
@@ -136,90 +139,136 @@ static GemvArgs gemv_args(const void* w, int n, int k, const uint16_t* x, int x_
   return a;
 }
 
-// Enqueues one operation of decoder layer l for `batch` sequences. The
+// Arguments of the operations of decoder layer l for `batch` sequences. The
 // residual stream goes x_in -> (o projection) x_out -> (down projection)
-// x_out; q, o and h live in the workspace.
+// x_out; q, o and h live in the workspace. At batch 1 the RMSNorms run in the
+// projections' prologues; above it in a separate kernel into xn.
+static GemvArgs qkv_args(w4_model* m, int l, const uint16_t* x_in, int batch) {
+  const w4_config& c = m->cfg;
+  const w4_layer_weights& W = m->layers[l];
+  const WsLayout& L = m->L;
+  uint16_t* xn = m->at<uint16_t>(L.xn);
+  const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  GemvArgs a = batch == 1 ? gemv_args(W.qkv, qkv_rows, c.hidden, x_in, c.hidden, W.attn_norm, c.rms_eps,
+                                      nullptr, 0, nullptr, 1)
+                          : gemv_args(W.qkv, qkv_rows, c.hidden, xn, L.xn_stride, nullptr, 0.f, nullptr, 0,
+                                      nullptr, batch);
+  if (batch == 1) a.xn_out = xn;
+  a.qkv.q_out = m->at<uint16_t>(L.q);
+  a.qkv.q_stride = c.n_heads * c.head_dim;
+  a.qkv.k_pool = m->k_pool(l);
+  a.qkv.v_pool = m->v_pool(l);
+  a.qkv.bias = W.qkv_bias;
+  a.qkv.slot = m->at<int32_t>(L.slot);
+  a.qkv.rope = m->at<float>(L.rope);
+  a.qkv.n_heads = c.n_heads;
+  a.qkv.n_kv_heads = c.n_kv_heads;
+  a.qkv.head_dim = c.head_dim;
+  return a;
+}
+
+static AttnArgs attn_args(w4_model* m, int l, const StepInputs& in, int batch) {
+  const w4_config& c = m->cfg;
+  const WsLayout& L = m->L;
+  AttnArgs at{};
+  at.q = m->at<uint16_t>(L.q);
+  at.q_stride = c.n_heads * c.head_dim;
+  at.k_pool = m->k_pool(l);
+  at.v_pool = m->v_pool(l);
+  at.page_tables = in.page_tables;
+  at.ctx_lens = in.ctx_lens;
+  at.batch = batch;
+  at.max_pages = m->max_pages;
+  at.num_pages = m->num_pages;
+  at.n_heads = c.n_heads;
+  at.n_kv_heads = c.n_kv_heads;
+  at.pages_per_split = attention_pages_per_split(batch, c.n_kv_heads, m->max_pages);
+  at.max_splits = ceil_div(m->max_pages, at.pages_per_split);
+  at.partials = m->at<float>(L.partials);
+  at.counters = m->at<uint32_t>(L.counters);
+  at.out = m->at<uint16_t>(L.o);
+  at.out_stride = L.o_stride;
+  at.err = m->at<uint32_t>(L.err);
+  return at;
+}
+
+static GemvArgs oproj_args(w4_model* m, int l, const uint16_t* x_in, uint16_t* x_out, int batch) {
+  const w4_config& c = m->cfg;
+  return gemv_args(m->layers[l].o, c.hidden, c.n_heads * c.head_dim, m->at<uint16_t>(m->L.o), m->L.o_stride,
+                   nullptr, 0.f, x_out, c.hidden, x_in, batch);
+}
+
+static GemvArgs gate_up_args(w4_model* m, int l, const uint16_t* x, int batch) {
+  const w4_config& c = m->cfg;
+  const w4_layer_weights& W = m->layers[l];
+  const WsLayout& L = m->L;
+  uint16_t* xn = m->at<uint16_t>(L.xn);
+  uint16_t* h = m->at<uint16_t>(L.h);
+  GemvArgs a = batch == 1 ? gemv_args(W.gate_up, 2 * c.ffn, c.hidden, x, c.hidden, W.mlp_norm, c.rms_eps, h,
+                                      L.h_stride, nullptr, 1)
+                          : gemv_args(W.gate_up, 2 * c.ffn, c.hidden, xn, L.xn_stride, nullptr, 0.f, h,
+                                      L.h_stride, nullptr, batch);
+  if (batch == 1) a.xn_out = xn;
+  return a;
+}
+
+static GemvArgs down_args(w4_model* m, int l, uint16_t* x, int batch) {
+  const w4_config& c = m->cfg;
+  return gemv_args(m->layers[l].down, c.hidden, c.ffn, m->at<uint16_t>(m->L.h), m->L.h_stride, nullptr, 0.f, x,
+                   c.hidden, x, batch);
+}
+
+// Enqueues one operation of decoder layer l for `batch` sequences.
 static int enqueue_op(w4_model* m, int op, int l, const uint16_t* x_in, uint16_t* x_out,
                       const StepInputs& in, int batch, hipStream_t s) {
   const w4_config& c = m->cfg;
   const w4_layer_weights& W = m->layers[l];
   const WsLayout& L = m->L;
-  uint32_t* err = m->at<uint32_t>(L.err);
   uint16_t* xn = m->at<uint16_t>(L.xn);
-  uint16_t* q = m->at<uint16_t>(L.q);
-  uint16_t* o = m->at<uint16_t>(L.o);
-  uint16_t* h = m->at<uint16_t>(L.h);
   const bool b1 = batch == 1;
   switch (op) {
-    case W4_OP_QKV: {  // qkv projection (RMSNorm prologue at batch 1), RoPE, K/V page write
-      const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+    case W4_OP_QKV:  // qkv projection (RMSNorm prologue at batch 1), RoPE, K/V page write
       if (!b1) W4_LAUNCH(launch_rmsnorm_rows(x_in, c.hidden, W.attn_norm, c.rms_eps, c.hidden, xn,
                                              L.xn_stride, batch, s));
-      GemvArgs a = b1 ? gemv_args(W.qkv, qkv_rows, c.hidden, x_in, c.hidden, W.attn_norm,
-                                  c.rms_eps, nullptr, 0, nullptr, 1)
-                      : gemv_args(W.qkv, qkv_rows, c.hidden, xn, L.xn_stride, nullptr, 0.f,
-                                  nullptr, 0, nullptr, batch);
-      if (b1) a.xn_out = xn;
-      a.qkv.q_out = q;
-      a.qkv.q_stride = c.n_heads * c.head_dim;
-      a.qkv.k_pool = m->k_pool(l);
-      a.qkv.v_pool = m->v_pool(l);
-      a.qkv.bias = W.qkv_bias;
-      a.qkv.slot = m->at<int32_t>(L.slot);
-      a.qkv.rope = m->at<float>(L.rope);
-      a.qkv.n_heads = c.n_heads;
-      a.qkv.n_kv_heads = c.n_kv_heads;
-      a.qkv.head_dim = c.head_dim;
-      W4_LAUNCH(launch_w4_gemv(EPI_QKV, a, s));
+      W4_LAUNCH(launch_w4_gemv(EPI_QKV, qkv_args(m, l, x_in, batch), s));
       return W4_OK;
-    }
-    case W4_OP_ATTN: {  // paged attention, split over pages, LSE merge by the last split
-      AttnArgs at{};
-      at.q = q;
-      at.q_stride = c.n_heads * c.head_dim;
-      at.k_pool = m->k_pool(l);
-      at.v_pool = m->v_pool(l);
-      at.page_tables = in.page_tables;
-      at.ctx_lens = in.ctx_lens;
-      at.batch = batch;
-      at.max_pages = m->max_pages;
-      at.num_pages = m->num_pages;
-      at.n_heads = c.n_heads;
-      at.n_kv_heads = c.n_kv_heads;
-      at.pages_per_split = attention_pages_per_split(batch, c.n_kv_heads, m->max_pages);
-      at.max_splits = ceil_div(m->max_pages, at.pages_per_split);
-      at.partials = m->at<float>(L.partials);
-      at.counters = m->at<uint32_t>(L.counters);
-      at.out = o;
-      at.out_stride = L.o_stride;
-      at.err = err;
-      W4_LAUNCH(launch_attention(at, c.head_dim, c.n_heads / c.n_kv_heads, s));
+    case W4_OP_ATTN:  // paged attention, split over pages, LSE merge by the last split
+      W4_LAUNCH(launch_attention(attn_args(m, l, in, batch), c.head_dim, c.n_heads / c.n_kv_heads, s));
       return W4_OK;
-    }
     case W4_OP_OPROJ:  // o projection + residual
-      W4_LAUNCH(launch_w4_gemv(EPI_RESID, gemv_args(W.o, c.hidden, c.n_heads * c.head_dim, o,
-                                                    L.o_stride, nullptr, 0.f, x_out, c.hidden,
-                                                    x_in, batch), s));
+      W4_LAUNCH(launch_w4_gemv(EPI_RESID, oproj_args(m, l, x_in, x_out, batch), s));
       return W4_OK;
     case W4_OP_GATE_UP:  // gate/up (RMSNorm prologue at batch 1) with SiLU-mul
       if (!b1) W4_LAUNCH(launch_rmsnorm_rows(x_out, c.hidden, W.mlp_norm, c.rms_eps, c.hidden, xn,
                                              L.xn_stride, batch, s));
-      {
-        GemvArgs a = b1 ? gemv_args(W.gate_up, 2 * c.ffn, c.hidden, x_out, c.hidden, W.mlp_norm,
-                                    c.rms_eps, h, L.h_stride, nullptr, 1)
-                        : gemv_args(W.gate_up, 2 * c.ffn, c.hidden, xn, L.xn_stride, nullptr, 0.f,
-                                    h, L.h_stride, nullptr, batch);
-        if (b1) a.xn_out = xn;
-        W4_LAUNCH(launch_w4_gemv(EPI_SILU, a, s));
-      }
+      W4_LAUNCH(launch_w4_gemv(EPI_SILU, gate_up_args(m, l, x_out, batch), s));
       return W4_OK;
     case W4_OP_DOWN:  // down projection + residual
-      W4_LAUNCH(launch_w4_gemv(EPI_RESID, gemv_args(W.down, c.hidden, c.ffn, h, L.h_stride,
-                                                    nullptr, 0.f, x_out, c.hidden, x_out, batch),
-                               s));
+      W4_LAUNCH(launch_w4_gemv(EPI_RESID, down_args(m, l, x_out, batch), s));
       return W4_OK;
   }
   return fail(W4_EINVAL, "unknown layer op %d", op);
+}
+
+// One decoder layer (batch 1) as a single persistent launch: the same
+// kernels' device code and splits, workgroups meeting at grid barriers.
+static int enqueue_layer_persistent(w4_model* m, int l, uint16_t* x, const StepInputs& in, hipStream_t s) {
+  const w4_config& c = m->cfg;
+  LayerPhases t{};
+  t.qkv = qkv_args(m, l, x, 1);
+  t.qkv.xn_out = nullptr;
+  t.attn = attn_args(m, l, in, 1);
+  t.o = oproj_args(m, l, x, x, 1);
+  t.gate_up = gate_up_args(m, l, x, 1);
+  t.gate_up.xn_out = nullptr;
+  t.down = down_args(m, l, x, 1);
+  t.tw_q = w4_b1_split(t.qkv.tiles, t.qkv.groups).tw;
+  t.tw_o = w4_b1_split(t.o.tiles, t.o.groups).tw;
+  t.tw_g = w4_b1_split(t.gate_up.tiles, t.gate_up.groups).tw;
+  t.tw_d = w4_b1_split(t.down.tiles, t.down.groups).tw;
+  t.bar = m->at<uint32_t>(m->L.bar);
+  W4_LAUNCH(launch_persistent(t, c, m->persist_grid, s));
+  return W4_OK;
 }
 
 // Enqueues one decoder layer: x_out = layer(x_in) for `batch` sequences.
@@ -292,8 +341,9 @@ static int enqueue_step(w4_model* m, const StepInputs& in, int batch, uint16_t* 
   uint16_t* x = m->at<uint16_t>(m->L.x);
   int rc0 = enqueue_plan(m, in.tokens, in, batch, s);
   if (rc0) return rc0;
+  const bool persistent = m->use_persistent && batch == 1;
   for (int l = 0; l < c.n_layers; ++l) {
-    int rc = enqueue_layer(m, l, x, x, in, batch, s);
+    int rc = persistent ? enqueue_layer_persistent(m, l, x, in, s) : enqueue_layer(m, l, x, x, in, batch, s);
     if (rc) return rc;
   }
   return enqueue_lm_head(m, x, batch, logits, s);
@@ -355,7 +405,8 @@ static StepInputs staged(w4_model* m) {
 // Runs the step eagerly or through a graph captured once per key.
 static int run_step(w4_model* m, const StepInputs& in, int batch, uint16_t* logits,
                     hipStream_t s, const void* key_inputs) {
-  if (!m->use_graph) return enqueue_step(m, in, batch, logits, s);
+  // the persistent path is a handful of launches already: no capture needed
+  if (!m->use_graph || (m->use_persistent && batch == 1)) return enqueue_step(m, in, batch, logits, s);
   w4_model::Key key(batch, logits, key_inputs ? in.tokens : nullptr,
                     key_inputs ? in.positions : nullptr, key_inputs ? in.page_tables : nullptr,
                     key_inputs ? in.ctx_lens : nullptr);
@@ -458,6 +509,7 @@ W4_EXPORT int w4_model_create(const w4_config* cfg, const w4_weights* weights, v
     delete m;
     return fail(W4_EHIP, "w4_model_create: %s", hipGetErrorString(e));
   }
+  m->persist_grid = std::min(persistent_grid(m->cfg), kMaxPersistGrid);
   *out = m;
   return W4_OK;
 }
@@ -473,6 +525,15 @@ W4_EXPORT int w4_set_graph(w4_model* m, int enabled) {
   clear_error();
   if (!m) return fail(W4_ESTATE, "null model");
   m->use_graph = enabled != 0;
+  return W4_OK;
+}
+
+W4_EXPORT int w4_set_persistent(w4_model* m, int enabled) {
+  clear_error();
+  if (!m) return fail(W4_ESTATE, "null model");
+  if (enabled && m->persist_grid == 0)
+    return fail(W4_EINVAL, "w4_set_persistent: no persistent kernel for this configuration or device");
+  m->use_persistent = enabled != 0;
   return W4_OK;
 }
 

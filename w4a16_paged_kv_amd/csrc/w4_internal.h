@@ -27,15 +27,15 @@ void clear_error();
 
 inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 constexpr int kPage = 16;       // tokens per KV page
 constexpr int kGroup = 128;     // input columns per INT4 scale group
 constexpr int kTileRows = 16;   // rows per packed tile
 
 // ----------------------------------------------------------- packed sizes
-inline int w4_tiles(int n) { return ceil_div(n, kTileRows); }
-inline int w4_groups(int k) { return ceil_div(k, kGroup); }
+__host__ __device__ inline int w4_tiles(int n) { return ceil_div(n, kTileRows); }
+__host__ __device__ inline int w4_groups(int k) { return ceil_div(k, kGroup); }
 inline size_t w4_nibble_bytes(int n, int k) { return (size_t)w4_tiles(n) * w4_groups(k) * 1024; }
 
 // --------------------------------------------------------- kernel arguments
@@ -128,6 +128,31 @@ struct AttnArgs {
   int32_t out_stride;
   uint32_t* err;
 };
+
+// Batch-1 GEMV work split (policy in gemv_b1.h): S wavefronts per tile, TW
+// tiles per 1024-thread workgroup, IT activation words per thread.
+struct B1Split {
+  int s, tw, it;
+};
+B1Split w4_b1_split(int tiles, int groups);
+
+// The persistent layer kernel (persistent.hip): one launch per decoder
+// layer, its five operations' arguments passed by value like those of the
+// per-operation kernels (the kernel reads each field from the argument
+// segment where it needs it).
+struct LayerPhases {
+  GemvArgs qkv, o, gate_up, down;
+  AttnArgs attn;
+  int32_t tw_q, tw_o, tw_g, tw_d;  // tiles per workgroup of each projection
+  uint32_t* bar;                   // barrier words, zero-initialised once
+};
+
+constexpr uint32_t kPersistEpochs = 8;  // grid barriers one launch may use (4)
+constexpr int kMaxPersistGrid = 1024;    // workgroups (one per CU) the barrier words provide for
+size_t persistent_bar_words(int grid);
+size_t persistent_lds_bytes(const w4_config& c);
+int persistent_grid(const w4_config& c);  // co-resident workgroups (one per CU), or 0 if unsupported
+hipError_t launch_persistent(const LayerPhases& t, const w4_config& c, int grid, hipStream_t s);
 
 // Launchers (return hipGetLastError of the launch).
 hipError_t launch_w4_gemv(int epi, const GemvArgs& a, hipStream_t s);
