@@ -72,10 +72,10 @@ __device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* ds
 }
 
 // ------------------------------------------------------------ batch 1
-// One launch per projection: 1024 threads per workgroup, S wavefronts per
-// tile on TW tiles (S TW <= 16; the other wavefronts only help stage the
-// activations), IT activation words per thread: the same decomposition and
-// arithmetic as the projection phases of the persistent layer kernel. The
+// One launch per projection: S wavefronts per tile on TW tiles (S TW <= 16;
+// any further wavefronts only help stage the activations), IT activation
+// words per thread: the same decomposition and arithmetic as the projection
+// phases of the persistent layer kernel. The
 // activation loads go out first, then the first weight batch, so the
 // prologue waits for the activations only (the vector-memory counter is in
 // order).
@@ -330,18 +330,24 @@ B1Split w4_b1_split(int tiles, int groups) {
 }
 
 template <int EPI, int S, int IT>
-static void launch_b1(const GemvArgs& a, int tw, hipStream_t s) {
-  const size_t lds = gemv_b1_lds_bytes(a.groups, kB1Threads / 64, tw);
-  hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S, IT>), dim3(ceil_div(a.tiles, tw)), dim3(kB1Threads), lds, s,
-                     a, tw);
+static void launch_b1(const GemvArgs& a, int tw, int nt, hipStream_t s) {
+  const size_t lds = gemv_b1_lds_bytes(a.groups, nt / 64, tw);
+  hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S, IT>), dim3(ceil_div(a.tiles, tw)), dim3(nt), lds, s, a, tw);
 }
 
+// Without RMSNorm the staging has no reduction across threads, so the
+// workgroup shrinks to its S * TW working wavefronts (same results, fewer
+// idle wavefronts to launch); with RMSNorm it keeps the 1024 threads whose
+// sum-of-squares order the persistent layer kernel reproduces.
 template <int EPI, int S>
 static hipError_t launch_b1_it(const GemvArgs& a, const B1Split& sp, hipStream_t s) {
-  switch (sp.it) {
-    case 1: launch_b1<EPI, S, 1>(a, sp.tw, s); return hipSuccess;
-    case 2: launch_b1<EPI, S, 2>(a, sp.tw, s); return hipSuccess;
-    case 3: launch_b1<EPI, S, 3>(a, sp.tw, s); return hipSuccess;
+  constexpr bool NORM = GemvB1<EPI, S, 1>::NORM;
+  const int nt = NORM ? kB1Threads : std::max(256, 64 * S * sp.tw);
+  const int it = NORM ? sp.it : ceil_div(a.groups * kGroup, 8 * nt);
+  switch (it) {
+    case 1: launch_b1<EPI, S, 1>(a, sp.tw, nt, s); return hipSuccess;
+    case 2: launch_b1<EPI, S, 2>(a, sp.tw, nt, s); return hipSuccess;
+    case 3: launch_b1<EPI, S, 3>(a, sp.tw, nt, s); return hipSuccess;
   }
   return hipErrorInvalidValue;  // activation row longer than one workgroup can stage
 }
