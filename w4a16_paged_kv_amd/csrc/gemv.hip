@@ -320,12 +320,12 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t count, uint32_t value) {
 B1Split w4_b1_split(int tiles, int groups) {
   const int tw = std::min(16, ceil_div(tiles, 256));
   int s = 1;
-  for (int c : {16, 8, 4, 2})
-    if (groups >= 2 * c && c * tw <= 16) {
+  for (int c : {8, 4, 2})
+    if (groups >= 2 * c && c * tw <= 8) {
       s = c;
       break;
     }
-  const int it = ceil_div(groups * kGroup, 8 * kB1Threads);  // activation words per thread
+  const int it = ceil_div(groups * kGroup, 8 * kB1Threads);  // per thread, at kB1Threads
   return {s, tw, it};
 }
 
@@ -335,19 +335,27 @@ static void launch_b1(const GemvArgs& a, int tw, int nt, hipStream_t s) {
   hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S, IT>), dim3(ceil_div(a.tiles, tw)), dim3(nt), lds, s, a, tw);
 }
 
-// Without RMSNorm the staging has no reduction across threads, so the
-// workgroup shrinks to its S * TW working wavefronts (same results, fewer
-// idle wavefronts to launch); with RMSNorm it keeps the 1024 threads whose
-// sum-of-squares order the persistent layer kernel reproduces.
+// The workgroup is its S * TW working wavefronts (at least four), unless
+// the activation row then needs more than kMaxIt words per thread; then it
+// has kB1Threads threads like the persistent kernel's phases. The staged
+// row and every product are the same either way, and so is the RMSNorm sum
+// when the row fits one pass of the threads (8 * nt >= k: each thread then
+// holds one word, the words past k are zero).
+constexpr int kMaxIt = 5;
 template <int EPI, int S>
 static hipError_t launch_b1_it(const GemvArgs& a, const B1Split& sp, hipStream_t s) {
-  constexpr bool NORM = GemvB1<EPI, S, 1>::NORM;
-  const int nt = NORM ? kB1Threads : std::max(256, 64 * S * sp.tw);
-  const int it = NORM ? sp.it : ceil_div(a.groups * kGroup, 8 * nt);
+  int nt = std::max(256, 64 * S * sp.tw);
+  int it = ceil_div(a.groups * kGroup, 8 * nt);
+  if (it > kMaxIt) {
+    nt = kB1Threads;
+    it = sp.it;
+  }
   switch (it) {
     case 1: launch_b1<EPI, S, 1>(a, sp.tw, nt, s); return hipSuccess;
     case 2: launch_b1<EPI, S, 2>(a, sp.tw, nt, s); return hipSuccess;
     case 3: launch_b1<EPI, S, 3>(a, sp.tw, nt, s); return hipSuccess;
+    case 4: launch_b1<EPI, S, 4>(a, sp.tw, nt, s); return hipSuccess;
+    case 5: launch_b1<EPI, S, 5>(a, sp.tw, nt, s); return hipSuccess;
   }
   return hipErrorInvalidValue;  // activation row longer than one workgroup can stage
 }
@@ -360,7 +368,6 @@ static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
     const B1Split sp = w4_b1_split(a.tiles, a.groups);
     hipError_t e = hipErrorInvalidValue;
     switch (sp.s) {
-      case 16: e = launch_b1_it<EPI, 16>(a, sp, s); break;
       case 8: e = launch_b1_it<EPI, 8>(a, sp, s); break;
       case 4: e = launch_b1_it<EPI, 4>(a, sp, s); break;
       case 2: e = launch_b1_it<EPI, 2>(a, sp, s); break;

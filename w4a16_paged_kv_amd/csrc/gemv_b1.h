@@ -321,17 +321,20 @@ __device__ __forceinline__ QkvPre qkv_pre(const GemvArgs& a, int vb, int tw) {
   return p;
 }
 
-// Threads of a batch-1 GEMV workgroup, in its own launch and as a phase of
-// the persistent layer kernel (identical decomposition, identical results).
+// Threads of a batch-1 GEMV workgroup as a phase of the persistent layer
+// kernel; the per-projection launch runs only the S * TW working
+// wavefronts (same decomposition, same results).
 constexpr int kB1Threads = 1024;
 
 // Batch-1 work split. TW = ceil(tiles / 256) tiles per workgroup, so a
 // matrix of up to 256 x 16 tiles runs as at most one workgroup per CU: each
 // CU then stages the activation row once, and no second workgroup on a CU
 // waits for its activations behind the first one's weight stream. The S
-// wavefronts of a tile split its groups (S <= groups / 2, S * TW <= 16), so
-// small matrices still put thousands of wavefronts in flight. IT activation
-// words per thread (at most 3). (B1Split, w4_b1_split: w4_internal.h.)
+// wavefronts of a tile split its groups (S <= groups / 2, S * TW <= 8).
+// Measured on the 7B shapes: eight wavefronts per CU stream faster than
+// sixteen (qkv 6.0 -> 5.0 us, down 10.0 -> 9.1 us), because the CU issues
+// the oldest wavefront's loads first and the youngest ones fall behind.
+// IT activation words per thread. (B1Split, w4_b1_split: w4_internal.h.)
 // LDS of one batch-1 GEMV: the staged activation row, then reductions.
 __host__ __device__ constexpr size_t gemv_b1_lds_bytes(int groups, int waves, int tw) {
   return (size_t)groups * kGroup * 2 + (size_t)(waves * 16 + tw * 16 + waves) * 4;

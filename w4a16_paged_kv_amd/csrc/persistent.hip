@@ -164,7 +164,7 @@ struct PersistCfg {
 
 static const PersistCfg* persistent_cfg(const w4_config& c) {
   static const PersistCfg cfgs[] = {
-      W4_CFG(128, 7, 8, 2, 1, 8, 1, 1, 1, 10, 1, 16, 1, 3),
+      W4_CFG(128, 7, 4, 2, 1, 8, 1, 1, 1, 10, 1, 8, 1, 3),
       W4_CFG(64, 7, 2, 1, 1, 2, 1, 1, 2, 1, 1, 4, 1, 1),
   };
   const int gq = c.n_heads / c.n_kv_heads;
