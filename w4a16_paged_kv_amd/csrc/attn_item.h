@@ -32,13 +32,6 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ h2_t as_h2a(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 __device__ __forceinline__ uint16_t f2h_a(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
-__device__ __forceinline__ float dpp_xor1(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-}
-
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Device-scope relaxed accesses: coherent across the XCDs' L2 caches.
@@ -51,31 +44,6 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 
 constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time each
 
-__device__ __forceinline__ int f_bits(float v) { return __builtin_bit_cast(int, v); }
-__device__ __forceinline__ float bits_f(int v) { return __builtin_bit_cast(float, v); }
-
-// Cross-lane reductions on the VALU rather than through LDS permutes:
-// DPP row rotates inside a 16-lane row, v_permlane16_swap / v_permlane32_swap
-// across rows. row4: lanes i, i+4, i+8, i+12 of a row; rows: lanes i, i^16,
-// i^32, i^48; ror8 alone pairs lanes i and i^8 of a row.
-__device__ __forceinline__ float ror4(float v) {
-  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x124, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float ror8(float v) {
-  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x128, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float rows_max(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
-  v = fmaxf(bits_f(a[0]), bits_f(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
-  return fmaxf(bits_f(b[0]), bits_f(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
-  v = bits_f(a[0]) + bits_f(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
-  return bits_f(b[0]) + bits_f(b[1]);
-}
 __device__ __forceinline__ float half_sum(float v) {  // lanes i and i^32
   const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
   return bits_f(b[0]) + bits_f(b[1]);

@@ -38,10 +38,45 @@ __device__ __forceinline__ h2_t nib_pair(uint32_t word, int i) {
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 
+__device__ __forceinline__ int f_bits(float v) { return __builtin_bit_cast(int, v); }
+__device__ __forceinline__ float bits_f(int v) { return __builtin_bit_cast(float, v); }
+
+// Cross-lane reductions on the VALU rather than through LDS permutes:
+// DPP row rotates and quad permutes inside a 16-lane row, v_permlane16_swap
+// / v_permlane32_swap across rows. ror4 + ror8 combine lanes i, i+4, i+8,
+// i+12 of a row; xor1 + xor2 the four lanes of a quad; rows_* lanes i, i^16,
+// i^32, i^48 (every lane receives the result).
+__device__ __forceinline__ float ror4(float v) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x124, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float ror8(float v) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
+  v = fmaxf(bits_f(a[0]), bits_f(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
+  return fmaxf(bits_f(b[0]), bits_f(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
+  v = bits_f(a[0]) + bits_f(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
+  return bits_f(b[0]) + bits_f(b[1]);
+}
+// Sum over the 64 lanes, in the same order in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += ror4(v);
+  v += ror8(v);
+  v += dpp_xor1(v);
+  v += dpp_xor2(v);
+  return rows_sum(v);
 }
 
 // Device-coherent accesses: 16-bit stores and loads through the atomic
@@ -201,7 +236,8 @@ __device__ __forceinline__ uint32_t quad_perm(uint32_t v, int ctrl_is_odd) {
 // Stages the row: with NORM it becomes fp16(x * rsqrt(mean(x^2) + eps) *
 // gamma) (RMSNorm in FP16); the slots of odd r are divided by 16 (exact
 // fp16 scaling). The natural-order (normalised) row also goes to xn_out if
-// given. Ends with a barrier. Requires kpad <= 8 * IT * NT.
+// given. Ends with a barrier. Requires kpad <= 8 * IT * NT, NT <= 1024 and
+// red[16] 16-byte aligned.
 template <int IT, bool NORM>
 __device__ void stage_row_mfma(const StageRegs<IT, NORM>& r, float eps, int k, int kpad, uint16_t* xs,
                                float* red, uint16_t* xn_out, const int NT) {
@@ -231,8 +267,14 @@ __device__ void stage_row_mfma(const StageRegs<IT, NORM>& r, float eps, int k, i
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
+    // the per-wavefront sums in order (slots past NT / 64 read as zero)
     float tot = 0.f;
-    for (int w = 0; w < NT / 64; ++w) tot += red[w];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f4_t r4 = *reinterpret_cast<const f4_t*>(red + 4 * q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tot += 4 * q + j < NT / 64 ? r4[j] : 0.f;
+    }
     rs = 1.0f / sqrtf(tot / (float)k + eps);
 #pragma unroll
     for (int it = 0; it < IT; ++it)
@@ -337,7 +379,7 @@ constexpr int kB1Threads = 1024;
 // IT activation words per thread. (B1Split, w4_b1_split: w4_internal.h.)
 // LDS of one batch-1 GEMV: the staged activation row, then reductions.
 __host__ __device__ constexpr size_t gemv_b1_lds_bytes(int groups, int waves, int tw) {
-  return (size_t)groups * kGroup * 2 + (size_t)(waves * 16 + tw * 16 + waves) * 4;
+  return (size_t)groups * kGroup * 2 + (size_t)(waves * 16 + tw * 16 + 16) * 4;  // + 16 RMSNorm slots
 }
 
 // One wavefront's share of a batch-1 GEMV. Virtual workgroup vb covers tiles
