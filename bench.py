@@ -217,9 +217,12 @@ def main():
     shares = {n: op_ms[n] * launches_per_step(n, sh) for n in op_ms}
     dom = max(shares, key=shares.get)
     dom_bytes = per[dom] / launches_per_step(dom, sh)
-    kernels = {"qkv": "gemv.hip", "oproj": "gemv.hip", "gate_up": "gemv.hip", "down": "gemv.hip",
-               "lm_head": "gemv.hip", "embed": "gemv.hip", "attn": "attention.hip"}
-    digest = source_digest(kernels[dom], "w4_internal.h")
+    # the sources each operation's kernel is built from (the digest ties the
+    # committed counter summary to them)
+    gemv_src = ("gemv.hip", "gemv_b1.h", "w4_internal.h")
+    kernels = {"qkv": gemv_src, "oproj": gemv_src, "gate_up": gemv_src, "down": gemv_src, "lm_head": gemv_src,
+               "embed": gemv_src, "attn": ("attention.hip", "attn_item.h", "gemv_b1.h", "w4_internal.h")}
+    digest = source_digest(*kernels[dom])
     achieved = dom_bytes / (op_ms[dom] * 1e-3)
 
     cpu = None if args.no_cpu else cpu_baseline(w)

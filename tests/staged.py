@@ -21,7 +21,12 @@ def buf(dm, which, batch):
 
 
 def kv_slot(dm, layer, which, page, slot):
-    return to_np16(dm.kv_cache[layer, which, page, :, slot])
+    """The [Hkv][D] values of one token slot (V slices are [D][16] on the device)."""
+    pool = dm.kv_cache[layer, which]
+    if which == 1:
+        pool = pool.view(pool.shape[0], pool.shape[1], pool.shape[3], pool.shape[2])
+        return to_np16(pool[page, :, :, slot])
+    return to_np16(pool[page, :, slot])
 
 
 def staged_layer(dm, w, layer, x_in, lw, kp, vp, tag="", log=print, live=None):

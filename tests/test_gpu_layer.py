@@ -30,8 +30,10 @@ def run_layer(dm: DeviceModel, x_in: np.ndarray, layer: int = 0):
 
 
 def check_kv_writes_only_the_slot(dm, w, cache0):
-    kv = dm.kv_cache.cpu()
-    changed = (kv.view(torch.int16) != cache0.cpu().view(torch.int16)).any(dim=-1)   # [L,2,P,Hkv,16]
+    diff = dm.kv_cache.cpu().view(torch.int16) != cache0.cpu().view(torch.int16)    # [L,2,P,Hkv,16,D]
+    k_changed = diff[:, 0].any(dim=-1)                                                 # K slices [16][D]
+    v_changed = diff[:, 1].reshape(diff[:, 1].shape[:3] + (diff.shape[-1], 16)).any(dim=-2)  # V slices [D][16]
+    changed = torch.stack([k_changed, v_changed], dim=1)                                # [L,2,P,Hkv,16]
     expect = torch.zeros_like(changed)
     for b in range(w.batch):
         pos = int(w.positions[b])

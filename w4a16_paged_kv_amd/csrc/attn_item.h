@@ -27,9 +27,6 @@
 
 namespace w4 {
 
-typedef float f4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ h2_t as_h2a(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 __device__ __forceinline__ uint16_t f2h_a(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -44,10 +41,6 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 
 constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time each
 
-__device__ __forceinline__ float half_sum(float v) {  // lanes i and i^32
-  const auto b = __builtin_amdgcn_permlane32_swap(f_bits(v), f_bits(v), false, false);
-  return bits_f(b[0]) + bits_f(b[1]);
-}
 
 // One work item (split of pages, KV head, sequence) on one workgroup of NT
 // threads. The first kAttnWaves wavefronts stream pages; any further
@@ -64,14 +57,9 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   static_assert(GQ >= 1 && GQ <= 8, "group");
   static_assert(NT >= kAttnWaves * 64 && NT % 64 == 0, "threads");
   constexpr int W = kAttnWaves;
-  constexpr int CW = 4;               // PV columns per lane
-  constexpr int LD = D / CW;          // lanes per token row for PV
-  constexpr int TPI = 64 / LD;        // token rows per PV load instruction
-  constexpr int NTOK = kPage / TPI;   // tokens per lane for PV
+  constexpr int NS = D / 16;          // 16-column slices of the P V product
   __shared__ float s_m[W][8], s_l[W][8];
-  __shared__ __align__(16) float s_pb[W][kPage][8];  // per-wavefront softmax weights [token][head]
-  __shared__ __align__(16) float s_al[W][8];         // per-wavefront rescale factors [head]
-  __shared__ float s_o[W][GQ][D];
+  __shared__ __align__(16) float s_o[W][GQ][D];
   __shared__ __align__(16) uint16_t s_q[GQ * D];     // the group's query heads
   __shared__ int s_last;
 
@@ -121,14 +109,18 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   const int qrow = min(qh, GQ - 1);        // heads past GQ read a real row and are zeroed
 
   const float scale = kLog2e / sqrtf((float)D);
+  // P V on the matrix cores too: O^T = V^T P with v_mfma_f32_16x16x16_f16,
+  // A = a 16-column slice of V^T (lane l: column 16 s + (l & 15), tokens
+  // 4 (l >> 4) .. +4, contiguous in the column-major V page), B = P, which
+  // the score step already left in B-operand order (lane l holds tokens
+  // 4 (l >> 4) + j of head l & 15); lane l accumulates
+  // O[head l & 15][16 s + 4 (l >> 4) + j], so each lane rescales only its
+  // own head's values.
   float m_h = -INFINITY, l_h = 0.f;        // softmax state of head qh
-  float o[GQ][CW];
+  f4_t acc[NS];
 #pragma unroll
-  for (int h = 0; h < GQ; ++h)
-#pragma unroll
-    for (int e = 0; e < CW; ++e) o[h][e] = 0.f;
-  const int d0 = CW * (lane % LD);         // PV columns of this lane
-  const int t0 = lane / LD;                // first PV token row of this lane
+  for (int sl = 0; sl < NS; ++sl) acc[sl] = (f4_t){0.f, 0.f, 0.f, 0.f};
+  const int tk = 4 * (lane >> 4);          // this lane's tokens in the P V operands
   const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
 
   // page p's id, validated (an invalid id is counted and read as page 0,
@@ -140,7 +132,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     return bad ? 0 : id;
   };
   u4_t kf[NK], kn[PF ? NK : 1];
-  u2_t vf[NTOK], vn[PF ? NTOK : 1];
+  u2_t vf[NS], vn[PF ? NS : 1];
   auto load_kv = [&](int page, u4_t* kk, u2_t* vv) {
     page = __builtin_amdgcn_readfirstlane(page);  // one page per wavefront: keeps the resources scalar
     const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
@@ -148,7 +140,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) kk[i] = ld128_agent(rk, 2 * (qh * D + 32 * i + kc));
 #pragma unroll
-    for (int i = 0; i < NTOK; ++i) vv[i] = ld64_agent(rv, 2 * ((t0 + TPI * i) * D + d0));
+    for (int i = 0; i < NS; ++i) vv[i] = ld64_agent(rv, 2 * ((16 * i + qh) * kPage + tk));
   };
   int valid_cur = 0, valid_nxt = 0;
   const int p_stop = pager ? p_end : pw0;  // non-page wavefronts skip the loop
@@ -177,80 +169,54 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     const float pm = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     const float n_h = fmaxf(m_h, pm);
     const float al = n_h == -INFINITY ? 1.f : exp2f(m_h - n_h);
+    // the fp32 weights enter the product as two fp16 terms (hi + lo: about
+    // 22 significant bits), so P V keeps fp32 accuracy on the fp16 MFMA
     float pj[4];
+    h4_t ph, pl;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pj[j] = n_h == -INFINITY ? 0.f : exp2f(sv[j] - n_h);
+    for (int j = 0; j < 4; ++j) {
+      pj[j] = n_h == -INFINITY ? 0.f : exp2f(sv[j] - n_h);
+      ph[j] = (_Float16)pj[j];
+      pl[j] = (_Float16)(pj[j] - (float)ph[j]);
+    }
     l_h = l_h * al + rows_sum((pj[0] + pj[1]) + (pj[2] + pj[3]));
     m_h = n_h;
-    // broadcast weights and rescale factors to the PV lanes through LDS
-    // (wavefront-private rows; LDS operations of a wavefront stay in order)
-    if (qh < 8) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s_pb[wave][4 * (lane >> 4) + j][qh] = pj[j];
-      if (lane < 8) s_al[wave][qh] = al;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // masked tokens contribute nothing even if their slots hold NaN
     if (valid < kPage) {
 #pragma unroll
-      for (int i = 0; i < NTOK; ++i)
-        if (t0 + TPI * i >= valid) vf[i] = (u2_t){0u, 0u};
-    }
-    const f4v al0 = *reinterpret_cast<const f4v*>(&s_al[wave][0]);
-    const f4v al1 = *reinterpret_cast<const f4v*>(&s_al[wave][4]);
+      for (int i = 0; i < NS; ++i) {
+        h4_t v4 = __builtin_bit_cast(h4_t, vf[i]);
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      const float al = h < 4 ? al0[h & 3] : al1[h & 3];
-#pragma unroll
-      for (int e = 0; e < CW; ++e) o[h][e] *= al;
-    }
-#pragma unroll
-    for (int i = 0; i < NTOK; ++i) {
-      const f4v p0 = *reinterpret_cast<const f4v*>(&s_pb[wave][t0 + TPI * i][0]);
-      const f4v p1 = *reinterpret_cast<const f4v*>(&s_pb[wave][t0 + TPI * i][4]);
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        const float pv = h < 4 ? p0[h & 3] : p1[h & 3];
-#pragma unroll
-        for (int e = 0; e < CW / 2; ++e) {
-          const h2_t v2 = as_h2a(vf[i][e]);
-          o[h][2 * e] = fmaf(pv, (float)v2[0], o[h][2 * e]);
-          o[h][2 * e + 1] = fmaf(pv, (float)v2[1], o[h][2 * e + 1]);
-        }
+        for (int j = 0; j < 4; ++j)
+          if (tk + j >= valid) v4[j] = (_Float16)0.f;
+        vf[i] = __builtin_bit_cast(u2_t, v4);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const h4_t v4 = __builtin_bit_cast(h4_t, vf[i]);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, ph, acc[i] * al, 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, pl, acc[i], 0, 0, 0);
+    }
     if (PF) {
 #pragma unroll
       for (int i = 0; i < NK; ++i) kf[i] = kn[PF ? i : 0];
 #pragma unroll
-      for (int i = 0; i < NTOK; ++i) vf[i] = vn[PF ? i : 0];
+      for (int i = 0; i < NS; ++i) vf[i] = vn[PF ? i : 0];
       valid_cur = valid_nxt;
     } else if (p + W < p_stop) {
       load_kv(checked(p + W, pid_nxt, valid_cur), kf, vf);
       pid_nxt = pt[min(p + 2 * W, a.max_pages - 1)];
     }
   }
-  // reduce o over the lanes holding other token rows of the same columns
-  // (lanes apart by multiples of LD: 32 for D = 128, 16 for D = 64)
-#pragma unroll
-  for (int h = 0; h < GQ; ++h)
-#pragma unroll
-    for (int e = 0; e < CW; ++e) o[h][e] = LD == 32 ? half_sum(o[h][e]) : rows_sum(o[h][e]);
   if (pager && lane < 8) {
     s_m[wave][lane] = m_h;
     s_l[wave][lane] = l_h;
   }
-  if (pager && lane < LD)
+  if (pager && qh < GQ)
 #pragma unroll
-    for (int h = 0; h < GQ; ++h)
-#pragma unroll
-      for (int e = 0; e < CW; ++e) s_o[wave][h][d0 + e] = o[h][e];
+    for (int i = 0; i < NS; ++i) *reinterpret_cast<f4_t*>(&s_o[wave][qh][16 * i + tk]) = acc[i];
   __syncthreads();
 
   // combine the wavefronts: this split's (o, m, l), or the output if one split

@@ -21,6 +21,7 @@
 namespace w4 {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
@@ -100,12 +101,16 @@ __device__ __forceinline__ u2_t ld64_agent(__amdgpu_buffer_rsrc_t r, int byte_of
 
 // ------------------------------------------------------------- epilogues
 
-__device__ __forceinline__ void kv_store(const QkvEpilogue& e, uint16_t* pool, int slot, int kvh, int dim0,
-                                         int dim1, float v0, float v1) {
+// One token's K or V values (dims dim0, dim1 of KV head kvh) into its page
+// slot. A (page, head) slice of K is [16 tokens][D]; of V it is [D][16
+// tokens] (column-major), the operand layout of the attention's P V product.
+__device__ __forceinline__ void kv_store(const QkvEpilogue& e, uint16_t* pool, bool v_layout, int slot, int kvh,
+                                         int dim0, int dim1, float v0, float v1) {
   if (slot < 0) return;  // invalid position or page: counted by the token plan
-  uint16_t* dst = pool + (((size_t)(slot >> 4) * e.n_kv_heads + kvh) * kPage + (slot & 15)) * e.head_dim;
-  st16_agent(dst + dim0, f2h(v0));
-  st16_agent(dst + dim1, f2h(v1));
+  uint16_t* sl = pool + ((size_t)(slot >> 4) * e.n_kv_heads + kvh) * kPage * e.head_dim;
+  const int t = slot & 15;
+  st16_agent(sl + (v_layout ? dim0 * kPage + t : t * e.head_dim + dim0), f2h(v0));
+  st16_agent(sl + (v_layout ? dim1 * kPage + t : t * e.head_dim + dim1), f2h(v1));
 }
 
 // Rows i and i+8 of tile t hold the rotate-half RoPE pair (dim0, dim0 + D/2)
@@ -136,10 +141,10 @@ __device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float 
       st16_agent(q + dim0, f2h(r0));
       st16_agent(q + dim1, f2h(r1));
     } else {
-      kv_store(e, e.k_pool, slot, head - e.n_heads, dim0, dim1, r0, r1);
+      kv_store(e, e.k_pool, false, slot, head - e.n_heads, dim0, dim1, r0, r1);
     }
   } else {
-    kv_store(e, e.v_pool, slot, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
+    kv_store(e, e.v_pool, true, slot, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
   }
 }
 

@@ -47,11 +47,18 @@ def upload_layer(w: Workload, l: int, bias: bool = False, device="cuda") -> Dict
     return d
 
 
+def v_pages_device(v: np.ndarray) -> np.ndarray:
+    """V pages [P][Hkv][16][D] in the device layout [P][Hkv][D][16] (each
+    (page, head) slice column-major)."""
+    return np.ascontiguousarray(np.swapaxes(v, -1, -2))
+
+
 def upload_kv(w: Workload, kv_cache: torch.Tensor, l: int, kv=None) -> None:
-    """Copy layer l's generated K and V pages into the [L][2][P][Hkv][16][D] cache."""
+    """Copy layer l's generated K and V pages into the [L][2][P][Hkv][16 x D] cache
+    (K slices [16][D], V slices [D][16])."""
     k, v = kv if kv is not None else w.kv(l)
     kv_cache[l, 0].copy_(to_dev(k, kv_cache.device))
-    kv_cache[l, 1].copy_(to_dev(v, kv_cache.device))
+    kv_cache[l, 1].copy_(to_dev(v_pages_device(v), kv_cache.device).view(kv_cache[l, 1].shape))
 
 
 def upload_embedding(w: Workload, device="cuda") -> torch.Tensor:
