@@ -320,7 +320,15 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     for (int u = 0; u < kFirst; ++u)
       if (u < nsplit) O = fmaf(wh[u], v0[r][u], O);
     const float* ps = pb + (size_t)h * (D + 2) + d;
-    for (int sp = kFirst; sp < nsplit; ++sp) O = fmaf(wh[sp], ld_agent(ps + (size_t)sp * GQ * (D + 2)), O);
+    // splits past the first sixteen: eight loads in flight, then their sums (in order)
+    for (int sp0 = kFirst; sp0 < nsplit; sp0 += 8) {
+      float t8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t8[u] = ld_agent(ps + (size_t)min(sp0 + u, nsplit - 1) * GQ * (D + 2));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp0 + u < nsplit) O = fmaf(wh[sp0 + u], t8[u], O);
+    }
     st16_agent(out + h * D + d, f2h_a(O));
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

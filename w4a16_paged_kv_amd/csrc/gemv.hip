@@ -100,73 +100,154 @@ __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
 }
 
 // ------------------------------------------------------- batch 2..16, MFMA
-// D[m][n] = sum_k x[m][k] W[n][k] over one 128-column group with four
-// v_mfma_f32_16x16x32_f16; lane l supplies A row m = l & 15 (batch row,
-// clamped to batch-1) and B column n = l & 15 (weight row), both for the
-// k-slots 8 (l >> 4) .. +8 of each step, which the packed layout provides.
-// The fp32 group result is scaled per weight row and accumulated.
-// Activations come pre-normalised; columns >= k read as zero.
-
-template <int EPI, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void w4_gemm_mfma_kernel(GemvArgs a) {
-  constexpr int NT = WAVES * 64;
-  __shared__ float red[WAVES][16][17];
-  __shared__ float tot[16][17];
+// The batch-1 decomposition with all 16 A rows real: the activation rows
+// (RMSNorm applied while staging when gamma is given; rows >= batch zero)
+// are staged in LDS in the MFMA k-slot
+// order, a window of GW groups at a time (one window up to K = 4096, 128 KiB
+// of LDS at most; rows padded by 16 bytes so the 16 lanes of a lane group,
+// one row each, read distinct banks), and the same packed blocks, exact dequantisation and
+// v_mfma_f32_16x16x32_f16 give D[batch row][weight row] in every lane. TW
+// tiles per workgroup, S wavefronts per tile; each wavefront streams its
+// window's blocks two batches of four ahead, the first batch issued before
+// the window is staged.
+template <int EPI, int S>
+__global__ __launch_bounds__(1024) void w4_gemm_rows_kernel(GemvArgs a, int TW, int GW) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int NT = blockDim.x, NW = NT >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.groups;
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + (size_t)t * G * 64 + lane;
-  const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024) +
-                       (size_t)t * G * 16 + (lane & 15);
-  const int mrow = min(lane & 15, a.batch - 1);
-  const uint16_t* xr = a.x + (size_t)mrow * a.x_stride + 32 * (lane >> 4);
-
-  f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;
-  for (int base = wave; base < G; base += U * WAVES) {
-    u4_t wv[U];
-    float sc[U];
+  const int KW = GW * kGroup + 8;  // row stride: 16 bytes of padding spread the 16 rows over the LDS banks
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                        // [16][KW]
+  float* red = reinterpret_cast<float*>(smem + (size_t)16 * KW * 2);       // [NW][16][16]
+  float* vals = red + NW * 256;                                            // [TW][16][16]
+  const int t = blockIdx.x * TW + wave / S, ks = wave % S;
+  const bool live = wave < S * TW && t < a.tiles;
+  const size_t base = (size_t)(live ? t : 0) * G;
+  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + base * 64 + lane;
+  const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024) + base * 16 + (lane & 15);
+  const uint16_t* xl = xs + (size_t)(lane & 15) * KW + 32 * (lane >> 4);
+  const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
+  const int e = threadIdx.x & 1;
+  const int wpr = GW * 16;  // 8-column words per staged row
+  // RMSNorm of the rows (with gamma): wavefront w sums the squares of rows
+  // w, w + NW, ..; the rows are scaled while they are staged
+  __shared__ float s_rs[16];
+  if (a.gamma) {
+    const int kw = a.k / 8;
+    for (int m = wave; m < 16; m += NW) {
+      float ss = 0.f;
+      if (m < a.batch)
+        for (int w0 = 0; w0 < kw; w0 += 8 * 64) {
+          u4_t v[8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = base + u * WAVES;
-      wv[u] = g < G ? __builtin_nontemporal_load(wb + (size_t)g * 64) : (u4_t){0u, 0u, 0u, 0u};
-      sc[u] = g < G ? h2f(sb[(size_t)g * 16]) : 0.f;
-    }
+          for (int j = 0; j < 8; ++j)
+            v[j] = *reinterpret_cast<const u4_t*>(a.x + (size_t)m * a.x_stride + 8 * min(w0 + lane + 64 * j, kw - 1));
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int g = base + u * WAVES;
-      if (g < G) {
-        f4_t d = {0.f, 0.f, 0.f, 0.f};
-        const u4_t* xp = reinterpret_cast<const u4_t*>(xr + (size_t)g * kGroup);
-        const int col0 = g * kGroup + 32 * (lane >> 4);
+          for (int j = 0; j < 8; ++j)
+            if (w0 + lane + 64 * j < kw)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u4_t xv = col0 + 8 * j < a.k ? xp[j] : (u4_t){0u, 0u, 0u, 0u};
-          const h8_t av = __builtin_bit_cast(h8_t, xv);
-          u4_t braw;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) braw[i] = __builtin_bit_cast(uint32_t, nib_pair(wv[u][j], i));
-          const h8_t bv = __builtin_bit_cast(h8_t, braw);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, d, 0, 0, 0);
+              for (int c = 0; c < 4; ++c) {
+                const h2_t h = as_h2(v[j][c]);
+                ss = fmaf((float)h[0], (float)h[0], ss);
+                ss = fmaf((float)h[1], (float)h[1], ss);
+              }
         }
-        acc += d * sc[u];
+      ss = wave_sum(ss);
+      if (lane == 0) s_rs[m] = 1.0f / sqrtf(ss / (float)a.k + a.eps);
+    }
+    __syncthreads();
+  }
+  f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < G; g0 += GW) {
+    const int gn = min(GW, G - g0);
+    const int ng = (live && ks < gn) ? (gn - ks + S - 1) / S : 0;  // groups g0 + ks + S i, i < ng
+    const int last = ng > 0 ? ng - 1 : 0;
+    u4_t bufA[kUnroll], bufB[kUnroll];
+    uint32_t scA[kUnroll], scB[kUnroll];
+    auto load = [&](u4_t* buf, uint32_t* sc, int i0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int g = min(g0 + ks + S * min(i0 + u, last), G - 1);
+        sc[u] = sb[(size_t)g * 16];
+        buf[u] = __builtin_nontemporal_load(wb + (size_t)g * 64);
+      }
+    };
+    auto compute = [&](const u4_t* buf, const uint32_t* sc, int i0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (i0 + u < ng) {
+          const f4_t d = mfma_block(buf[u], xl + (size_t)(ks + S * (i0 + u)) * kGroup, mlo, mhi);
+          acc += d * h2f((uint16_t)sc[u]);
+        }
+    };
+    load(bufA, scA, 0);
+    __syncthreads();  // the previous window's reads of xs are done
+    // stage the window: word wd = row * wpr + cw holds columns 128 g0 + 8 cw ..
+    // of activation row `row` (zero past k, past the window and for rows >= batch)
+    const int words = 16 * wpr;
+    for (int w0 = 0; w0 < words; w0 += 8 * NT) {  // every lane runs every round (quad permutes)
+      u4_t xv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int wd = w0 + (int)threadIdx.x + j * NT;
+        const int row = wd / wpr, cw = wd % wpr;
+        const int col = 128 * g0 + 8 * cw;
+        const bool in = wd < words && row < a.batch && cw < 16 * gn && col < a.k;
+        const u4_t v = *reinterpret_cast<const u4_t*>(a.x + (size_t)min(row, a.batch - 1) * a.x_stride +
+                                                      min(col, a.k - 8));
+        xv[j] = in ? v : (u4_t){0u, 0u, 0u, 0u};
+        if (a.gamma) {  // fp16(x * rs * gamma), the batch-1 staging's rounding
+          const u4_t gv = *reinterpret_cast<const u4_t*>(a.gamma + min(col, a.k - 8));
+          const float rs = s_rs[min(row, 15)];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const h2_t hv = as_h2(xv[j][c]), hg = as_h2(gv[c]);
+            h2_t r;
+            r[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
+            r[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
+            xv[j][c] = __builtin_bit_cast(uint32_t, r);
+          }
+          if (a.xn_out && blockIdx.x == 0 && in)
+            *reinterpret_cast<u4_t*>(a.xn_out + (size_t)row * a.xn_stride + col) = xv[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int wd = w0 + (int)threadIdx.x + j * NT;
+        const u4_t o = slot_word(xv[j], e);
+        if (wd < words) *reinterpret_cast<u4_t*>(xs + (size_t)(wd / wpr) * KW + 8 * (wd % wpr)) = o;
       }
     }
+    __syncthreads();
+    for (int i = 0; i < ng; i += 2 * kUnroll) {
+      load(bufB, scB, i + kUnroll);
+      compute(bufA, scA, i);
+      if (i + kUnroll >= ng) break;
+      load(bufA, scA, i + 2 * kUnroll);
+      compute(bufB, scB, i + kUnroll);
+    }
   }
-  // acc[j] = D[m = 4 (lane >> 4) + j][n = lane & 15]
+  // lane l: acc[j] = D[batch row 4 (l >> 4) + j][weight row l & 15]
+  if (wave < S * TW)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) red[wave][4 * (lane >> 4) + j][lane & 15] = acc[j];
+    for (int j = 0; j < 4; ++j) red[(wave * 16 + 4 * (lane >> 4) + j) * 16 + (lane & 15)] = acc[j];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 256; idx += NT) {
+  for (int idx = threadIdx.x; idx < TW * 256; idx += NT) {
+    const int tl = idx >> 8, mn = idx & 255;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[w][idx >> 4][idx & 15];
-    tot[idx >> 4][idx & 15] = v;
+    for (int k = 0; k < S; ++k) v += red[(tl * S + k) * 256 + mn];
+    vals[idx] = v;
   }
   __syncthreads();
   constexpr int per = epi_items<EPI>();
-  for (int item = threadIdx.x; item < a.batch * per; item += NT)
-    epilogue<EPI>(a, item / per, t, item % per, &tot[item / per][0]);
+  for (int item = threadIdx.x; item < TW * a.batch * per; item += NT) {
+    const int tl = item / (a.batch * per), r = item % (a.batch * per);
+    const int m = r / per, i = r % per;
+    const int tt = blockIdx.x * TW + tl;
+    if (tt < a.tiles) epilogue<EPI>(a, m, tt, i, vals + (tl * 16 + m) * 16);
+  }
 }
 
 // ------------------------------------------------------------ fp16 lm_head
@@ -360,6 +441,19 @@ static hipError_t launch_b1_it(const GemvArgs& a, const B1Split& sp, hipStream_t
   return hipErrorInvalidValue;  // activation row longer than one workgroup can stage
 }
 
+// Kernels above 64 KiB of dynamic LDS need the per-function opt-in once (the
+// limit covers the kernel's static LDS too: 160 KiB per workgroup in all).
+constexpr int kRowsMaxDynLds = 160 * 1024 - 1024;
+template <int EPI, int S>
+static hipError_t launch_rows(const GemvArgs& a, int tw, int gw, int nt, size_t lds, hipStream_t s) {
+  if (lds > (size_t)kRowsMaxDynLds) return hipErrorInvalidValue;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemm_rows_kernel<EPI, S>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kRowsMaxDynLds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((w4_gemm_rows_kernel<EPI, S>), dim3(ceil_div(a.tiles, tw)), dim3(nt), lds, s, a, tw, gw);
+  return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
   if (a.batch == 1) {
@@ -375,8 +469,20 @@ static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
     }
     if (e != hipSuccess) return e;
   } else {
-    constexpr int WAVES = 4;
-    hipLaunchKernelGGL((w4_gemm_mfma_kernel<EPI, WAVES>), dim3(a.tiles), dim3(WAVES * 64), 0, s, a);
+    if (a.batch > 16) return hipErrorInvalidValue;
+    const B1Split sp = w4_b1_split(a.tiles, a.groups);
+    const int nt = std::max(256, 64 * sp.s * sp.tw);
+    const int gw = std::min(a.groups, 32);  // activation window: at most 4096 columns (128 KiB of LDS)
+    const size_t lds = (size_t)16 * (gw * kGroup + 8) * 2 + ((size_t)(nt / 64) * 256 + (size_t)sp.tw * 256) * 4;
+    hipError_t e = hipSuccess;
+    switch (sp.s) {
+      case 8: e = launch_rows<EPI, 8>(a, sp.tw, gw, nt, lds, s); break;
+      case 4: e = launch_rows<EPI, 4>(a, sp.tw, gw, nt, lds, s); break;
+      case 2: e = launch_rows<EPI, 2>(a, sp.tw, gw, nt, lds, s); break;
+      case 1: e = launch_rows<EPI, 1>(a, sp.tw, gw, nt, lds, s); break;
+      default: e = hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -238,6 +238,24 @@ __device__ __forceinline__ uint32_t quad_perm(uint32_t v, int ctrl_is_odd) {
                      : (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xA0, 0xF, 0xF, false);
 }
 
+// Slot group sg = wd of the natural word xv held by this lane (e = wd % 2),
+// built from the words of its 4-lane quad; the slots of odd r are divided
+// by 16 (exact fp16 scaling). All four lanes of the quad must take part.
+__device__ __forceinline__ u4_t slot_word(const u4_t xv, int e) {
+  const h2_t sc = e ? (h2_t){(_Float16)0.0625f, (_Float16)0.0625f} : (h2_t){(_Float16)1.0f, (_Float16)1.0f};
+  // words j0 (lanes {0,0,2,2} of the quad) and j0 + 1 (lanes {1,1,3,3})
+  const uint32_t a0 = quad_perm(xv[0], 0), a1 = quad_perm(xv[1], 0);
+  const uint32_t a2 = quad_perm(xv[2], 0), a3 = quad_perm(xv[3], 0);
+  const uint32_t b0 = quad_perm(xv[0], 1), b1 = quad_perm(xv[1], 1);
+  const uint32_t b2 = quad_perm(xv[2], 1), b3 = quad_perm(xv[3], 1);
+  u4_t o;
+  o[0] = __builtin_bit_cast(uint32_t, as_h2(e ? a1 : a0) * sc);
+  o[1] = __builtin_bit_cast(uint32_t, as_h2(e ? a3 : a2) * sc);
+  o[2] = __builtin_bit_cast(uint32_t, as_h2(e ? b1 : b0) * sc);
+  o[3] = __builtin_bit_cast(uint32_t, as_h2(e ? b3 : b2) * sc);
+  return o;
+}
+
 // Stages the row: with NORM it becomes fp16(x * rsqrt(mean(x^2) + eps) *
 // gamma) (RMSNorm in FP16); the slots of odd r are divided by 16 (exact
 // fp16 scaling). The natural-order (normalised) row also goes to xn_out if
@@ -292,20 +310,9 @@ __device__ void stage_row_mfma(const StageRegs<IT, NORM>& r, float eps, int k, i
         xv[it][d] = __builtin_bit_cast(uint32_t, v);
       }
   }
-  const h2_t sc = e ? (h2_t){(_Float16)0.0625f, (_Float16)0.0625f} : (h2_t){(_Float16)1.0f, (_Float16)1.0f};
   u4_t o[IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    // words j0 (lanes {0,0,2,2} of the quad) and j0 + 1 (lanes {1,1,3,3})
-    const uint32_t a0 = quad_perm(xv[it][0], 0), a1 = quad_perm(xv[it][1], 0);
-    const uint32_t a2 = quad_perm(xv[it][2], 0), a3 = quad_perm(xv[it][3], 0);
-    const uint32_t b0 = quad_perm(xv[it][0], 1), b1 = quad_perm(xv[it][1], 1);
-    const uint32_t b2 = quad_perm(xv[it][2], 1), b3 = quad_perm(xv[it][3], 1);
-    o[it][0] = __builtin_bit_cast(uint32_t, as_h2(e ? a1 : a0) * sc);
-    o[it][1] = __builtin_bit_cast(uint32_t, as_h2(e ? a3 : a2) * sc);
-    o[it][2] = __builtin_bit_cast(uint32_t, as_h2(e ? b1 : b0) * sc);
-    o[it][3] = __builtin_bit_cast(uint32_t, as_h2(e ? b3 : b2) * sc);
-  }
+  for (int it = 0; it < IT; ++it) o[it] = slot_word(xv[it], e);
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int wd = tid + it * NT;
@@ -322,10 +329,11 @@ __device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
   return r;
 }
 
-// Sum over one block of q * x for weight row lane & 15: d[0] of lanes 0..15
-// after four chained MFMAs over the lane group's staged chunk xl.
-__device__ __forceinline__ float mfma_block_b1(const u4_t w, const uint16_t* __restrict__ xl, uint32_t mlo,
-                                               uint32_t mhi) {
+// One block's product on the matrix cores: four chained MFMAs over the lane
+// group's staged chunk xl (A row l & 15); lane l ends with
+// D[activation row 4 (l >> 4) + j][weight row l & 15].
+__device__ __forceinline__ f4_t mfma_block(const u4_t w, const uint16_t* __restrict__ xl, uint32_t mlo,
+                                           uint32_t mhi) {
   const u4_t* xp = reinterpret_cast<const u4_t*>(xl);
   f4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -341,7 +349,13 @@ __device__ __forceinline__ float mfma_block_b1(const u4_t w, const uint16_t* __r
     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xp[r]), __builtin_bit_cast(h8_t, b),
                                                d, 0, 0, 0);
   }
-  return d[0];
+  return d;
+}
+// Batch 1: every lane group reads the same activation row; D row 0 (d[0] of
+// lanes 0..15) is the row sum for weight row lane & 15.
+__device__ __forceinline__ float mfma_block_b1(const u4_t w, const uint16_t* __restrict__ xl, uint32_t mlo,
+                                               uint32_t mhi) {
+  return mfma_block(w, xl, mlo, mhi)[0];
 }
 
 // The QKV epilogue's per-thread RoPE rotation and the token's K/V slot

@@ -141,19 +141,19 @@ static GemvArgs gemv_args(const void* w, int n, int k, const uint16_t* x, int x_
 
 // Arguments of the operations of decoder layer l for `batch` sequences. The
 // residual stream goes x_in -> (o projection) x_out -> (down projection)
-// x_out; q, o and h live in the workspace. At batch 1 the RMSNorms run in the
-// projections' prologues; above it in a separate kernel into xn.
+// x_out; q, o and h live in the workspace. The RMSNorms run while the qkv and
+// gate/up projections stage their activation rows (the normalised rows also
+// go to xn, from workgroup 0).
 static GemvArgs qkv_args(w4_model* m, int l, const uint16_t* x_in, int batch) {
   const w4_config& c = m->cfg;
   const w4_layer_weights& W = m->layers[l];
   const WsLayout& L = m->L;
   uint16_t* xn = m->at<uint16_t>(L.xn);
   const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
-  GemvArgs a = batch == 1 ? gemv_args(W.qkv, qkv_rows, c.hidden, x_in, c.hidden, W.attn_norm, c.rms_eps,
-                                      nullptr, 0, nullptr, 1)
-                          : gemv_args(W.qkv, qkv_rows, c.hidden, xn, L.xn_stride, nullptr, 0.f, nullptr, 0,
-                                      nullptr, batch);
-  if (batch == 1) a.xn_out = xn;
+  GemvArgs a = gemv_args(W.qkv, qkv_rows, c.hidden, x_in, c.hidden, W.attn_norm, c.rms_eps, nullptr, 0, nullptr,
+                         batch);
+  a.xn_out = xn;
+  a.xn_stride = L.xn_stride;
   a.qkv.q_out = m->at<uint16_t>(L.q);
   a.qkv.q_stride = c.n_heads * c.head_dim;
   a.qkv.k_pool = m->k_pool(l);
@@ -204,11 +204,10 @@ static GemvArgs gate_up_args(w4_model* m, int l, const uint16_t* x, int batch) {
   const WsLayout& L = m->L;
   uint16_t* xn = m->at<uint16_t>(L.xn);
   uint16_t* h = m->at<uint16_t>(L.h);
-  GemvArgs a = batch == 1 ? gemv_args(W.gate_up, 2 * c.ffn, c.hidden, x, c.hidden, W.mlp_norm, c.rms_eps, h,
-                                      L.h_stride, nullptr, 1)
-                          : gemv_args(W.gate_up, 2 * c.ffn, c.hidden, xn, L.xn_stride, nullptr, 0.f, h,
-                                      L.h_stride, nullptr, batch);
-  if (batch == 1) a.xn_out = xn;
+  GemvArgs a = gemv_args(W.gate_up, 2 * c.ffn, c.hidden, x, c.hidden, W.mlp_norm, c.rms_eps, h, L.h_stride,
+                         nullptr, batch);
+  a.xn_out = xn;
+  a.xn_stride = L.xn_stride;
   return a;
 }
 
@@ -222,14 +221,8 @@ static GemvArgs down_args(w4_model* m, int l, uint16_t* x, int batch) {
 static int enqueue_op(w4_model* m, int op, int l, const uint16_t* x_in, uint16_t* x_out,
                       const StepInputs& in, int batch, hipStream_t s) {
   const w4_config& c = m->cfg;
-  const w4_layer_weights& W = m->layers[l];
-  const WsLayout& L = m->L;
-  uint16_t* xn = m->at<uint16_t>(L.xn);
-  const bool b1 = batch == 1;
   switch (op) {
-    case W4_OP_QKV:  // qkv projection (RMSNorm prologue at batch 1), RoPE, K/V page write
-      if (!b1) W4_LAUNCH(launch_rmsnorm_rows(x_in, c.hidden, W.attn_norm, c.rms_eps, c.hidden, xn,
-                                             L.xn_stride, batch, s));
+    case W4_OP_QKV:  // RMSNorm while staging, qkv projection, RoPE, K/V page write
       W4_LAUNCH(launch_w4_gemv(EPI_QKV, qkv_args(m, l, x_in, batch), s));
       return W4_OK;
     case W4_OP_ATTN:  // paged attention, split over pages, LSE merge by the last split
@@ -238,9 +231,7 @@ static int enqueue_op(w4_model* m, int op, int l, const uint16_t* x_in, uint16_t
     case W4_OP_OPROJ:  // o projection + residual
       W4_LAUNCH(launch_w4_gemv(EPI_RESID, oproj_args(m, l, x_in, x_out, batch), s));
       return W4_OK;
-    case W4_OP_GATE_UP:  // gate/up (RMSNorm prologue at batch 1) with SiLU-mul
-      if (!b1) W4_LAUNCH(launch_rmsnorm_rows(x_out, c.hidden, W.mlp_norm, c.rms_eps, c.hidden, xn,
-                                             L.xn_stride, batch, s));
+    case W4_OP_GATE_UP:  // RMSNorm while staging, gate/up with SiLU-mul
       W4_LAUNCH(launch_w4_gemv(EPI_SILU, gate_up_args(m, l, x_out, batch), s));
       return W4_OK;
     case W4_OP_DOWN:  // down projection + residual

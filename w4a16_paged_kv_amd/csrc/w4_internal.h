@@ -87,12 +87,13 @@ struct GemvArgs {
   int32_t tiles, groups;  // ceil(n/16), ceil(k/128)
   const uint16_t* x;      // input fp16 [B][x_stride]
   int32_t x_stride;
-  const uint16_t* gamma;  // RMSNorm weight applied to x first (batch-1 kernel), or nullptr
+  const uint16_t* gamma;  // RMSNorm weight applied to each row of x first, or nullptr
   float eps;
   uint16_t* y;            // output fp16 [B][y_stride]
   int32_t y_stride;
   const uint16_t* resid;  // EPI_RESID: residual input [B][y_stride] (may alias y)
-  uint16_t* xn_out;       // batch-1 kernel: workgroup 0 also stores the normalised x here, or nullptr
+  uint16_t* xn_out;       // with gamma: workgroup 0 also stores the normalised rows here, or nullptr
+  int32_t xn_stride;      // row stride of xn_out (batch > 1)
   int32_t batch;
   QkvEpilogue qkv;
 };
@@ -107,7 +108,8 @@ struct F16GemvArgs {
   float eps;
   uint16_t* y;
   int32_t y_stride;
-  uint16_t* xn_out;       // batch-1 kernel: workgroup 0 also stores the normalised x here, or nullptr
+  uint16_t* xn_out;       // with gamma: workgroup 0 also stores the normalised rows here, or nullptr
+  int32_t xn_stride;      // row stride of xn_out (batch > 1)
   int32_t batch;
 };
 
