@@ -189,6 +189,16 @@ def main():
     ms = timed(step, args.steps)
     wall = time.perf_counter() - t_wall
     assert m.w4_device_errors() == 0
+    # per-step distribution (one event pair per step, after the timed region)
+    per_step = []
+    for _ in range(max(20, args.steps // 4)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per_step.append(a.elapsed_time(b))
+    pct = np.percentile(per_step, [10, 50, 90])
     # host-array inputs (includes the staging copies) and eager launches, for context
     host_ms = timed(lambda: m.decode_step(tokens, pos, pt, ctx, logits), max(10, args.steps // 4))
     m.w4_set_graph(False)
@@ -250,6 +260,7 @@ def main():
         "effective_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "pct_of_peak": round(100 * step_bytes / (ms * 1e-3) / PEAK_HBM, 2),
         "bytes_per_step": int(step_bytes),
+        "ms_per_step_p10_p50_p90": [round(float(v), 4) for v in pct],
         "ms_per_step_host_inputs": round(host_ms, 4),
         "ms_per_step_eager": round(eager_ms, 4),
         "wall_s_timed": round(wall, 3),
