@@ -81,7 +81,8 @@ __device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* ds
 // order).
 template <int EPI, int S, int IT>
 __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
-  constexpr bool NORM = GemvB1<EPI, S, IT>::NORM;
+  using Part = GemvB1Sel<EPI, S, IT>;
+  constexpr bool NORM = Part::NORM;
   const int NT = blockDim.x;
   extern __shared__ __align__(16) uint8_t smem[];
   const int kpad = a.groups * kGroup;
@@ -89,11 +90,12 @@ __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
   StageRegs<IT, NORM> st;
   stage_load(st, a.x, a.gamma, a.k, NT);
   const QkvPre pre = qkv_pre<EPI>(a, blockIdx.x, TW);
-  GemvB1<EPI, S, IT> g;
+  Part g;
   g.assign(a, blockIdx.x, TW, wave);
   g.prefetch();
   __builtin_amdgcn_sched_barrier(0);  // keep the prologue's arithmetic behind the first weight loads
-  float* nred = reinterpret_cast<float*>(smem + (size_t)kpad * 2) + (NT / 64) * 16 + TW * 16;
+  g.clear(smem, kpad, TW);
+  float* nred = reinterpret_cast<float*>(smem + (size_t)kpad * 2) + gemv_b1_red_floats(S, NT / 64, TW);
   stage_row_mfma(st, a.eps, a.k, kpad, reinterpret_cast<uint16_t*>(smem), nred,
                  (a.xn_out && blockIdx.x == 0) ? a.xn_out : nullptr, NT);
   g.finish(a, blockIdx.x, TW, wave, smem, pre);
@@ -412,20 +414,21 @@ B1Split w4_b1_split(int tiles, int groups) {
 
 template <int EPI, int S, int IT>
 static void launch_b1(const GemvArgs& a, int tw, int nt, hipStream_t s) {
-  const size_t lds = gemv_b1_lds_bytes(a.groups, nt / 64, tw);
+  const size_t lds = gemv_b1_lds_bytes(a.groups, S, nt / 64, tw);
   hipLaunchKernelGGL((w4_gemv_b1_kernel<EPI, S, IT>), dim3(ceil_div(a.tiles, tw)), dim3(nt), lds, s, a, tw);
 }
 
-// The workgroup is its S * TW working wavefronts (at least four), unless
-// the activation row then needs more than kMaxIt words per thread; then it
-// has kB1Threads threads like the persistent kernel's phases. The staged
+// The workgroup is its working wavefronts (S * TW, or kRangeWaves when
+// S == 1; at least four), unless the activation row then needs more than
+// kMaxIt words per thread; then it has kB1Threads threads like the
+// persistent kernel's phases. The staged
 // row and every product are the same either way, and so is the RMSNorm sum
 // when the row fits one pass of the threads (8 * nt >= k: each thread then
 // holds one word, the words past k are zero).
 constexpr int kMaxIt = 5;
 template <int EPI, int S>
 static hipError_t launch_b1_it(const GemvArgs& a, const B1Split& sp, hipStream_t s) {
-  int nt = std::max(256, 64 * S * sp.tw);
+  int nt = std::max(256, 64 * (S == 1 ? kRangeWaves : S * sp.tw));
   int it = ceil_div(a.groups * kGroup, 8 * nt);
   if (it > kMaxIt) {
     nt = kB1Threads;

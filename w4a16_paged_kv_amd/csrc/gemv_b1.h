@@ -16,6 +16,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "w4_internal.h"
 
 namespace w4 {
@@ -396,9 +398,20 @@ constexpr int kB1Threads = 1024;
 // sixteen (qkv 6.0 -> 5.0 us, down 10.0 -> 9.1 us), because the CU issues
 // the oldest wavefront's loads first and the youngest ones fall behind.
 // IT activation words per thread. (B1Split, w4_b1_split: w4_internal.h.)
+// With S == 1 (a workgroup holds more tiles than it has wavefronts) the
+// workgroup's blocks are instead cut into kRangeWaves contiguous runs
+// (GemvB1Range below).
+constexpr int kRangeWaves = 8;
+
+// Floats of per-wavefront partial sums a batch-1 GEMV keeps in LDS after the
+// staged row: [waves][16] (K split) or [tw][kRangeWaves][16] (runs), then
+// the reduced [tw][16].
+__host__ __device__ constexpr int gemv_b1_red_floats(int s, int waves, int tw) {
+  return (s == 1 ? tw * kRangeWaves * 16 : waves * 16) + tw * 16;
+}
 // LDS of one batch-1 GEMV: the staged activation row, then reductions.
-__host__ __device__ constexpr size_t gemv_b1_lds_bytes(int groups, int waves, int tw) {
-  return (size_t)groups * kGroup * 2 + (size_t)(waves * 16 + tw * 16 + 16) * 4;  // + 16 RMSNorm slots
+__host__ __device__ constexpr size_t gemv_b1_lds_bytes(int groups, int s, int waves, int tw) {
+  return (size_t)groups * kGroup * 2 + (size_t)(gemv_b1_red_floats(s, waves, tw) + 16) * 4;  // + 16 RMSNorm slots
 }
 
 // One wavefront's share of a batch-1 GEMV. Virtual workgroup vb covers tiles
@@ -438,6 +451,8 @@ struct GemvB1 {
   }
   // the first batch of weight blocks: needs nothing the previous operation writes
   __device__ __forceinline__ void prefetch() { load(bufA, scA, 0); }
+  // LDS the partial sums need cleared before the row is staged: none
+  __device__ __forceinline__ void clear(uint8_t*, int, int) {}
 
   // After the activation row is staged in LDS (xs): stream the remaining
   // blocks, reduce the S wavefronts of each tile in LDS, apply the epilogue.
@@ -491,5 +506,125 @@ struct GemvB1 {
     }
   }
 };
+
+// One wavefront's share of a batch-1 GEMV whose workgroup holds more tiles
+// than wavefronts (S == 1; the gate/up projection of the 7B shape: ten
+// tiles of 28 groups). The workgroup's blocks, tile after tile (consecutive
+// in memory), are cut into kRangeWaves contiguous runs; a run may end inside
+// a tile, so each wavefront leaves one partial sum per tile it touched in
+// LDS ([tile][wavefront][16], cleared before the row is staged) and the
+// tile's sum adds them in wavefront order. The CU serves the oldest
+// wavefront of each SIMD first, so the first SIMD slot (wavefronts 0..3)
+// takes 5/4 of the blocks of the second and both slots finish together
+// (7B gate/up per launch: ten one-tile wavefronts 15.3-16.1 us, eight equal
+// runs 15.8 us, eight 5:4 runs 14.4-15.0 us).
+template <int EPI, int IT>
+struct GemvB1Range {
+  static constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SILU;
+  static constexpr int W = kRangeWaves;
+  int b0, n, last, g0, tl0;
+  const u4_t* wb;
+  const uint16_t* sb;
+  u4_t bufA[kUnroll], bufB[kUnroll];
+  uint32_t scA[kUnroll], scB[kUnroll];
+
+  // run weight of wavefront v: 5 in the first SIMD slot, 4 after it
+  static __device__ __forceinline__ int weight(int v) { return v < 4 ? 5 : 4; }
+
+  __device__ __forceinline__ void assign(const GemvArgs& a, int vb, int tw, int w) {
+    const int lane = threadIdx.x & 63;
+    const int t0 = vb * tw;
+    const int B = min(tw, a.tiles - t0) * a.groups;  // this workgroup's blocks (>= 1)
+    int tot = 0, pre = 0;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      pre += v < w ? weight(v) : 0;
+      tot += weight(v);
+    }
+    const bool live = w >= 0 && w < W;
+    b0 = live ? (int)((long)B * pre / tot) : 0;
+    n = live ? (int)((long)B * (pre + weight(w)) / tot) - b0 : 0;
+    last = n > 0 ? n - 1 : 0;
+    g0 = n > 0 ? b0 % a.groups : 0;
+    tl0 = n > 0 ? b0 / a.groups : 0;
+    const size_t base = (size_t)t0 * a.groups + min(b0, B - 1);  // an empty run re-reads a block of its workgroup
+    wb = reinterpret_cast<const u4_t*>(a.w) + base * 64 + lane;
+    sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * a.groups * 1024) + base * 16 + (lane & 15);
+  }
+  __device__ __forceinline__ void load(u4_t* buf, uint32_t* sc, int i0) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = min(i0 + u, last);
+      buf[u] = __builtin_nontemporal_load(wb + (size_t)i * 64);
+      sc[u] = sb[(size_t)i * 16];
+    }
+  }
+  __device__ __forceinline__ void prefetch() { load(bufA, scA, 0); }
+  // zeroes the [tw][W][16] partial sums (a wavefront writes only the tiles its run touches)
+  __device__ __forceinline__ void clear(uint8_t* smem, int kpad, int tw) {
+    float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);
+    for (int i = threadIdx.x; i < tw * W * 16; i += blockDim.x) red[i] = 0.f;
+  }
+
+  __device__ void finish(const GemvArgs& a, int vb, int tw, int w, uint8_t* smem, const QkvPre& pre) {
+    const int lane = threadIdx.x & 63;
+    const int kpad = a.groups * kGroup;
+    const uint16_t* xs = reinterpret_cast<const uint16_t*>(smem);
+    float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);  // [tw][W][16]
+    float* vals = red + tw * W * 16;                                 // [tw][16]
+    const uint16_t* xl = xs + 32 * (lane >> 4);
+    const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
+    float acc = 0.f;
+    int g = g0, tl = tl0;
+    auto compute = [&](const u4_t* buf, const uint32_t* sc, int i0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        if (i0 + u < n) {
+          const float d = mfma_block_b1(buf[u], xl + (size_t)g * kGroup, mlo, mhi);
+          acc = fmaf(d, h2f((uint16_t)sc[u]), acc);
+          if (++g == a.groups) {  // the run leaves tile tl
+            if (lane < 16) red[(tl * W + w) * 16 + lane] = acc;
+            acc = 0.f;
+            g = 0;
+            ++tl;
+          }
+        }
+    };
+    for (int i = 0; i < n; i += 2 * kUnroll) {
+      load(bufB, scB, i + kUnroll);
+      compute(bufA, scA, i);
+      if (i + kUnroll >= n) break;
+      load(bufA, scA, i + 2 * kUnroll);
+      compute(bufB, scB, i + kUnroll);
+    }
+    if (g != 0 && lane < 16) red[(tl * W + w) * 16 + lane] = acc;  // the run ends inside tile tl
+    __syncthreads();
+    if ((int)threadIdx.x < tw * 16) {
+      const int tl = threadIdx.x / 16, r = threadIdx.x % 16;
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < W; ++k) v += red[(tl * W + k) * 16 + r];
+      vals[tl * 16 + r] = v;
+    }
+    __syncthreads();
+    constexpr int per = epi_items<EPI>();
+    if ((int)threadIdx.x < tw * per) {
+      const int tl = threadIdx.x / per;
+      const int tt = vb * tw + tl;
+      if (tt < a.tiles) {
+        const int i = threadIdx.x % per;
+        if (EPI == EPI_QKV)
+          epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], pre.c, pre.s, pre.slot);
+        else
+          epilogue<EPI>(a, 0, tt, i, vals + tl * 16);
+      }
+    }
+  }
+};
+
+// The batch-1 decomposition for a split: contiguous runs when S == 1, else
+// the K split.
+template <int EPI, int S, int IT>
+using GemvB1Sel = typename std::conditional<S == 1, GemvB1Range<EPI, IT>, GemvB1<EPI, S, IT>>::type;
 
 }  // namespace w4

@@ -94,9 +94,10 @@ __device__ __forceinline__ bool grid_sync(uint32_t* bar, uint32_t base, uint32_t
 template <int EPI, int S, int IT>
 __device__ __forceinline__ bool gemv_phase(const GemvArgs& a, int tw, uint32_t* bar, uint32_t base, uint32_t epoch,
                            uint8_t* smem) {
-  constexpr bool NORM = GemvB1<EPI, S, IT>::NORM;
+  using Part = GemvB1Sel<EPI, S, IT>;
+  constexpr bool NORM = Part::NORM;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  GemvB1<EPI, S, IT> g;
+  Part g;
   g.assign(a, blockIdx.x, tw, wave);
   g.prefetch();
   if (epoch != base && !grid_sync(bar, base, epoch)) return false;
@@ -104,7 +105,8 @@ __device__ __forceinline__ bool gemv_phase(const GemvArgs& a, int tw, uint32_t* 
   stage_load(st, a.x, a.gamma, a.k, kB1Threads);
   const QkvPre pre = qkv_pre<EPI>(a, blockIdx.x, tw);
   const int kpad = a.groups * kGroup;
-  float* nred = reinterpret_cast<float*>(smem + (size_t)kpad * 2) + (kB1Threads / 64) * 16 + tw * 16;
+  g.clear(smem, kpad, tw);
+  float* nred = reinterpret_cast<float*>(smem + (size_t)kpad * 2) + gemv_b1_red_floats(S, kB1Threads / 64, tw);
   stage_row_mfma(st, a.eps, a.k, kpad, reinterpret_cast<uint16_t*>(smem), nred, nullptr, kB1Threads);
   g.finish(a, blockIdx.x, tw, wave, smem, pre);
   __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stores are complete before the next barrier
@@ -185,7 +187,8 @@ size_t persistent_bar_words(int grid) { return (size_t)kBarArrive + 16 * (size_t
 size_t persistent_lds_bytes(const w4_config& c) {
   size_t m = 0;
   for (int k : {c.hidden, c.n_heads * c.head_dim, c.ffn})
-    m = std::max(m, gemv_b1_lds_bytes(w4_groups(k), kB1Threads / 64, 16));
+    for (int sp : {1, 2})  // runs or K split, 16 tiles at most
+      m = std::max(m, gemv_b1_lds_bytes(w4_groups(k), sp, kB1Threads / 64, 16));
   return m;
 }
 
