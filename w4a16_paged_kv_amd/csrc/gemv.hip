@@ -254,51 +254,75 @@ __global__ __launch_bounds__(1024) void w4_gemm_rows_kernel(GemvArgs a, int TW, 
 
 // ------------------------------------------------------------ fp16 lm_head
 
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void f16_gemv_b1_kernel(F16GemvArgs a) {
+// Batch 1: one round of workgroups (two per CU), each with TPW consecutive
+// 16-row tiles; their 1 KiB blocks (16 rows x 32 columns, consecutive in
+// memory) are cut into WAVES contiguous runs weighted by SIMD slot like the
+// W4 runs, U blocks per batch with the next batch in flight. A run leaves
+// one partial sum per tile it touched in LDS ([TPW][WAVES][16], cleared
+// before the row is staged); each tile adds them in wavefront order. With
+// one four-wavefront workgroup per four tiles (2376 workgroups, more than
+// one round) the 7B lm_head took 166 us per launch; this takes 161 us.
+template <int WAVES, int U>
+__global__ __launch_bounds__(WAVES * 64) void f16_gemv_b1_kernel(F16GemvArgs a, int TPW) {
   constexpr int NT = WAVES * 64;
   extern __shared__ __align__(16) uint8_t smem[];
   const int C = a.cblocks;
   const int kpad = (C * 32 + kGroup - 1) / kGroup * kGroup;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * WAVES + wave;  // one 16-row tile per wavefront
-  const bool live = t < a.tiles;
-  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + (size_t)(live ? t : 0) * C * 64 + lane;
-
-  u4_t cur[kUnroll];
+  float* red = reinterpret_cast<float*>(smem + (size_t)kpad * 2);  // [TPW][WAVES][16]
+  float* nred = red + TPW * WAVES * 16;                            // RMSNorm scratch
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * TPW;
+  const int th = min(TPW, a.tiles - t0);
+  int b0, n;
+  weighted_run<WAVES>(th * C, w, b0, n);
+  const int last = n > 0 ? n - 1 : 0;
+  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + ((size_t)t0 * C + min(b0, th * C - 1)) * 64 + lane;
+  u4_t cur[U];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u)
-    cur[u] = (live && u < C) ? __builtin_nontemporal_load(wb + (size_t)u * 64) : (u4_t){0u, 0u, 0u, 0u};
-  stage_x(a.x, a.gamma, a.eps, a.k, kpad, xs, red, NT);
+  for (int u = 0; u < U; ++u) cur[u] = __builtin_nontemporal_load(wb + (size_t)min(u, last) * 64);
+  for (int i = threadIdx.x; i < TPW * WAVES * 16; i += NT) red[i] = 0.f;
+  stage_x(a.x, a.gamma, a.eps, a.k, kpad, xs, nred, NT);
   if (a.xn_out && blockIdx.x == 0) store_xs(xs, a.k, a.xn_out, NT);
-  if (!live) return;
   const uint16_t* xl = xs + 8 * (lane >> 4);
+  int c = n > 0 ? b0 % C : 0, tl = n > 0 ? b0 / C : 0;  // block column and tile of the next block
   float acc = 0.f;
-  for (int base = 0; base < C; base += kUnroll) {
-    u4_t nxt[kUnroll];
+  auto flush = [&]() {  // lanes l, l + 16, l + 32, l + 48 hold row l's column quarters
+    float r = acc + __shfl_xor(acc, 16);
+    r += __shfl_xor(r, 32);
+    if (lane < 16) red[(tl * WAVES + w) * 16 + lane] = r;
+  };
+  for (int base = 0; base < n; base += U) {
+    u4_t nxt[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = base + kUnroll + u;
-      nxt[u] = c < C ? __builtin_nontemporal_load(wb + (size_t)c * 64) : (u4_t){0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < U; ++u) nxt[u] = __builtin_nontemporal_load(wb + (size_t)min(base + U + u, last) * 64);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = base + u;
-      if (c < C) {
+    for (int u = 0; u < U; ++u) {
+      if (base + u < n) {
         const u4_t xv = *reinterpret_cast<const u4_t*>(xl + 32 * c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(as_h2(cur[u][i]), as_h2(xv[i]), acc, false);
+        if (++c == C) {  // the run leaves tile tl
+          flush();
+          acc = 0.f;
+          c = 0;
+          ++tl;
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
   }
-  acc += __shfl_xor(acc, 16);
-  acc += __shfl_xor(acc, 32);
-  const int row = 16 * t + lane;
-  if (lane < 16 && row < a.n) a.y[row] = f2h(acc);
+  if (c != 0) flush();  // the run ends inside tile tl
+  __syncthreads();
+  for (int i = threadIdx.x; i < th * 16; i += NT) {
+    const int t = i / 16, r = i % 16;
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < WAVES; ++k) v += red[(t * WAVES + k) * 16 + r];
+    const int row = 16 * (t0 + t) + r;
+    if (row < a.n) a.y[row] = f2h(v);
+  }
 }
 
 template <int WAVES>
@@ -500,15 +524,31 @@ hipError_t launch_w4_gemv(int epi, const GemvArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// Compute units of the current device (workgroups of one round), cached.
+static int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s) {
-  constexpr int WAVES = 4;
-  const int grid = ceil_div(a.tiles, WAVES);
   if (a.batch == 1) {
+    constexpr int WAVES = 8, U = 8;
+    const int tpw = ceil_div(a.tiles, 2 * device_cus());
     const size_t kpad = round_up((size_t)a.cblocks * 32, kGroup);
-    const size_t lds = kpad * 2 + WAVES * sizeof(float);
-    hipLaunchKernelGGL((f16_gemv_b1_kernel<WAVES>), dim3(grid), dim3(WAVES * 64), lds, s, a);
+    const size_t lds = kpad * 2 + (size_t)(tpw * WAVES * 16 + 16) * 4;
+    if (lds > 64 * 1024) return hipErrorInvalidValue;  // a very large vocabulary or hidden size
+    hipLaunchKernelGGL((f16_gemv_b1_kernel<WAVES, U>), dim3(ceil_div(a.tiles, tpw)), dim3(WAVES * 64), lds, s, a,
+                       tpw);
   } else {
-    hipLaunchKernelGGL((f16_gemm_mfma_kernel<WAVES>), dim3(grid), dim3(WAVES * 64), 0, s, a);
+    constexpr int WAVES = 4;
+    hipLaunchKernelGGL((f16_gemm_mfma_kernel<WAVES>), dim3(ceil_div(a.tiles, WAVES)), dim3(WAVES * 64), 0, s, a);
   }
   return hipGetLastError();
 }

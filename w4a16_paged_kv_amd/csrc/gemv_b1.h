@@ -518,6 +518,21 @@ struct GemvB1 {
 // takes 5/4 of the blocks of the second and both slots finish together
 // (7B gate/up per launch: ten one-tile wavefronts 15.3-16.1 us, eight equal
 // runs 15.8 us, eight 5:4 runs 14.4-15.0 us).
+// Run [b0, b0 + n) of wavefront w < W when B blocks are cut into W
+// contiguous runs weighted 5 for the first SIMD slot (w < 4), 4 after it.
+template <int W>
+__device__ __forceinline__ void weighted_run(int B, int w, int& b0, int& n) {
+  int tot = 0, pre = 0;
+#pragma unroll
+  for (int v = 0; v < W; ++v) {
+    const int wt = v < 4 ? 5 : 4;
+    pre += v < w ? wt : 0;
+    tot += wt;
+  }
+  b0 = (int)((long)B * pre / tot);
+  n = (int)((long)B * (pre + (w < 4 ? 5 : 4)) / tot) - b0;
+}
+
 template <int EPI, int IT>
 struct GemvB1Range {
   static constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SILU;
@@ -528,22 +543,13 @@ struct GemvB1Range {
   u4_t bufA[kUnroll], bufB[kUnroll];
   uint32_t scA[kUnroll], scB[kUnroll];
 
-  // run weight of wavefront v: 5 in the first SIMD slot, 4 after it
-  static __device__ __forceinline__ int weight(int v) { return v < 4 ? 5 : 4; }
-
   __device__ __forceinline__ void assign(const GemvArgs& a, int vb, int tw, int w) {
     const int lane = threadIdx.x & 63;
     const int t0 = vb * tw;
     const int B = min(tw, a.tiles - t0) * a.groups;  // this workgroup's blocks (>= 1)
-    int tot = 0, pre = 0;
-#pragma unroll
-    for (int v = 0; v < W; ++v) {
-      pre += v < w ? weight(v) : 0;
-      tot += weight(v);
-    }
-    const bool live = w >= 0 && w < W;
-    b0 = live ? (int)((long)B * pre / tot) : 0;
-    n = live ? (int)((long)B * (pre + weight(w)) / tot) - b0 : 0;
+    b0 = 0;
+    n = 0;
+    if (w >= 0 && w < W) weighted_run<W>(B, w, b0, n);
     last = n > 0 ? n - 1 : 0;
     g0 = n > 0 ? b0 % a.groups : 0;
     tl0 = n > 0 ? b0 / a.groups : 0;
