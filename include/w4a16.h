@@ -168,9 +168,11 @@ typedef struct w4_config {
 
 /* Device KV cache: fp16 [L][2][P][Hkv][16 * D] -- for layer l, K pages then V
  * pages, each page holding one 4 KiB (for D = 128) slice per KV head
- * [RT-arch]. A K slice is [16 tokens][D]; a V slice is [D][16 tokens]
- * (column-major: four consecutive tokens of one dimension are one operand
- * of the attention's P V product on the matrix cores). */
+ * [RT-arch]. A K slice is [16 tokens][D]. A V slice holds value (token t,
+ * dim d) at element ((d / 32) * 64 + d % 16 + 16 (t / 4)) * 8 + ((d / 16) % 2)
+ * * 4 + t % 4: four consecutive tokens of one dimension are one operand of
+ * the attention's P V product on the matrix cores, and a lane's operands of
+ * two neighbouring 16-dim slices are 16 contiguous bytes. */
 size_t kv_cache_bytes(const w4_config* cfg, int32_t num_pages);
 
 typedef struct w4_layer_weights {
@@ -302,7 +304,7 @@ int  w4_gemv_f16(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, 
  * out[b][h] = fp16(sum_t softmax_t(q[b][h] . K_t / sqrt(D)) V_t) over tokens
  * t in [0, ctx_lens[b]), K_t/V_t read from KV head h / (Hq/Hkv) through the
  * page table. q: device fp16 [batch][Hq][D]; k_pool: device fp16
- * [num_pages][Hkv][16][D]; v_pool: device fp16 [num_pages][Hkv][D][16] (the
+ * [num_pages][Hkv][16][D]; v_pool: device fp16 [num_pages][Hkv][16 * D] (the
  * KV cache's slice layouts); page_tables: device int32 [batch][max_pages];
  * ctx_lens: device int32 [batch]; out: device fp16 [batch][Hq][D].
  * Device-resident indices are clamped like decode_step_device: a page id

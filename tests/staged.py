@@ -11,7 +11,7 @@ import workloads as wl
 from oracle import decode as od
 from oracle import runs
 from tests.gpu_util import assert_close, to_np16
-from workloads.device import DeviceModel, to_dev
+from workloads.device import DeviceModel, to_dev, v_pages_host
 
 
 def buf(dm, which, batch):
@@ -21,11 +21,10 @@ def buf(dm, which, batch):
 
 
 def kv_slot(dm, layer, which, page, slot):
-    """The [Hkv][D] values of one token slot (V slices are [D][16] on the device)."""
+    """The [Hkv][D] values of one token slot (V slices in the device order)."""
     pool = dm.kv_cache[layer, which]
     if which == 1:
-        pool = pool.view(pool.shape[0], pool.shape[1], pool.shape[3], pool.shape[2])
-        return to_np16(pool[page, :, :, slot])
+        return to_np16(v_pages_host(pool[page])[:, slot])
     return to_np16(pool[page, :, slot])
 
 

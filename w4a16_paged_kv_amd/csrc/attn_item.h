@@ -111,7 +111,8 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   const float scale = kLog2e / sqrtf((float)D);
   // P V on the matrix cores too: O^T = V^T P with v_mfma_f32_16x16x16_f16,
   // A = a 16-column slice of V^T (lane l: column 16 s + (l & 15), tokens
-  // 4 (l >> 4) .. +4, contiguous in the column-major V page), B = P, which
+  // 4 (l >> 4) .. +4; the V page keeps them, for slices 2i and 2i + 1, in
+  // 16 contiguous bytes per lane: v_slice_offset), B = P, which
   // the score step already left in B-operand order (lane l holds tokens
   // 4 (l >> 4) + j of head l & 15); lane l accumulates
   // O[head l & 15][16 s + 4 (l >> 4) + j], so each lane rescales only its
@@ -132,15 +133,15 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     return bad ? 0 : id;
   };
   u4_t kf[NK], kn[PF ? NK : 1];
-  u2_t vf[NS], vn[PF ? NS : 1];
-  auto load_kv = [&](int page, u4_t* kk, u2_t* vv) {
+  u4_t vf[NS / 2], vn[PF ? NS / 2 : 1];  // V operands of slice pairs (2i, 2i + 1)
+  auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
     page = __builtin_amdgcn_readfirstlane(page);  // one page per wavefront: keeps the resources scalar
     const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
     const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
 #pragma unroll
     for (int i = 0; i < NK; ++i) kk[i] = ld128_agent(rk, 2 * (qh * D + 32 * i + kc));
 #pragma unroll
-    for (int i = 0; i < NS; ++i) vv[i] = ld64_agent(rv, 2 * ((16 * i + qh) * kPage + tk));
+    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128_agent(rv, 16 * (64 * i + lane));
   };
   int valid_cur = 0, valid_nxt = 0;
   const int p_stop = pager ? p_end : pw0;  // non-page wavefronts skip the loop
@@ -185,17 +186,18 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     // masked tokens contribute nothing even if their slots hold NaN
     if (valid < kPage) {
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        h4_t v4 = __builtin_bit_cast(h4_t, vf[i]);
+      for (int i = 0; i < NS / 2; ++i) {
+        h8_t v8 = __builtin_bit_cast(h8_t, vf[i]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (tk + j >= valid) v4[j] = (_Float16)0.f;
-        vf[i] = __builtin_bit_cast(u2_t, v4);
+        for (int j = 0; j < 8; ++j)
+          if (tk + (j & 3) >= valid) v8[j] = (_Float16)0.f;
+        vf[i] = __builtin_bit_cast(u4_t, v8);
       }
     }
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const h4_t v4 = __builtin_bit_cast(h4_t, vf[i]);
+      const u4_t vp = vf[i >> 1];
+      const h4_t v4 = __builtin_bit_cast(h4_t, (i & 1) ? (u2_t){vp[2], vp[3]} : (u2_t){vp[0], vp[1]});
       acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, ph, acc[i] * al, 0, 0, 0);
       acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, pl, acc[i], 0, 0, 0);
     }
@@ -203,7 +205,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
 #pragma unroll
       for (int i = 0; i < NK; ++i) kf[i] = kn[PF ? i : 0];
 #pragma unroll
-      for (int i = 0; i < NS; ++i) vf[i] = vn[PF ? i : 0];
+      for (int i = 0; i < NS / 2; ++i) vf[i] = vn[PF ? i : 0];
       valid_cur = valid_nxt;
     } else if (p + W < p_stop) {
       load_kv(checked(p + W, pid_nxt, valid_cur), kf, vf);

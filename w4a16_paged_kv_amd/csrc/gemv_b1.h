@@ -103,16 +103,26 @@ __device__ __forceinline__ u2_t ld64_agent(__amdgpu_buffer_rsrc_t r, int byte_of
 
 // ------------------------------------------------------------- epilogues
 
+// Element (token t, dim d) of a (page, head) V slice sits in the operand
+// order of the attention's P V product (v_mfma_f32_16x16x16_f16, A = a
+// 16-dim slice of V^T): lane L = d % 16 + 16 (t / 4) holds tokens t / 4 * 4
+// .. +4 of dim d for two consecutive 16-dim slices, 16 contiguous bytes per
+// lane and slice pair, so one 16-byte load per lane fetches two operands:
+// offset ((d / 32) * 64 + L) * 8 + ((d / 16) % 2) * 4 + t % 4.
+__host__ __device__ __forceinline__ int v_slice_offset(int t, int d) {
+  return ((d >> 5) * 64 + (d & 15) + 16 * (t >> 2)) * 8 + ((d >> 4) & 1) * 4 + (t & 3);
+}
+
 // One token's K or V values (dims dim0, dim1 of KV head kvh) into its page
-// slot. A (page, head) slice of K is [16 tokens][D]; of V it is [D][16
-// tokens] (column-major), the operand layout of the attention's P V product.
+// slot. A (page, head) slice of K is [16 tokens][D]; of V it is in the P V
+// operand order above.
 __device__ __forceinline__ void kv_store(const QkvEpilogue& e, uint16_t* pool, bool v_layout, int slot, int kvh,
                                          int dim0, int dim1, float v0, float v1) {
   if (slot < 0) return;  // invalid position or page: counted by the token plan
   uint16_t* sl = pool + ((size_t)(slot >> 4) * e.n_kv_heads + kvh) * kPage * e.head_dim;
   const int t = slot & 15;
-  st16_agent(sl + (v_layout ? dim0 * kPage + t : t * e.head_dim + dim0), f2h(v0));
-  st16_agent(sl + (v_layout ? dim1 * kPage + t : t * e.head_dim + dim1), f2h(v1));
+  st16_agent(sl + (v_layout ? v_slice_offset(t, dim0) : t * e.head_dim + dim0), f2h(v0));
+  st16_agent(sl + (v_layout ? v_slice_offset(t, dim1) : t * e.head_dim + dim1), f2h(v1));
 }
 
 // Rows i and i+8 of tile t hold the rotate-half RoPE pair (dim0, dim0 + D/2)

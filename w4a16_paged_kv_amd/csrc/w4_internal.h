@@ -53,7 +53,7 @@ struct QkvEpilogue {
   uint16_t* q_out;            // [B][q_stride] fp16, q heads in logical order
   int32_t q_stride;
   uint16_t* k_pool;           // [P][Hkv][16][D]
-  uint16_t* v_pool;           // [P][Hkv][D][16]
+  uint16_t* v_pool;           // [P][Hkv][16 * D], slices in P V operand order (v_slice_offset)
   const uint16_t* bias;       // fp16 [(Hq+2Hkv)D] logical order, or nullptr
   const int32_t* slot;        // token plan: [B] page * 16 + position % 16, or -1 (no K/V store)
   const float* rope;          // token plan: [B][D/2][2] cos, sin of pair i's angle
@@ -117,7 +117,7 @@ struct AttnArgs {
   const uint16_t* q;          // [B][q_stride], heads of D values
   int32_t q_stride;
   const uint16_t* k_pool;     // [P][Hkv][16][D]
-  const uint16_t* v_pool;     // [P][Hkv][D][16]
+  const uint16_t* v_pool;     // [P][Hkv][16 * D], slices in P V operand order (v_slice_offset)
   const int32_t* page_tables; // [B][max_pages]
   const int32_t* ctx_lens;    // [B]
   int32_t batch;

@@ -48,14 +48,30 @@ def upload_layer(w: Workload, l: int, bias: bool = False, device="cuda") -> Dict
 
 
 def v_pages_device(v: np.ndarray) -> np.ndarray:
-    """V pages [P][Hkv][16][D] in the device layout [P][Hkv][D][16] (each
-    (page, head) slice column-major)."""
-    return np.ascontiguousarray(np.swapaxes(v, -1, -2))
+    """V pages [..][16 tokens][D] in the device's slice order, same shape:
+    value (t, d) at flat ((d // 32) * 64 + d % 16 + 16 (t // 4)) * 8 +
+    ((d // 16) % 2) * 4 + t % 4 of its slice (the operand order of the
+    attention's P V product)."""
+    *lead, T, D = v.shape
+    s = v.reshape(*lead, 4, 4, D // 32, 2, 16)          # t = 4q + j, d = 32P + 16e + r
+    n = len(lead)
+    s = s.transpose(*range(n), n + 2, n, n + 4, n + 3, n + 1)  # [P][q][r][e][j]
+    return np.ascontiguousarray(s).reshape(*lead, T, D)
+
+
+def v_pages_host(vd):
+    """Inverse of v_pages_device (numpy arrays or torch tensors)."""
+    *lead, T, D = vd.shape
+    n = len(lead)
+    s = vd.reshape(*lead, D // 32, 4, 16, 2, 4)         # [P][q][r][e][j]
+    order = (*range(n), n + 1, n + 4, n, n + 3, n + 2)  # -> [q][j][P][e][r]
+    s = s.permute(*order) if hasattr(s, "permute") else s.transpose(*order)
+    return s.reshape(*lead, T, D)
 
 
 def upload_kv(w: Workload, kv_cache: torch.Tensor, l: int, kv=None) -> None:
     """Copy layer l's generated K and V pages into the [L][2][P][Hkv][16 x D] cache
-    (K slices [16][D], V slices [D][16])."""
+    (K slices [16][D], V slices in the device order of v_pages_device)."""
     k, v = kv if kv is not None else w.kv(l)
     kv_cache[l, 0].copy_(to_dev(k, kv_cache.device))
     kv_cache[l, 1].copy_(to_dev(v_pages_device(v), kv_cache.device).view(kv_cache[l, 1].shape))
