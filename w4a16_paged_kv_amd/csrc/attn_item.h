@@ -27,17 +27,7 @@
 
 namespace w4 {
 
-__device__ __forceinline__ uint16_t f2h_a(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
-
 constexpr float kLog2e = 1.4426950408889634f;
-
-// Device-scope relaxed accesses: coherent across the XCDs' L2 caches.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time each
 
@@ -221,30 +211,41 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     for (int i = 0; i < NS; ++i) *reinterpret_cast<f4_t*>(&s_o[wave][qh][16 * i + tk]) = acc[i];
   __syncthreads();
 
-  // combine the wavefronts: this split's (o, m, l), or the output if one split
-  float* part = a.partials + (((size_t)b * a.n_kv_heads + kvh) * a.max_splits + split) * GQ * (D + 2);
-  for (int idx = threadIdx.x; idx < GQ * D; idx += NT) {
-    const int h = idx / D, d = idx % D;
+  // combine the wavefronts: this split's (o, m, l), or the output if one
+  // split. Thread g < GQ D / 4 takes four consecutive dims of one head and
+  // stores them with one 16-byte (partial) or 8-byte (output) store.
+  constexpr int PS = D + 4;      // floats per (split, head) partial: o[D], m, l, 2 unused (16-byte rows)
+  constexpr int NG = GQ * D / 4;  // four-dim groups of the item's output
+  float* part = a.partials + (((size_t)b * a.n_kv_heads + kvh) * a.max_splits + split) * GQ * PS;
+  const __amdgpu_buffer_rsrc_t rpart = coherent_rsrc(part);
+  const __amdgpu_buffer_rsrc_t rout = coherent_rsrc(out);
+  for (int g = threadIdx.x; g < NG; g += NT) {
+    const int h = g / (D / 4), d0 = 4 * (g % (D / 4));
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
+    f4_t O = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < W; ++w) {
         const float f = exp2f(s_m[w][h] - M);
         L += f * s_l[w][h];
-        O += f * s_o[w][h][d];
+        const f4_t o = *reinterpret_cast<const f4_t*>(&s_o[w][h][d0]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) O[j] = fmaf(f, o[j], O[j]);
       }
     }
     if (nsplit == 1) {
-      st16_agent(out + h * D + d, f2h_a(L > 0.f ? O / L : 0.f));
+      h4_t r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = (_Float16)(L > 0.f ? O[j] / L : 0.f);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, r), rout, 2 * (h * D + d0), 0, kPolicySc1);
     } else {
-      st_agent(&part[h * (D + 2) + d], O);
-      if (d == 0) {
-        st_agent(&part[h * (D + 2) + D], M);
-        st_agent(&part[h * (D + 2) + D + 1], L);
-      }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, O), rpart, 4 * (h * PS + d0), 0, kPolicySc1);
+      if (d0 == 0)
+        __builtin_amdgcn_raw_buffer_store_b64((u2_t){(uint32_t)f_bits(M), (uint32_t)f_bits(L)}, rpart,
+                                              4 * (h * PS + D), 0, kPolicySc1);
     }
   }
   if (nsplit == 1) return;
@@ -260,34 +261,41 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
              (uint32_t)(nsplit - 1);
   __syncthreads();
   if (!s_last) return;
-  // One pass: wavefront h loads (m, l) of head h for every split while each
-  // thread's first sixteen partial outputs are already in flight; the
-  // wavefront reduces them on the VALU and leaves the merge weights
-  // w[h][s] = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s' in LDS.
-  const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * (D + 2);
-  float* s_w = &s_o[0][0][0];  // reuse: [GQ][nsplit] (nsplit <= 128)
+  // One pass: wavefront h < GQ loads (m, l) of head h for every split while
+  // every thread's first kU partial outputs (16 bytes each) are in flight;
+  // TPG threads share a four-dim group, thread part p taking the splits
+  // p, p + TPG, ...; the wavefront h reduces (m, l) on the VALU and leaves
+  // the merge weights w[h][s] = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s' in
+  // LDS, the parts are summed in order through LDS.
+  constexpr int kPool = kAttnWaves * 64;  // threads the split of the work is sized for (any NT >= it)
+  constexpr int TPG = NG * 4 <= kPool ? 4 : NG * 2 <= kPool ? 2 : 1;
+  constexpr int kU = 8;
+  static_assert(GQ * 128 + (TPG - 1) * NG * 4 <= W * GQ * D, "merge scratch fits s_o");
+  const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * PS;
+  const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(pb);
+  float* s_w = &s_o[0][0][0];                                  // reuse: [GQ][nsplit] (nsplit <= 128)
+  f4_t* s_x = reinterpret_cast<f4_t*>(&s_o[0][0][0] + GQ * 128);  // [TPG - 1][NG]
   float mm[2] = {-INFINITY, -INFINITY}, ll[2] = {0.f, 0.f};
   if (wave < GQ) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int sp = lane + 64 * r;
       if (sp < nsplit) {
-        mm[r] = ld_agent(&pb[((size_t)sp * GQ + wave) * (D + 2) + D]);
-        ll[r] = ld_agent(&pb[((size_t)sp * GQ + wave) * (D + 2) + D + 1]);
+        const u2_t ml = ld64_agent(rp, 4 * ((sp * GQ + wave) * PS + D));
+        mm[r] = bits_f((int)ml[0]);
+        ll[r] = bits_f((int)ml[1]);
       }
     }
   }
-  constexpr int kFirst = 16;
-  constexpr int kItems = (GQ * D + NT - 1) / NT;
-  float v0[kItems][kFirst];
+  const bool worker = (int)threadIdx.x < NG * TPG;
+  const int gi = worker ? (int)threadIdx.x % NG : 0, pi = worker ? (int)threadIdx.x / NG : 0;
+  const int mh = gi / (D / 4), md0 = 4 * (gi % (D / 4));
+  auto ldo = [&](int sp) {  // split sp's four dims of the group (clamped: loads stay in the item)
+    return __builtin_bit_cast(f4_t, ld128_agent(rp, 4 * ((min(sp, nsplit - 1) * GQ + mh) * PS + md0)));
+  };
+  f4_t v0[kU];
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
-    const int idx = min((int)threadIdx.x + r * NT, GQ * D - 1);
-    const float* ps = pb + (size_t)(idx / D) * (D + 2) + idx % D;
-#pragma unroll
-    for (int u = 0; u < kFirst; ++u)
-      v0[r][u] = ld_agent(ps + (size_t)min(u, nsplit - 1) * GQ * (D + 2));
-  }
+  for (int u = 0; u < kU; ++u) v0[u] = ldo(pi + TPG * u);
   if (wave < GQ) {
     float M = fmaxf(mm[0], mm[1]);
     M = fmaxf(M, ror4(M));
@@ -311,27 +319,43 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     }
   }
   __syncthreads();
+  f4_t O = {0.f, 0.f, 0.f, 0.f};
+  if (worker) {
+    const float* wh = s_w + mh * nsplit;
 #pragma unroll
-  for (int r = 0; r < kItems; ++r) {
-    const int idx = threadIdx.x + r * NT;
-    if (idx >= GQ * D) break;
-    const int h = idx / D, d = idx % D;
-    const float* wh = s_w + h * nsplit;
-    float O = 0.f;
+    for (int u = 0; u < kU; ++u) {
+      const int sp = pi + TPG * u;
+      if (sp < nsplit)
 #pragma unroll
-    for (int u = 0; u < kFirst; ++u)
-      if (u < nsplit) O = fmaf(wh[u], v0[r][u], O);
-    const float* ps = pb + (size_t)h * (D + 2) + d;
-    // splits past the first sixteen: eight loads in flight, then their sums (in order)
-    for (int sp0 = kFirst; sp0 < nsplit; sp0 += 8) {
-      float t8[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) t8[u] = ld_agent(ps + (size_t)min(sp0 + u, nsplit - 1) * GQ * (D + 2));
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (sp0 + u < nsplit) O = fmaf(wh[sp0 + u], t8[u], O);
+        for (int j = 0; j < 4; ++j) O[j] = fmaf(wh[sp], v0[u][j], O[j]);
     }
-    st16_agent(out + h * D + d, f2h_a(O));
+    // splits past the first TPG kU: kU loads in flight, then their sums (in order)
+    for (int sp0 = TPG * kU; sp0 < nsplit; sp0 += TPG * kU) {
+      f4_t t8[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) t8[u] = ldo(sp0 + pi + TPG * u);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int sp = sp0 + pi + TPG * u;
+        if (sp < nsplit)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) O[j] = fmaf(wh[sp], t8[u][j], O[j]);
+      }
+    }
+    if (pi > 0) s_x[(pi - 1) * NG + gi] = O;
+  }
+  __syncthreads();
+  if (worker && pi == 0) {
+#pragma unroll
+    for (int p = 1; p < TPG; ++p) {
+      const f4_t x = s_x[(p - 1) * NG + gi];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) O[j] += x[j];
+    }
+    h4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = (_Float16)O[j];
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, r), rout, 2 * (mh * D + md0), 0, kPolicySc1);
   }
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -124,7 +124,7 @@ struct AttnArgs {
   int32_t max_pages, num_pages;
   int32_t n_heads, n_kv_heads;
   int32_t pages_per_split, max_splits;
-  float* partials;            // [B][Hkv][max_splits][GQ][D + 2]
+  float* partials;            // [B][Hkv][max_splits][GQ][D + 4]: o[D], m, l, 2 unused
   uint32_t* counters;         // [B][Hkv], zero between launches
   uint16_t* out;              // [B][out_stride]
   int32_t out_stride;
@@ -172,7 +172,7 @@ bool attention_supported(int head_dim, int group);
 int attention_pages_per_split(int batch, int n_kv_heads, int max_pages);
 inline size_t attention_partial_floats(int batch, int n_kv_heads, int max_splits, int group,
                                        int head_dim) {
-  return (size_t)batch * n_kv_heads * max_splits * group * (head_dim + 2);
+  return (size_t)batch * n_kv_heads * max_splits * group * (head_dim + 4);  // o[D], m, l, 2 unused
 }
 
 }  // namespace w4
