@@ -72,13 +72,13 @@ __device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* ds
 }
 
 // ------------------------------------------------------------ batch 1
-// One launch per projection: S wavefronts per tile on TW tiles (S TW <= 16;
-// any further wavefronts only help stage the activations), IT activation
-// words per thread: the same decomposition and arithmetic as the projection
-// phases of the persistent layer kernel. The
-// activation loads go out first, then the first weight batch, so the
-// prologue waits for the activations only (the vector-memory counter is in
-// order).
+// One launch per projection: S wavefronts per tile on TW tiles (S TW <= 8),
+// or kRangeWaves contiguous runs when S == 1; any further wavefronts only
+// help stage the activations. IT activation words per thread: the same
+// decomposition and arithmetic as the projection phases of the persistent
+// layer kernel. The activation loads go out first, then the first weight
+// batch, so the prologue waits for the activations only (the vector-memory
+// counter is in order).
 template <int EPI, int S, int IT>
 __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
   using Part = GemvB1Sel<EPI, S, IT>;
@@ -89,6 +89,12 @@ __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   StageRegs<IT, NORM> st;
   stage_load(st, a.x, a.gamma, a.k, NT);
+  // every wavefront's activation loads reach the CU's memory pipeline before
+  // any weight prefetch (down projection 9.2 -> 8.6 us): the barrier waits
+  // for no load
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   const QkvPre pre = qkv_pre<EPI>(a, blockIdx.x, TW);
   Part g;
   g.assign(a, blockIdx.x, TW, wave);
