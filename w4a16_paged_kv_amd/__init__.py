@@ -256,12 +256,13 @@ class Model:
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      max_batch, max_pages, ctypes.byref(h)))
         self.handle = h.value
+        self._destroy = lib().w4_model_destroy  # held: module globals may be gone when __del__ runs at exit
         self.kv_cache, self.workspace = kv_cache, workspace
         self.num_pages, self.max_batch, self.max_pages = num_pages, max_batch, max_pages
 
     def close(self):
         if getattr(self, "handle", None):
-            lib().w4_model_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
     __del__ = close
