@@ -110,16 +110,26 @@ __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
 // ------------------------------------------------------- batch 2..16, MFMA
 // The batch-1 decomposition with all 16 A rows real: the activation rows
 // (RMSNorm applied while staging when gamma is given; rows >= batch zero)
-// are staged in LDS in the MFMA k-slot
-// order, a window of GW groups at a time (one window up to K = 4096, 128 KiB
-// of LDS at most; rows padded by 16 bytes so the 16 lanes of a lane group,
-// one row each, read distinct banks), and the same packed blocks, exact dequantisation and
+// are staged in LDS in the MFMA k-slot order, a window of GW groups at a
+// time (one window up to K = 4096, 128 KiB of LDS at most; rows padded by 16
+// bytes so the 16 lanes of a lane group, one row each, read distinct banks),
+// and the same packed blocks, exact dequantisation and
 // v_mfma_f32_16x16x32_f16 give D[batch row][weight row] in every lane. TW
 // tiles per workgroup, S wavefronts per tile; each wavefront streams its
-// window's blocks two batches of four ahead, the first batch issued before
-// the window is staged.
+// window's blocks two batches of four ahead.
+//
+// Staging: thread t holds 8-column word t of the window in every one of the
+// 16 rows (NT >= 16 GW), so each thread issues its 16 activation loads (and
+// one RMSNorm-weight load) at once, before the window's first weight batch.
+// When the whole row is one window the RMSNorm sums come from those same
+// registers (per-thread partial sums of each row, reduced on the VALU per
+// wavefront and in wavefront order through LDS); longer rows with RMSNorm
+// take a pre-pass over the rows instead. Reading the rows twice (sums, then
+// staging) and the RMSNorm weights once per row took gate/up from 12.4 us of
+// prologue to ~3 us.
+constexpr int kRowsThreads = 768;  // launch bound: 16 activation words per thread stay in registers
 template <int EPI, int S>
-__global__ __launch_bounds__(1024) void w4_gemm_rows_kernel(GemvArgs a, int TW, int GW) {
+__global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, int TW, int GW) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int NT = blockDim.x, NW = NT >> 6;
   const int lane = threadIdx.x & 63;
@@ -137,11 +147,12 @@ __global__ __launch_bounds__(1024) void w4_gemm_rows_kernel(GemvArgs a, int TW, 
   const uint16_t* xl = xs + (size_t)(lane & 15) * KW + 32 * (lane >> 4);
   const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
   const int e = threadIdx.x & 1;
-  const int wpr = GW * 16;  // 8-column words per staged row
-  // RMSNorm of the rows (with gamma): wavefront w sums the squares of rows
-  // w, w + NW, ..; the rows are scaled while they are staged
+  const bool one_window = G <= GW;
   __shared__ float s_rs[16];
-  if (a.gamma) {
+  __shared__ float s_ss[kRowsThreads / 64][16];
+  // RMSNorm over rows longer than one window: wavefront w sums the squares
+  // of rows w, w + NW, .. in a pre-pass
+  if (a.gamma && !one_window) {
     const int kw = a.k / 8;
     for (int m = wave; m < 16; m += NW) {
       float ss = 0.f;
@@ -189,43 +200,68 @@ __global__ __launch_bounds__(1024) void w4_gemm_rows_kernel(GemvArgs a, int TW, 
           acc += d * h2f((uint16_t)sc[u]);
         }
     };
-    load(bufA, scA, 0);
-    __syncthreads();  // the previous window's reads of xs are done
-    // stage the window: word wd = row * wpr + cw holds columns 128 g0 + 8 cw ..
-    // of activation row `row` (zero past k, past the window and for rows >= batch)
-    const int words = 16 * wpr;
-    for (int w0 = 0; w0 < words; w0 += 8 * NT) {  // every lane runs every round (quad permutes)
-      u4_t xv[8];
+    // word cw of every row: columns 128 g0 + 8 cw .. +8 (zero past k, past the
+    // window and for rows >= batch); unconditional loads from clamped addresses
+    const int cw = threadIdx.x;
+    const int col = 128 * g0 + 8 * cw;
+    const bool cin = cw < 16 * gn && col < a.k;
+    const int colc = min(col, a.k - 8);
+    u4_t xv[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int wd = w0 + (int)threadIdx.x + j * NT;
-        const int row = wd / wpr, cw = wd % wpr;
-        const int col = 128 * g0 + 8 * cw;
-        const bool in = wd < words && row < a.batch && cw < 16 * gn && col < a.k;
-        const u4_t v = *reinterpret_cast<const u4_t*>(a.x + (size_t)min(row, a.batch - 1) * a.x_stride +
-                                                      min(col, a.k - 8));
-        xv[j] = in ? v : (u4_t){0u, 0u, 0u, 0u};
-        if (a.gamma) {  // fp16(x * rs * gamma), the batch-1 staging's rounding
-          const u4_t gv = *reinterpret_cast<const u4_t*>(a.gamma + min(col, a.k - 8));
-          const float rs = s_rs[min(row, 15)];
+    for (int m = 0; m < 16; ++m)
+      xv[m] = *reinterpret_cast<const u4_t*>(a.x + (size_t)min(m, a.batch - 1) * a.x_stride + colc);
+    const u4_t gv = a.gamma ? *reinterpret_cast<const u4_t*>(a.gamma + colc) : (u4_t){0u, 0u, 0u, 0u};
+    __builtin_amdgcn_sched_barrier(0);
+    load(bufA, scA, 0);  // the window's first weight batch, behind the activation loads
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const h2_t hv = as_h2(xv[j][c]), hg = as_h2(gv[c]);
-            h2_t r;
-            r[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
-            r[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
-            xv[j][c] = __builtin_bit_cast(uint32_t, r);
-          }
-          if (a.xn_out && blockIdx.x == 0 && in)
-            *reinterpret_cast<u4_t*>(a.xn_out + (size_t)row * a.xn_stride + col) = xv[j];
+    for (int m = 0; m < 16; ++m)
+      if (!(cin && m < a.batch)) xv[m] = (u4_t){0u, 0u, 0u, 0u};
+    if (a.gamma && one_window) {  // this thread's share of each row's sum of squares, in order
+      float ss[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        ss[m] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const h2_t h = as_h2(xv[m][c]);
+          ss[m] = fmaf((float)h[0], (float)h[0], ss[m]);
+          ss[m] = fmaf((float)h[1], (float)h[1], ss[m]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int wd = w0 + (int)threadIdx.x + j * NT;
-        const u4_t o = slot_word(xv[j], e);
-        if (wd < words) *reinterpret_cast<u4_t*>(xs + (size_t)(wd / wpr) * KW + 8 * (wd % wpr)) = o;
+      for (int m = 0; m < 16; ++m) {
+        const float v = wave_sum(ss[m]);
+        if (lane == 0) s_ss[wave][m] = v;
       }
+      __syncthreads();
+      if (threadIdx.x < 16) {
+        float tot = 0.f;
+        for (int w = 0; w < NW; ++w) tot += s_ss[w][threadIdx.x];
+        s_rs[threadIdx.x] = 1.0f / sqrtf(tot / (float)a.k + a.eps);
+      }
+    }
+    __syncthreads();  // s_rs ready; the previous window's reads of xs are done
+    if (a.gamma) {  // fp16(x * rs * gamma), the batch-1 staging's rounding
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const float rs = s_rs[m];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const h2_t hv = as_h2(xv[m][c]), hg = as_h2(gv[c]);
+          h2_t r;
+          r[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
+          r[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
+          xv[m][c] = __builtin_bit_cast(uint32_t, r);
+        }
+        if (a.xn_out && blockIdx.x == 0 && cin && m < a.batch)
+          *reinterpret_cast<u4_t*>(a.xn_out + (size_t)m * a.xn_stride + col) = xv[m];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const u4_t o = slot_word(xv[m], e);  // every lane: quad permutes
+      if (cw < 16 * GW) *reinterpret_cast<u4_t*>(xs + (size_t)m * KW + 8 * cw) = o;
     }
     __syncthreads();
     for (int i = 0; i < ng; i += 2 * kUnroll) {
@@ -504,8 +540,9 @@ static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
   } else {
     if (a.batch > 16) return hipErrorInvalidValue;
     const B1Split sp = w4_b1_split(a.tiles, a.groups);
-    const int nt = std::max(256, 64 * sp.s * sp.tw);
     const int gw = std::min(a.groups, 32);  // activation window: at most 4096 columns (128 KiB of LDS)
+    const int nt = std::max({256, 64 * sp.s * sp.tw, (int)round_up(16 * gw, 64)});  // a thread per window word
+    if (nt > kRowsThreads) return hipErrorInvalidValue;
     const size_t lds = (size_t)16 * (gw * kGroup + 8) * 2 + ((size_t)(nt / 64) * 256 + (size_t)sp.tw * 256) * 4;
     hipError_t e = hipSuccess;
     switch (sp.s) {
