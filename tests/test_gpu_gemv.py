@@ -13,7 +13,11 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [  # (n, k): miniature and Qwen2.5-7B projection shapes, incl. a partial group (k = 448)
     (576, 448), (448, 448), (3072, 448), (448, 1536),
-    (4608, 3584), (3584, 3584), (37888, 3584), (3584, 18944), (40, 200)]
+    (4608, 3584), (3584, 3584), (37888, 3584), (3584, 18944), (40, 200),
+    # many tiles per workgroup with few groups: batch-1 runs of one or two
+    # blocks crossing tiles (6 and 16 tiles per workgroup), and batch > 1
+    # shapes past one workgroup per CU
+    (24000, 256), (65536, 128)]
 
 
 @pytest.mark.parametrize("n,k", SHAPES)

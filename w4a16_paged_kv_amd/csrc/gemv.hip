@@ -539,10 +539,10 @@ static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   } else {
     if (a.batch > 16) return hipErrorInvalidValue;
-    const B1Split sp = w4_b1_split(a.tiles, a.groups);
+    B1Split sp = w4_b1_split(a.tiles, a.groups);
+    sp.tw = std::min(sp.tw, kRowsThreads / (64 * sp.s));  // many tiles: more than one workgroup per CU
     const int gw = std::min(a.groups, 32);  // activation window: at most 4096 columns (128 KiB of LDS)
     const int nt = std::max({256, 64 * sp.s * sp.tw, (int)round_up(16 * gw, 64)});  // a thread per window word
-    if (nt > kRowsThreads) return hipErrorInvalidValue;
     const size_t lds = (size_t)16 * (gw * kGroup + 8) * 2 + ((size_t)(nt / 64) * 256 + (size_t)sp.tw * 256) * 4;
     hipError_t e = hipSuccess;
     switch (sp.s) {
