@@ -10,9 +10,13 @@ namespace w4 {
 // At most 128 VGPRs, so two workgroups share a CU (four wavefronts per
 // SIMD): the many-sequence workloads need that memory parallelism (32
 // sequences, contexts up to 8192: 120 -> 85 us with the bound).
+// The grid is (sequence, KV head, split) with the split slowest, so the
+// dispatcher sends every sequence's first splits before any later ones and
+// the items past a short sequence's last split (which exit at once) come at
+// the end (32 sequences, contexts 128-8192: 78 -> 75 us).
 template <int D, int GQ>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void paged_attn_kernel(AttnArgs a) {
-  attn_item<D, GQ, kAttnWaves * 64>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  attn_item<D, GQ, kAttnWaves * 64>(a, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 bool attention_supported(int head_dim, int group) {
@@ -37,7 +41,7 @@ int attention_pages_per_split(int batch, int n_kv_heads, int max_pages) {
 
 template <int D, int GQ>
 static hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((paged_attn_kernel<D, GQ>), dim3(a.max_splits, a.n_kv_heads, a.batch),
+  hipLaunchKernelGGL((paged_attn_kernel<D, GQ>), dim3(a.batch, a.n_kv_heads, a.max_splits),
                      dim3(kAttnWaves * 64), 0, s, a);
   return hipGetLastError();
 }
