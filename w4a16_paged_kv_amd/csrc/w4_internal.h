@@ -168,7 +168,7 @@ hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_
 bool attention_supported(int head_dim, int group);
 
 // Pages per attention split for a batch / context size: enough workgroups to
-// cover the chip, each split at least 4 pages (one per wavefront).
+// cover the chip, each split at least one page per wavefront (eight pages).
 int attention_pages_per_split(int batch, int n_kv_heads, int max_pages);
 inline size_t attention_partial_floats(int batch, int n_kv_heads, int max_splits, int group,
                                        int head_dim) {
