@@ -102,3 +102,13 @@ def test_layer_mini_batches_and_ragged(ctx):
 def test_layer_full_shape_batch16():
     ctx = wl.rng(22, 0, wl.CTX).integers(1, 700, 16)
     staged(wl.custom("full_b16", 22, wl.QWEN7B, ctx))
+
+
+@pytest.mark.parametrize("ffn,ctx", [(4480, [40, 3, 129, 77, 16]), (12160, [5, 300, 64])])
+def test_layer_long_ffn_split_k(ffn, ctx):
+    """Batch > 1 with the down projection's rows longer than one activation
+    window (35 and 95 groups): K split over 2 and 3 workgroups per tile group
+    (uneven chunks) and the last arrival's sum. The Qwen2.5-7B batch-16 tests
+    cover five chunks and a partial last tile group."""
+    sh = wl.Shape(hidden=448, n_heads=7, n_kv_heads=1, head_dim=64, ffn=ffn, vocab=64, n_layers=1)
+    staged(wl.custom(f"ffn{ffn}", 24, sh, ctx, gamma="random"))

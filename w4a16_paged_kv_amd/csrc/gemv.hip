@@ -129,7 +129,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
 // prologue to ~3 us.
 constexpr int kRowsThreads = 768;  // launch bound: 16 activation words per thread stay in registers
 template <int EPI, int S>
-__global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, int TW, int GW) {
+__global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, int TW, int GW, int CH) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int NT = blockDim.x, NW = NT >> 6;
   const int lane = threadIdx.x & 63;
@@ -139,7 +139,9 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                        // [16][KW]
   float* red = reinterpret_cast<float*>(smem + (size_t)16 * KW * 2);       // [NW][16][16]
   float* vals = red + NW * 256;                                            // [TW][16][16]
-  const int t = blockIdx.x * TW + wave / S, ks = wave % S;
+  const int tg = blockIdx.x / CH, kc = blockIdx.x % CH;  // tile group, K chunk (chunks of a group adjacent)
+  const int t = tg * TW + wave / S, ks = wave % S;
+  const int k1 = CH > 1 ? min(G, (kc + 1) * GW) : G;       // groups [kc GW, k1)
   const bool live = wave < S * TW && t < a.tiles;
   const size_t base = (size_t)(live ? t : 0) * G;
   const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + base * 64 + lane;
@@ -178,8 +180,8 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
     __syncthreads();
   }
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int g0 = 0; g0 < G; g0 += GW) {
-    const int gn = min(GW, G - g0);
+  for (int g0 = kc * GW; g0 < k1; g0 += GW) {
+    const int gn = min(GW, k1 - g0);
     const int ng = (live && ks < gn) ? (gn - ks + S - 1) / S : 0;  // groups g0 + ks + S i, i < ng
     const int last = ng > 0 ? ng - 1 : 0;
     u4_t bufA[kUnroll], bufB[kUnroll];
@@ -285,11 +287,37 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
     vals[idx] = v;
   }
   __syncthreads();
+  if (CH > 1) {
+    // K split: store this chunk's sums, count the tile group's arrivals; the
+    // last workgroup adds the CH chunks in order and runs the epilogue.
+    // Partial sums move between workgroups (and XCDs) through device-coherent
+    // 16-byte stores and loads; each workgroup's stores complete before it
+    // counts itself.
+    const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.kpart + (size_t)tg * CH * TW * 256);
+    for (int q = threadIdx.x; q < TW * 64; q += NT)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, *reinterpret_cast<const f4_t*>(vals + 4 * q)),
+                                             rp, 16 * (kc * TW * 64 + q), 0, kPolicySc1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ int s_last_k;
+    if (threadIdx.x == 0)
+      s_last_k = __hip_atomic_fetch_add(a.kcount + tg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(CH - 1);
+    __syncthreads();
+    if (!s_last_k) return;
+    for (int q = threadIdx.x; q < TW * 64; q += NT) {
+      f4_t v = {0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < CH; ++c) v += __builtin_bit_cast(f4_t, ld128_agent(rp, 16 * (c * TW * 64 + q)));
+      *reinterpret_cast<f4_t*>(vals + 4 * q) = v;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.kcount + tg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
   constexpr int per = epi_items<EPI>();
   for (int item = threadIdx.x; item < TW * a.batch * per; item += NT) {
     const int tl = item / (a.batch * per), r = item % (a.batch * per);
     const int m = r / per, i = r % per;
-    const int tt = blockIdx.x * TW + tl;
+    const int tt = tg * TW + tl;
     if (tt < a.tiles) epilogue<EPI>(a, m, tt, i, vals + (tl * 16 + m) * 16);
   }
 }
@@ -514,13 +542,38 @@ static hipError_t launch_b1_it(const GemvArgs& a, const B1Split& sp, hipStream_t
 // limit covers the kernel's static LDS too: 160 KiB per workgroup in all).
 constexpr int kRowsMaxDynLds = 160 * 1024 - 1024;
 template <int EPI, int S>
-static hipError_t launch_rows(const GemvArgs& a, int tw, int gw, int nt, size_t lds, hipStream_t s) {
+static hipError_t launch_rows(const GemvArgs& a, const RowsPlan& p, int nt, size_t lds, hipStream_t s) {
   if (lds > (size_t)kRowsMaxDynLds) return hipErrorInvalidValue;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemm_rows_kernel<EPI, S>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kRowsMaxDynLds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((w4_gemm_rows_kernel<EPI, S>), dim3(ceil_div(a.tiles, tw)), dim3(nt), lds, s, a, tw, gw);
+  hipLaunchKernelGGL((w4_gemm_rows_kernel<EPI, S>), dim3(ceil_div(a.tiles, p.tw) * p.ch), dim3(nt), lds, s, a, p.tw,
+                     p.gw, p.ch);
   return hipGetLastError();
+}
+
+// Rows longer than one window (more than 32 groups) with split-K buffers:
+// CH = ceil(groups / 32) workgroups per tile group, each one window of
+// consecutive groups, and TW tiles per workgroup so that about one round of
+// workgroups covers the chip; every workgroup then stages a CH-th of the
+// activation rows instead of all of them (down projection, batch 16: 606 KiB
+// of activations per workgroup for 148 KiB of weights before the split).
+RowsPlan w4_rows_plan(int tiles, int groups, bool split_k) {
+  if (!split_k || groups <= 32) {
+    const B1Split sp = w4_b1_split(tiles, groups);
+    // many tiles: more than one workgroup per CU
+    return {sp.s, std::min(sp.tw, kRowsThreads / (64 * sp.s)), std::min(groups, 32), 1};
+  }
+  const int ch = ceil_div(groups, 32);
+  const int gw = ceil_div(groups, ch);
+  const int tw = std::max(1, std::min(kRowsThreads / 64, ceil_div(tiles * ch, 256)));
+  int s = 1;
+  for (int c : {8, 4, 2})
+    if (gw >= 2 * c && 64 * c * tw <= kRowsThreads) {
+      s = c;
+      break;
+    }
+  return {s, tw, gw, ch};
 }
 
 template <int EPI>
@@ -539,17 +592,18 @@ static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   } else {
     if (a.batch > 16) return hipErrorInvalidValue;
-    B1Split sp = w4_b1_split(a.tiles, a.groups);
-    sp.tw = std::min(sp.tw, kRowsThreads / (64 * sp.s));  // many tiles: more than one workgroup per CU
-    const int gw = std::min(a.groups, 32);  // activation window: at most 4096 columns (128 KiB of LDS)
-    const int nt = std::max({256, 64 * sp.s * sp.tw, (int)round_up(16 * gw, 64)});  // a thread per window word
-    const size_t lds = (size_t)16 * (gw * kGroup + 8) * 2 + ((size_t)(nt / 64) * 256 + (size_t)sp.tw * 256) * 4;
+    // the split-K path needs its buffers, and RMSNorm needs whole rows
+    if ((a.kpart == nullptr) != (a.kcount == nullptr)) return hipErrorInvalidValue;
+    const RowsPlan p = w4_rows_plan(a.tiles, a.groups, a.kpart != nullptr && a.gamma == nullptr);
+    // activation window: at most 4096 columns (128 KiB of LDS); a thread per window word
+    const int nt = std::max({256, 64 * p.s * p.tw, (int)round_up(16 * p.gw, 64)});
+    const size_t lds = (size_t)16 * (p.gw * kGroup + 8) * 2 + ((size_t)(nt / 64) * 256 + (size_t)p.tw * 256) * 4;
     hipError_t e = hipSuccess;
-    switch (sp.s) {
-      case 8: e = launch_rows<EPI, 8>(a, sp.tw, gw, nt, lds, s); break;
-      case 4: e = launch_rows<EPI, 4>(a, sp.tw, gw, nt, lds, s); break;
-      case 2: e = launch_rows<EPI, 2>(a, sp.tw, gw, nt, lds, s); break;
-      case 1: e = launch_rows<EPI, 1>(a, sp.tw, gw, nt, lds, s); break;
+    switch (p.s) {
+      case 8: e = launch_rows<EPI, 8>(a, p, nt, lds, s); break;
+      case 4: e = launch_rows<EPI, 4>(a, p, nt, lds, s); break;
+      case 2: e = launch_rows<EPI, 2>(a, p, nt, lds, s); break;
+      case 1: e = launch_rows<EPI, 1>(a, p, nt, lds, s); break;
       default: e = hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -21,7 +21,7 @@
 namespace w4 {
 
 struct WsLayout {
-  size_t err, counters, bar, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, total;
+  size_t err, counters, bar, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, kpart, kcount, total;
   int xn_stride, o_stride, h_stride, max_splits;
 };
 
@@ -54,6 +54,17 @@ static WsLayout ws_layout(const w4_config& c, int max_batch, int max_pages) {
   L.h = take((size_t)max_batch * L.h_stride * 2);
   L.partials = take(attention_partial_floats(max_batch, c.n_kv_heads, L.max_splits, group,
                                              c.head_dim) * 4);
+  // batch > 1: K split of the o and down projections when their rows are
+  // longer than one activation window (partial sums and arrival counters)
+  size_t kp = 0, kw = 0;
+  if (max_batch > 1)
+    for (int k : {c.n_heads * c.head_dim, c.ffn}) {
+      const RowsPlan p = w4_rows_plan(w4_tiles(c.hidden), w4_groups(k), true);
+      kp = std::max(kp, w4_rows_kpart_floats(p, w4_tiles(c.hidden)));
+      kw = std::max(kw, w4_rows_kcount_words(p, w4_tiles(c.hidden)));
+    }
+  L.kpart = kp ? take(kp * 4) : 0;
+  L.kcount = kw ? take(kw * 4) : 0;
   L.total = off;
   return L;
 }
@@ -192,10 +203,20 @@ static AttnArgs attn_args(w4_model* m, int l, const StepInputs& in, int batch) {
   return at;
 }
 
+// batch > 1: the K-split buffers, if the workspace has them
+static void with_ksplit(w4_model* m, GemvArgs& a) {
+  if (a.batch > 1 && m->L.kcount) {
+    a.kpart = m->at<float>(m->L.kpart);
+    a.kcount = m->at<uint32_t>(m->L.kcount);
+  }
+}
+
 static GemvArgs oproj_args(w4_model* m, int l, const uint16_t* x_in, uint16_t* x_out, int batch) {
   const w4_config& c = m->cfg;
-  return gemv_args(m->layers[l].o, c.hidden, c.n_heads * c.head_dim, m->at<uint16_t>(m->L.o), m->L.o_stride,
-                   nullptr, 0.f, x_out, c.hidden, x_in, batch);
+  GemvArgs a = gemv_args(m->layers[l].o, c.hidden, c.n_heads * c.head_dim, m->at<uint16_t>(m->L.o),
+                         m->L.o_stride, nullptr, 0.f, x_out, c.hidden, x_in, batch);
+  with_ksplit(m, a);
+  return a;
 }
 
 static GemvArgs gate_up_args(w4_model* m, int l, const uint16_t* x, int batch) {
@@ -213,8 +234,10 @@ static GemvArgs gate_up_args(w4_model* m, int l, const uint16_t* x, int batch) {
 
 static GemvArgs down_args(w4_model* m, int l, uint16_t* x, int batch) {
   const w4_config& c = m->cfg;
-  return gemv_args(m->layers[l].down, c.hidden, c.ffn, m->at<uint16_t>(m->L.h), m->L.h_stride, nullptr, 0.f, x,
-                   c.hidden, x, batch);
+  GemvArgs a = gemv_args(m->layers[l].down, c.hidden, c.ffn, m->at<uint16_t>(m->L.h), m->L.h_stride, nullptr,
+                         0.f, x, c.hidden, x, batch);
+  with_ksplit(m, a);
+  return a;
 }
 
 // Enqueues one operation of decoder layer l for `batch` sequences.

@@ -96,6 +96,12 @@ struct GemvArgs {
   int32_t xn_stride;      // row stride of xn_out (batch > 1)
   int32_t batch;
   QkvEpilogue qkv;
+  // batch > 1, rows longer than one activation window: K split over the
+  // workgroups of a tile group (w4_rows_plan), partial sums
+  // [workgroups][TW][16][16] and arrival counters [tile groups] (zero between
+  // launches); nullptr: one workgroup per tile group, windows in turn
+  float* kpart;
+  uint32_t* kcount;
 };
 
 struct F16GemvArgs {
@@ -137,6 +143,21 @@ struct B1Split {
   int s, tw, it;
 };
 B1Split w4_b1_split(int tiles, int groups);
+
+// Batch 2..16 work split: S wavefronts per tile, TW tiles per workgroup, an
+// activation window of GW groups, CH workgroups per tile group, each taking
+// GW consecutive groups (CH = 1: one workgroup takes all groups, a window at
+// a time).
+struct RowsPlan {
+  int s, tw, gw, ch;
+};
+RowsPlan w4_rows_plan(int tiles, int groups, bool split_k);
+inline size_t w4_rows_kpart_floats(const RowsPlan& p, int tiles) {
+  return p.ch > 1 ? (size_t)ceil_div(tiles, p.tw) * p.ch * p.tw * 256 : 0;
+}
+inline size_t w4_rows_kcount_words(const RowsPlan& p, int tiles) {
+  return p.ch > 1 ? (size_t)ceil_div(tiles, p.tw) : 0;
+}
 
 // The persistent layer kernel (persistent.hip): one launch per decoder
 // layer, its five operations' arguments passed by value like those of the
