@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
   const int e = threadIdx.x & 1;
   const bool one_window = G <= GW;
   __shared__ float s_rs[16];
-  __shared__ float s_ss[kRowsThreads / 64][16];
+  __shared__ __align__(16) float s_ss[kRowsThreads / 64][16];
   // RMSNorm over rows longer than one window: wavefront w sums the squares
   // of rows w, w + NW, .. in a pre-pass
   if (a.gamma && !one_window) {
@@ -231,11 +231,14 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
           ss[m] = fmaf((float)h[1], (float)h[1], ss[m]);
         }
       }
+      // the 16 rows' reductions without a branch between them, so their
+      // dependent DPP chains interleave
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const float v = wave_sum(ss[m]);
-        if (lane == 0) s_ss[wave][m] = v;
-      }
+      for (int m = 0; m < 16; ++m) ss[m] = wave_sum(ss[m]);
+      if (lane == 0)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f4_t*>(&s_ss[wave][4 * q]) = (f4_t){ss[4 * q], ss[4 * q + 1], ss[4 * q + 2], ss[4 * q + 3]};
       __syncthreads();
       if (threadIdx.x < 16) {
         float tot = 0.f;
