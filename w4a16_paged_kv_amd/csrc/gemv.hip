@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
   const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
   const int e = threadIdx.x & 1;
   const bool one_window = G <= GW;
-  __shared__ float s_rs[16];
+  __shared__ __align__(16) float s_rs[16];
   __shared__ __align__(16) float s_ss[kRowsThreads / 64][16];
   // RMSNorm over rows longer than one window: wavefront w sums the squares
   // of rows w, w + NW, .. in a pre-pass
@@ -248,9 +248,16 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
     }
     __syncthreads();  // s_rs ready; the previous window's reads of xs are done
     if (a.gamma) {  // fp16(x * rs * gamma), the batch-1 staging's rounding
+      float rsv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4_t r4 = *reinterpret_cast<const f4_t*>(&s_rs[4 * q]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rsv[4 * q + j] = r4[j];
+      }
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
-        const float rs = s_rs[m];
+        const float rs = rsv[m];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const h2_t hv = as_h2(xv[m][c]), hg = as_h2(gv[c]);
