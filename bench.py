@@ -136,8 +136,8 @@ def main():
                          "counters taken over this run can be scaled by a copy of known size")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step here is "
-              "single-GPU, see the sharding notes in DESIGN.md", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the decode step is built "
+              "and measured for a single GPU; sharding across GPUs is not part of this library", file=sys.stderr)
         sys.exit(2)
 
     import torch
