@@ -248,9 +248,15 @@ static int enqueue_op(w4_model* m, int op, int l, const uint16_t* x_in, uint16_t
     case W4_OP_QKV:  // RMSNorm while staging, qkv projection, RoPE, K/V page write
       W4_LAUNCH(launch_w4_gemv(EPI_QKV, qkv_args(m, l, x_in, batch), s));
       return W4_OK;
-    case W4_OP_ATTN:  // paged attention, split over pages, LSE merge by the last split
-      W4_LAUNCH(launch_attention(attn_args(m, l, in, batch), c.head_dim, c.n_heads / c.n_kv_heads, s));
+    case W4_OP_ATTN: {  // paged attention, split over pages, LSE merge by the last split
+      const AttnArgs at = attn_args(m, l, in, batch);
+      // the partials buffer holds max_pages / 4 splits per (sequence, KV head)
+      if (at.max_splits > m->L.max_splits)
+        return fail(W4_EINVAL, "attention split of %d pages needs %d splits > %d", at.pages_per_split,
+                    at.max_splits, m->L.max_splits);
+      W4_LAUNCH(launch_attention(at, c.head_dim, c.n_heads / c.n_kv_heads, s));
       return W4_OK;
+    }
     case W4_OP_OPROJ:  // o projection + residual
       W4_LAUNCH(launch_w4_gemv(EPI_RESID, oproj_args(m, l, x_in, x_out, batch), s));
       return W4_OK;
