@@ -405,36 +405,52 @@ __global__ __launch_bounds__(WAVES * 64) void f16_gemv_b1_kernel(F16GemvArgs a, 
   }
 }
 
+// Batch 2..16: each wavefront computes TT tiles, so one load of the
+// activation operand (16 rows x 32 columns, from L2) serves TT weight blocks
+// (batch-16 7B lm_head: one tile per wavefront 200 us, two 186 us, four
+// 193 us). Weight blocks past the last tile re-read it; their rows are not
+// stored.
 template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void f16_gemm_mfma_kernel(F16GemvArgs a) {
+  constexpr int TT = 2, U = 8;
   const int C = a.cblocks;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * WAVES + wave;
-  if (t >= a.tiles) return;
-  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + (size_t)t * C * 64 + lane;
+  const int t0 = (blockIdx.x * WAVES + wave) * TT;
+  if (t0 >= a.tiles) return;
+  const u4_t* wb = reinterpret_cast<const u4_t*>(a.w) + lane;
   const int mrow = min(lane & 15, a.batch - 1);
   const uint16_t* xr = a.x + (size_t)mrow * a.x_stride + 8 * (lane >> 4);
-  f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 8;
+  f4_t acc[TT];
+#pragma unroll
+  for (int q = 0; q < TT; ++q) acc[q] = (f4_t){0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < C; base += U) {
-    u4_t wv[U], xv[U];
+    u4_t wv[TT][U], xv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = base + u;
-      wv[u] = c < C ? __builtin_nontemporal_load(wb + (size_t)c * 64) : (u4_t){0u, 0u, 0u, 0u};
       xv[u] = (c < C && 32 * c + 8 * (lane >> 4) < a.k) ? *reinterpret_cast<const u4_t*>(xr + 32 * c)
                                                            : (u4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < TT; ++q) {
+        const int t = min(t0 + q, a.tiles - 1);
+        wv[q][u] = c < C ? __builtin_nontemporal_load(wb + ((size_t)t * C + c) * 64) : (u4_t){0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xv[u]),
-                                                  __builtin_bit_cast(h8_t, wv[u]), acc, 0, 0, 0);
-  }
-  const int row = 16 * t + (lane & 15);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = 4 * (lane >> 4) + j;
-    if (m < a.batch && row < a.n) a.y[(size_t)m * a.y_stride + row] = f2h(acc[j]);
+      for (int q = 0; q < TT; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xv[u]),
+                                                       __builtin_bit_cast(h8_t, wv[q][u]), acc[q], 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < TT; ++q) {
+    const int row = 16 * (t0 + q) + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = 4 * (lane >> 4) + j;
+      if (m < a.batch && row < a.n) a.y[(size_t)m * a.y_stride + row] = f2h(acc[q][j]);
+    }
   }
 }
 
@@ -655,7 +671,7 @@ hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s) {
                        tpw);
   } else {
     constexpr int WAVES = 4;
-    hipLaunchKernelGGL((f16_gemm_mfma_kernel<WAVES>), dim3(ceil_div(a.tiles, WAVES)), dim3(WAVES * 64), 0, s, a);
+    hipLaunchKernelGGL((f16_gemm_mfma_kernel<WAVES>), dim3(ceil_div(a.tiles, WAVES * 2)), dim3(WAVES * 64), 0, s, a);
   }
   return hipGetLastError();
 }
