@@ -128,6 +128,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
 // staging) and the RMSNorm weights once per row took gate/up from 12.4 us of
 // prologue to ~3 us.
 constexpr int kRowsThreads = 768;  // launch bound: 16 activation words per thread stay in registers
+constexpr int kMaxChunks = 8;      // K split: at most 8 workgroups per tile group (rows up to 32768 columns)
 template <int EPI, int S>
 __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, int TW, int GW, int CH) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -316,8 +317,14 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
     __syncthreads();
     if (!s_last_k) return;
     for (int q = threadIdx.x; q < TW * 64; q += NT) {
+      f4_t part[kMaxChunks];  // every chunk's load in flight at once, then the sum in chunk order
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c)
+        part[c] = __builtin_bit_cast(f4_t, ld128_agent(rp, 16 * (min(c, CH - 1) * TW * 64 + q)));
       f4_t v = {0.f, 0.f, 0.f, 0.f};
-      for (int c = 0; c < CH; ++c) v += __builtin_bit_cast(f4_t, ld128_agent(rp, 16 * (c * TW * 64 + q)));
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c)
+        if (c < CH) v += part[c];
       *reinterpret_cast<f4_t*>(vals + 4 * q) = v;
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.kcount + tg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -585,7 +592,7 @@ static hipError_t launch_rows(const GemvArgs& a, const RowsPlan& p, int nt, size
 // activation rows instead of all of them (down projection, batch 16: 606 KiB
 // of activations per workgroup for 148 KiB of weights before the split).
 RowsPlan w4_rows_plan(int tiles, int groups, bool split_k) {
-  if (!split_k || groups <= 32) {
+  if (!split_k || groups <= 32 || groups > 32 * kMaxChunks) {
     const B1Split sp = w4_b1_split(tiles, groups);
     // many tiles: more than one workgroup per CU
     return {sp.s, std::min(sp.tw, kRowsThreads / (64 * sp.s)), std::min(groups, 32), 1};
