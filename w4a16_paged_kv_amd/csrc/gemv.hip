@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "gemv_b1.h"
 
@@ -656,15 +657,15 @@ hipError_t launch_w4_gemv(int epi, const GemvArgs& a, hipStream_t s) {
 
 // Compute units of the current device (workgroups of one round), cached.
 static int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];  // zero-initialised; racing callers store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 
 hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s) {
