@@ -117,7 +117,7 @@ __global__ __launch_bounds__(1024) void w4_gemv_b1_kernel(GemvArgs a, int TW) {
 // and the same packed blocks, exact dequantisation and
 // v_mfma_f32_16x16x32_f16 give D[batch row][weight row] in every lane. TW
 // tiles per workgroup, S wavefronts per tile; each wavefront streams its
-// window's blocks two batches of four ahead.
+// window's blocks two batches of kUnroll (three) ahead.
 //
 // Staging: thread t holds 8-column word t of the window in every one of the
 // 16 rows (NT >= 16 GW), so each thread issues its 16 activation loads (and

@@ -208,7 +208,11 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i,
 // ones keep the activation prologue amortised over several tiles. Each
 // wavefront streams its blocks U at a time with the next U loads in flight.
 
-constexpr int kUnroll = 4;  // blocks per batch; two batches in flight
+// Blocks per batch, two batches in flight. Batch-1 step on the 7B shape:
+// batches of 2, 3, 4, 6, 8 blocks gave 1.297, 1.265, 1.275, 1.384, 1.451 ms
+// (three: gate/up 14.8 -> 14.6 us, down 8.7 -> 8.35 us, o-proj 4.23 -> 4.09 us;
+// the batch-16 step 2.584 -> 2.557 ms).
+constexpr int kUnroll = 3;
 
 constexpr uint32_t kMaskLo = 0x000F000Fu;  // nibble offsets (0,1) / (4,5) of a word
 constexpr uint32_t kMaskHi = 0x00F000F0u;  // nibble offsets (2,3) / (6,7), as 16u
