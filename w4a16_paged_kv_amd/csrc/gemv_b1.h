@@ -437,6 +437,9 @@ __host__ __device__ constexpr size_t gemv_b1_lds_bytes(int groups, int s, int wa
 // counts stay exact, and scales stay fp16 in their own registers until used.
 template <int EPI, int S, int IT>
 struct GemvB1 {
+  // a one-word-per-thread row with an eight-way K split (the 7B o-projection)
+  // streams batches of two blocks: 4.08 -> 3.99 us per launch
+  static constexpr int kUnroll = (S == 8 && IT == 1) ? 2 : w4::kUnroll;
   static constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SILU;  // batch 1: RMSNorm prologue
   int t, ks, ng, last;
   const u4_t* wb;
