@@ -29,4 +29,6 @@ Modules:
   dense    -- brute-force dense re-statement (no pages, dense weights,
               repeat-kv multi-head attention) used to cross-check ``decode``
   packing  -- reads the packed weight formats of the library back into (q, s)
+  generate -- greedy token loop over ``decode`` (argmax, positions advancing
+              across page boundaries, optional teacher forcing)
 """
