@@ -319,6 +319,39 @@ int  paged_attention_decode(const uint16_t* q, const void* k_pool, const void* v
                             int32_t num_pages, int32_t max_pages, void* workspace,
                             size_t ws_bytes, uint16_t* out, void* stream);
 
+/* ------------------------------------------------------ greedy generation
+ * The token loop around the decode step ("Building a Custom LLM Inference
+ * Runtime on H100", Architecture Overview: the orchestrator runs the
+ * tokenization loop and feeds each chosen token back).
+ *
+ * w4_argmax_f16: out[b] = the index of the largest of logits[b][0..vocab),
+ * the lowest index among equal maxima; values compare exactly (fp16 widened
+ * to fp32); NaN is never chosen and a row of NaNs yields -1. logits: device
+ * fp16 [batch][vocab]; out: device int32 [batch]; 1 <= batch <= 65535.
+ * Asynchronous on `stream`; W4_EINVAL on a null pointer or bad size. */
+int  w4_argmax_f16(const uint16_t* logits, int32_t batch, int32_t vocab, int32_t* out,
+                   void* stream);
+/* n_steps greedy decode steps for `batch` sequences of `pool` (whose page ids
+ * index the model's KV cache). Sequence b (pool id seqs[b]) starts with token
+ * first_tokens[b] at position first_positions[b]; its prior tokens
+ * [0, first_positions[b]) must already be in the KV cache at the pages the
+ * pool holds for it (W4_ERANGE otherwise), and first_positions[b] + n_steps
+ * <= 16 * max_pages_per_seq. Step s decodes position p = first_positions[b]
+ * + s with ctx_len p + 1: kv_seq_reserve grows the sequence by one page
+ * whenever p starts a new page (W4_ENOPAGES when the pool is empty),
+ * page_table rebuilds the table, decode_step runs (graph or eager as set by
+ * w4_set_graph), w4_argmax_f16 picks each sequence's next token into
+ * next_tokens (device int32 [batch], 256-byte aligned, caller-owned) and the
+ * host copies it to out_tokens[s][b] (host int32 [n_steps][batch]), which is
+ * the input token of step s + 1. logits: device fp16 [batch][vocab], holding
+ * the last step's logits on return. Synchronises `stream` once per step.
+ * On an error, *steps_done (optional) counts the steps whose tokens are in
+ * out_tokens; pages already reserved stay with their sequences. */
+int  w4_generate_greedy(w4_model* model, w4_kv_pool* pool, const int32_t* seqs,
+                        const int32_t* first_tokens, const int32_t* first_positions,
+                        int32_t batch, int32_t n_steps, uint16_t* logits, int32_t* next_tokens,
+                        int32_t* out_tokens, int32_t* steps_done, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,7 +52,8 @@ def generate(w: "wl.Workload", n_steps: int, forced: Optional[np.ndarray] = None
     forced: optional int [n_steps, B]; when given, the input of step s + 1 is
     forced[s] instead of the oracle's own choice (teacher forcing: the chosen
     tokens are still returned). Returns {"tokens": int [n_steps, B],
-    "logits": float64 [n_steps, B, V], "positions": int [n_steps, B]}.
+    "logits": float64 [n_steps, B, V], "positions": int [n_steps, B], "pools":
+    the float64 (K, V) pools of every layer after the last step}.
     """
     sh, B = w.shape, w.batch
     assert w.lm_head and n_steps >= 1
@@ -79,4 +80,4 @@ def generate(w: "wl.Workload", n_steps: int, forced: Optional[np.ndarray] = None
         out_pos[s] = pos
         out_tok[s] = [greedy_token(logits[b]) for b in range(B)]
         tokens = np.asarray(forced[s], dtype=np.int64) if forced is not None else out_tok[s]
-    return {"tokens": out_tok, "logits": out_logits, "positions": out_pos}
+    return {"tokens": out_tok, "logits": out_logits, "positions": out_pos, "pools": pools}

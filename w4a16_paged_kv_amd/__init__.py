@@ -85,6 +85,9 @@ _SIGS = {
     "paged_attention_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "paged_attention_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                        c_int32, c_int32, c_int32, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "w4_argmax_f16": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "w4_generate_greedy": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                   c_void_p, c_void_p, c_void_p, POINTER(c_int32), c_void_p]),
 }
 EXPORTED = sorted(_SIGS)
 
@@ -306,8 +309,26 @@ class Model:
         _check(lib().decode_layer(self.handle, layer, _ptr(x_in), _ptr(x_out), *(_ptr(a) for a in arrs),
                                   len(arrs[0]), _stream(stream)))
 
+    def w4_generate_greedy(self, pool: "KvPool", seqs, first_tokens, first_positions, n_steps: int,
+                           logits, next_tokens, stream=None) -> np.ndarray:
+        """n_steps greedy steps; returns the chosen tokens, int32 [n_steps, B].
+        logits: device fp16 [B, vocab]; next_tokens: device int32 [B]."""
+        arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in (seqs, first_tokens, first_positions)]
+        batch = len(arrs[0])
+        out = np.zeros((max(n_steps, 0), batch), dtype=np.int32)
+        done = c_int32()
+        _check(lib().w4_generate_greedy(self.handle, pool.handle, *(_ptr(a) for a in arrs), batch, n_steps,
+                                        _ptr(logits), _ptr(next_tokens), _ptr(out), ctypes.byref(done),
+                                        _stream(stream)))
+        return out
+
 
 # ------------------------------------------------------------------ kernels
+
+def w4_argmax_f16(logits, out, stream=None) -> None:
+    """out[b] = argmax of logits[b] (lowest index among equal maxima); device tensors."""
+    batch, vocab = logits.shape
+    _check(lib().w4_argmax_f16(_ptr(logits), batch, vocab, _ptr(out), _stream(stream)))
 
 def w4_gemv(packed, x, y, n: int, k: int, batch: int = 1, stream=None) -> None:
     _check(lib().w4_gemv(_ptr(packed), _ptr(x), _ptr(y), n, k, batch, _stream(stream)))

@@ -789,3 +789,67 @@ W4_EXPORT void* w4_model_buffer(w4_model* m, int32_t which, int32_t* row_stride)
   if (row_stride) *row_stride = stride;
   return m->ws + off;
 }
+
+// Greedy generation: the token loop of "Building a Custom LLM Inference
+// Runtime on H100" (Architecture Overview: the orchestrator drives the decode
+// step and feeds each chosen token back). Every step grows each sequence's
+// pages through the pool when its new position starts a page ("The Three
+// Critical Bugs", Bug 1: logical position -> physical page), builds the page
+// table, runs decode_step and takes the argmax of the logits on the device.
+W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* seqs,
+                                 const int32_t* first_tokens, const int32_t* first_positions,
+                                 int32_t batch, int32_t n_steps, uint16_t* logits,
+                                 int32_t* next_tokens, int32_t* out_tokens, int32_t* steps_done,
+                                 void* stream) {
+  clear_error();
+  if (steps_done) *steps_done = 0;
+  int rc = check_model(m, batch);
+  if (rc) return rc;
+  if (!pool || !seqs || !first_tokens || !first_positions || !logits || !next_tokens ||
+      (n_steps > 0 && !out_tokens))
+    return fail(W4_EINVAL, "w4_generate_greedy: null pointer");
+  if (n_steps < 0) return fail(W4_EINVAL, "w4_generate_greedy: n_steps %d < 0", n_steps);
+  if (!aligned256(next_tokens))
+    return fail(W4_EALIGN, "w4_generate_greedy: next_tokens not 256-byte aligned");
+  const int64_t cap = (int64_t)m->max_pages * kPage;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t p0 = first_positions[b];
+    if (p0 < 0 || (int64_t)p0 + n_steps > cap)
+      return fail(W4_ERANGE, "w4_generate_greedy: sequence %d positions [%d, %lld) outside [0, %lld)",
+                  b, p0, (long long)p0 + n_steps, (long long)cap);
+    if (first_tokens[b] < 0 || first_tokens[b] >= m->cfg.vocab)
+      return fail(W4_ERANGE, "w4_generate_greedy: first token %d of sequence %d outside [0, %d)",
+                  first_tokens[b], b, m->cfg.vocab);
+    const int32_t have = kv_seq_pages(pool, seqs[b]);
+    if (have < 0) return fail(W4_ERANGE, "w4_generate_greedy: sequence id %d not in the pool", seqs[b]);
+    if ((int64_t)have * kPage < p0)
+      return fail(W4_ERANGE, "w4_generate_greedy: sequence %d holds %d pages, fewer than its %d prior tokens need",
+                  seqs[b], have, p0);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> tok(first_tokens, first_tokens + batch), pos(first_positions, first_positions + batch);
+  std::vector<int32_t> ctx(batch), pt((size_t)batch * m->max_pages);
+  for (int step = 0; step < n_steps; ++step) {
+    for (int b = 0; b < batch; ++b) {
+      ctx[b] = pos[b] + 1;
+      rc = kv_seq_reserve(pool, seqs[b], ctx[b]);
+      if (rc) return rc;
+    }
+    rc = page_table(pool, seqs, batch, m->max_pages, pt.data());
+    if (rc) return rc;
+    rc = decode_step(m, tok.data(), pos.data(), pt.data(), ctx.data(), batch, logits, stream);
+    if (rc) return rc;
+    W4_HIP(launch_argmax_f16(logits, batch, m->cfg.vocab, next_tokens, s));
+    int32_t* row = out_tokens + (size_t)step * batch;
+    W4_HIP(hipMemcpyAsync(row, next_tokens, batch * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    W4_HIP(hipStreamSynchronize(s));
+    for (int b = 0; b < batch; ++b) {
+      if (row[b] < 0)
+        return fail(W4_ERANGE, "w4_generate_greedy: step %d, sequence %d: every logit is NaN", step, b);
+      tok[b] = row[b];
+      ++pos[b];
+    }
+    if (steps_done) *steps_done = step + 1;
+  }
+  return W4_OK;
+}
