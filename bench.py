@@ -24,6 +24,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+GEN_STEPS = 16            # greedy generation steps timed after the step itself
+ARGMAX_CALLS = 20         # greedy-choice calls per timed graph replay
 METRIC = "decode ms/token + effective HBM GB/s (% of peak), Qwen2.5-7B-shape W4A16"
 
 
@@ -235,6 +237,54 @@ def main():
     digest = source_digest(*kernels[dom])
     achieved = dom_bytes / (op_ms[dom] * 1e-3)
 
+    # ---- greedy generation loop (w4_generate_greedy): the last GEN_STEPS
+    # positions of every sequence's context, with pool growth, page tables,
+    # the step, the device argmax and one host synchronisation per step; the
+    # pool hands out its own pages (every KV slot is an N(0,1) draw, so any
+    # page assignment is an equally valid input). Timed by the host clock.
+    gen_steps = int(min(GEN_STEPS, ctx.min()))
+    nxt = torch.empty((B,), dtype=torch.int32, device="cuda")
+    p0 = (ctx - gen_steps).astype(np.int32)
+
+    def generation(n):
+        pool = w4.KvPool(w.num_pages, B)
+        for b in range(B):
+            pool.kv_seq_reserve(b, int(p0[b]))
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        stop = None
+        try:
+            toks = m.w4_generate_greedy(pool, list(range(B)), tokens, p0, n, logits, nxt)
+            steps = n
+        except w4.W4Error as e:
+            # the seeded random-init model can overflow the fp16 residual on
+            # some trajectories (all logits NaN): that step still ran
+            if "NaN" not in str(e):
+                raise
+            toks, steps, stop = e.tokens, e.steps_done + 1, str(e)
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t
+        pool.close()
+        return t, toks, steps, stop
+
+    generation(2)
+    gen_s, gen_toks, gen_run, gen_stop = generation(gen_steps)
+    assert ((gen_toks >= 0) & (gen_toks < sh.vocab)).all()
+    g = torch.cuda.CUDAGraph()
+    amax_ws = torch.empty((w4.w4_argmax_workspace_bytes(B, sh.vocab),), dtype=torch.uint8, device="cuda")
+    with torch.cuda.graph(g):                     # 20 calls per replay: one replay's own
+        for _ in range(ARGMAX_CALLS):             # launch cost is not the kernels' time
+            w4.w4_argmax_f16(logits, nxt, amax_ws)
+    g.replay()
+    argmax_ms = timed(g.replay, args.op_reps) / ARGMAX_CALLS
+    del g
+    gen = {"steps": gen_run, "ms_per_step": round(gen_s * 1e3 / gen_run, 4),
+           "ms_per_token": round(gen_s * 1e3 / gen_run / B, 4), "clock": "host, one sync per step",
+           "stopped": gen_stop,
+           "argmax_us_per_call": round(argmax_ms * 1e3, 2), "argmax_kernels_per_call": 2,
+           "argmax_GBps": round(B * sh.vocab * 2 / (argmax_ms * 1e-3) / 1e9, 1),
+           "argmax_bytes_per_call": B * sh.vocab * 2}
+
     cpu = None if args.no_cpu else cpu_baseline(w)
 
     tok_s = B * 1e3 / ms
@@ -271,6 +321,7 @@ def main():
                      "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": round(achieved / PEAK_HBM, 4),
                      "traffic": read_traffic(dom, digest), "bytes_per_launch": int(dom_bytes),
                      "us_per_launch": round(op_ms[dom] * 1e3, 2), "source_digest": digest},
+        "generate": gen,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

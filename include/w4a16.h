@@ -328,9 +328,12 @@ int  paged_attention_decode(const uint16_t* q, const void* k_pool, const void* v
  * the lowest index among equal maxima; values compare exactly (fp16 widened
  * to fp32); NaN is never chosen and a row of NaNs yields -1. logits: device
  * fp16 [batch][vocab]; out: device int32 [batch]; 1 <= batch <= 65535.
- * Asynchronous on `stream`; W4_EINVAL on a null pointer or bad size. */
-int  w4_argmax_f16(const uint16_t* logits, int32_t batch, int32_t vocab, int32_t* out,
-                   void* stream);
+ * workspace: device, >= w4_argmax_workspace_bytes(batch, vocab) (per-chunk
+ * partials; at most 512 bytes per row), caller-owned. Asynchronous on
+ * `stream`; W4_EINVAL on a null pointer, a bad size or a short workspace. */
+size_t w4_argmax_workspace_bytes(int32_t batch, int32_t vocab);   /* 0 on bad sizes */
+int  w4_argmax_f16(const uint16_t* logits, int32_t batch, int32_t vocab, void* workspace,
+                   size_t ws_bytes, int32_t* out, void* stream);
 /* n_steps greedy decode steps for `batch` sequences of `pool` (whose page ids
  * index the model's KV cache). Sequence b (pool id seqs[b]) starts with token
  * first_tokens[b] at position first_positions[b]; its prior tokens
@@ -340,7 +343,8 @@ int  w4_argmax_f16(const uint16_t* logits, int32_t batch, int32_t vocab, int32_t
  * + s with ctx_len p + 1: kv_seq_reserve grows the sequence by one page
  * whenever p starts a new page (W4_ENOPAGES when the pool is empty),
  * page_table rebuilds the table, decode_step runs (graph or eager as set by
- * w4_set_graph), w4_argmax_f16 picks each sequence's next token into
+ * w4_set_graph), the w4_argmax_f16 kernels (partials in the model's
+ * workspace) pick each sequence's next token into
  * next_tokens (device int32 [batch], 256-byte aligned, caller-owned) and the
  * host copies it to out_tokens[s][b] (host int32 [n_steps][batch]), which is
  * the input token of step s + 1. logits: device fp16 [batch][vocab], holding

@@ -26,16 +26,18 @@ def f16_dev(a: np.ndarray) -> torch.Tensor:
 def gpu_argmax(rows: np.ndarray) -> np.ndarray:
     batch = rows.shape[0]
     out = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
-    w4.w4_argmax_f16(f16_dev(rows), out)
+    ws = torch.full((w4.w4_argmax_workspace_bytes(batch, rows.shape[1]),), 0x7f, dtype=torch.uint8, device="cuda")
+    w4.w4_argmax_f16(f16_dev(rows), out, ws)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
 @pytest.mark.parametrize("batch,vocab", [(1, 152064), (16, 152064), (3, 5000), (4, 5003), (2, 7),
-                                         (16, 1), (5, 1001)])
+                                         (16, 1), (5, 1001), (2, 2047), (3, 2049), (2, 131077)])
 def test_argmax_matches_oracle_bit_exactly(batch, vocab):
     """Ragged vocabularies (odd and non-multiple-of-8 rows take the unaligned
-    path on every other row), planted ties, -inf rows, NaNs."""
+    path on every other row; one chunk, two chunks, 64 chunks with a short
+    last one), planted ties (also across chunks), -inf rows, NaNs."""
     rs = np.random.default_rng(1000 + vocab + batch)
     rows = rs.standard_normal((batch, vocab)).astype(np.float16)
     for b in range(batch):

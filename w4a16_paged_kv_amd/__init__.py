@@ -85,7 +85,8 @@ _SIGS = {
     "paged_attention_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "paged_attention_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                        c_int32, c_int32, c_int32, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
-    "w4_argmax_f16": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "w4_argmax_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+    "w4_argmax_f16": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
     "w4_generate_greedy": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                    c_void_p, c_void_p, c_void_p, POINTER(c_int32), c_void_p]),
 }
@@ -317,18 +318,29 @@ class Model:
         batch = len(arrs[0])
         out = np.zeros((max(n_steps, 0), batch), dtype=np.int32)
         done = c_int32()
-        _check(lib().w4_generate_greedy(self.handle, pool.handle, *(_ptr(a) for a in arrs), batch, n_steps,
-                                        _ptr(logits), _ptr(next_tokens), _ptr(out), ctypes.byref(done),
-                                        _stream(stream)))
+        rc = lib().w4_generate_greedy(self.handle, pool.handle, *(_ptr(a) for a in arrs), batch, n_steps,
+                                      _ptr(logits), _ptr(next_tokens), _ptr(out), ctypes.byref(done),
+                                      _stream(stream))
+        if rc != W4_OK:
+            err = W4Error(rc, lib().w4_last_error().decode())
+            err.steps_done, err.tokens = done.value, out[:done.value]   # steps whose tokens were chosen
+            raise err
         return out
 
 
 # ------------------------------------------------------------------ kernels
 
-def w4_argmax_f16(logits, out, stream=None) -> None:
-    """out[b] = argmax of logits[b] (lowest index among equal maxima); device tensors."""
+def w4_argmax_workspace_bytes(batch: int, vocab: int) -> int:
+    return lib().w4_argmax_workspace_bytes(batch, vocab)
+
+
+def w4_argmax_f16(logits, out, workspace, stream=None) -> None:
+    """out[b] = argmax of logits[b] (lowest index among equal maxima); device
+    tensors; workspace >= w4_argmax_workspace_bytes(batch, vocab) bytes."""
     batch, vocab = logits.shape
-    _check(lib().w4_argmax_f16(_ptr(logits), batch, vocab, _ptr(out), _stream(stream)))
+    _check(lib().w4_argmax_f16(_ptr(logits), batch, vocab, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+
 
 def w4_gemv(packed, x, y, n: int, k: int, batch: int = 1, stream=None) -> None:
     _check(lib().w4_gemv(_ptr(packed), _ptr(x), _ptr(y), n, k, batch, _stream(stream)))

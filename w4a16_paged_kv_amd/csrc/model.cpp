@@ -16,12 +16,14 @@
 #include <tuple>
 #include <vector>
 
+#include "sample.h"
 #include "w4_internal.h"
 
 namespace w4 {
 
 struct WsLayout {
-  size_t err, counters, bar, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, kpart, kcount, total;
+  size_t err, counters, bar, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, kpart, kcount, amax,
+      total;
   int xn_stride, o_stride, h_stride, max_splits;
 };
 
@@ -65,6 +67,7 @@ static WsLayout ws_layout(const w4_config& c, int max_batch, int max_pages) {
     }
   L.kpart = kp ? take(kp * 4) : 0;
   L.kcount = kw ? take(kw * 4) : 0;
+  L.amax = take(argmax_workspace_bytes(max_batch, c.vocab));   // greedy token choice partials
   L.total = off;
   return L;
 }
@@ -839,7 +842,7 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
     if (rc) return rc;
     rc = decode_step(m, tok.data(), pos.data(), pt.data(), ctx.data(), batch, logits, stream);
     if (rc) return rc;
-    W4_HIP(launch_argmax_f16(logits, batch, m->cfg.vocab, next_tokens, s));
+    W4_HIP(launch_argmax_f16(logits, batch, m->cfg.vocab, m->ws + m->L.amax, next_tokens, s));
     int32_t* row = out_tokens + (size_t)step * batch;
     W4_HIP(hipMemcpyAsync(row, next_tokens, batch * sizeof(int32_t), hipMemcpyDeviceToHost, s));
     W4_HIP(hipStreamSynchronize(s));

@@ -186,8 +186,6 @@ hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16
 hipError_t launch_embed_plan(const TokenPlanArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t s);
-hipError_t launch_argmax_f16(const uint16_t* logits, int batch, int vocab, int32_t* out,
-                             hipStream_t s);
 bool attention_supported(int head_dim, int group);
 
 // Pages per attention split for a batch / context size: enough workgroups to
