@@ -115,6 +115,16 @@ size_t w4_packed_bytes(int32_t n, int32_t k);
 int pack_weights_w4g128(const int8_t* q, const uint16_t* scales, int32_t n, int32_t k,
                         uint32_t role, int32_t head_dim, void* out, size_t out_bytes);
 
+/* Symmetric group-wise INT4 quantisation [RT-arch] (the step before
+ * pack_weights_w4g128). w: host fp16 [n*k] row-major, every value finite;
+ * q: host int8 [n*k]; scales: host fp16 [n * ceil(k/128)]. Per row and
+ * group of 128 input columns (the last group partial): s = the fp16 value
+ * nearest to max|w| / 7; q = the integer in [-8, 7] nearest to w / s, halves
+ * to even (so |w - q s| <= s / 2, and +-max|w| maps to +-7); s = 0 gives
+ * q = 0. Pure and deterministic. W4_ERANGE on a non-finite weight (nothing
+ * written), W4_EINVAL on null pointers or bad shapes. */
+int quantize_w4g128(const uint16_t* w, int32_t n, int32_t k, int8_t* q, uint16_t* scales);
+
 /* Packed fp16 format (lm_head, kept in FP16 [RT-arch]): T = ceil(n/16)
  * tiles, C = ceil(k/32) column blocks; block (t, c) of 1024 bytes starts at
  * (t*C + c)*1024; lane l owns bytes [16l, 16l+16) = the 8 fp16 values of row

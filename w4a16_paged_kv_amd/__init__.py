@@ -53,6 +53,7 @@ _SIGS = {
     "w4_version": (ctypes.c_char_p, []),
     "w4_packed_bytes": (c_size_t, [c_int32, c_int32]),
     "pack_weights_w4g128": (c_int, [c_void_p, c_void_p, c_int32, c_int32, c_uint32, c_int32, c_void_p, c_size_t]),
+    "quantize_w4g128": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "w4_packed_f16_bytes": (c_size_t, [c_int32, c_int32]),
     "pack_weights_f16": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_size_t]),
     "kv_pool_create": (c_int, [c_int32, c_int32, POINTER(c_void_p)]),
@@ -154,6 +155,16 @@ def pack_weights_w4g128(q: np.ndarray, scales: np.ndarray, role: int = ROLE_PLAI
     out = np.empty(w4_packed_bytes(n, k), dtype=np.uint8)
     _check(lib().pack_weights_w4g128(_ptr(q), _ptr(scales), n, k, role, head_dim, _ptr(out), out.size))
     return out
+
+
+def quantize_w4g128(w: np.ndarray):
+    """fp16 [n, k] -> (q int8 [n, k], scales fp16 [n, ceil(k/128)]), host arrays."""
+    w = np.ascontiguousarray(w, dtype=np.float16)
+    n, k = w.shape
+    q = np.empty((n, k), dtype=np.int8)
+    s = np.empty((n, (k + 127) // 128), dtype=np.float16)
+    _check(lib().quantize_w4g128(_ptr(w), n, k, _ptr(q), _ptr(s)))
+    return q, s
 
 
 def w4_packed_f16_bytes(n: int, k: int) -> int:

@@ -1,6 +1,7 @@
 // Host side of libw4a16 that needs no GPU: error state, the weight packers
 // and the KV page pool.
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -75,6 +76,45 @@ W4_EXPORT const char* w4_version(void) { return "w4a16-paged-kv-amd 0.1 (gfx950)
 W4_EXPORT size_t w4_packed_bytes(int32_t n, int32_t k) {
   if (n <= 0 || k <= 0) return 0;
   return (size_t)w4_tiles(n) * w4_groups(k) * (1024 + 32);
+}
+
+// Symmetric group-wise INT4 quantisation ("How to build your own LLM runtime
+// from scratch", "Architectural decisions and optimizations": symmetric
+// group-wise INT4, group 128). Per (row, group of 128 input columns): the
+// scale is the fp16 value nearest to max|w| / 7 and each code the integer in
+// [-8, 7] nearest to w / s, halves to even (the default rounding mode of
+// nearbyint); a zero scale gives zero codes. w and s are fp16 values, so
+// their quotient is never within double rounding of a halfway point unless
+// it is one: the double division decides every code exactly.
+W4_EXPORT int quantize_w4g128(const uint16_t* w, int32_t n, int32_t k, int8_t* q,
+                              uint16_t* scales) {
+  clear_error();
+  if (!w || !q || !scales) return fail(W4_EINVAL, "quantize_w4g128: null pointer");
+  if (n <= 0 || k <= 0) return fail(W4_EINVAL, "quantize_w4g128: bad shape n=%d k=%d", n, k);
+  const size_t total = (size_t)n * k;
+  for (size_t i = 0; i < total; ++i)
+    if ((w[i] & 0x7c00u) == 0x7c00u)
+      return fail(W4_ERANGE, "quantize_w4g128: w[%zu] is not finite", i);
+  const int G = w4_groups(k);
+  parallel_for(n, [&](int r0, int r1) {
+    for (int r = r0; r < r1; ++r) {
+      for (int g = 0; g < G; ++g) {
+        const int lo = g * kGroup, hi = std::min(k, lo + kGroup);
+        const uint16_t* wr = w + (size_t)r * k;
+        double m = 0.0;
+        for (int j = lo; j < hi; ++j) m = std::max(m, std::fabs((double)__builtin_bit_cast(_Float16, wr[j])));
+        const _Float16 s16 = (_Float16)(m / 7.0);   // correctly rounded double -> fp16
+        scales[(size_t)r * G + g] = __builtin_bit_cast(uint16_t, s16);
+        const double s = (double)s16;
+        for (int j = lo; j < hi; ++j) {
+          double c = 0.0;
+          if (s > 0.0) c = std::nearbyint((double)__builtin_bit_cast(_Float16, wr[j]) / s);
+          q[(size_t)r * k + j] = (int8_t)std::min(7.0, std::max(-8.0, c));
+        }
+      }
+    }
+  });
+  return W4_OK;
 }
 
 W4_EXPORT int pack_weights_w4g128(const int8_t* q, const uint16_t* scales, int32_t n, int32_t k,
