@@ -352,15 +352,19 @@ int  w4_argmax_f16(const uint16_t* logits, int32_t batch, int32_t vocab, void* w
  * <= 16 * max_pages_per_seq. Step s decodes position p = first_positions[b]
  * + s with ctx_len p + 1: kv_seq_reserve grows the sequence by one page
  * whenever p starts a new page (W4_ENOPAGES when the pool is empty),
- * page_table rebuilds the table, decode_step runs (graph or eager as set by
- * w4_set_graph), the w4_argmax_f16 kernels (partials in the model's
- * workspace) pick each sequence's next token into
- * next_tokens (device int32 [batch], 256-byte aligned, caller-owned) and the
- * host copies it to out_tokens[s][b] (host int32 [n_steps][batch]), which is
- * the input token of step s + 1. logits: device fp16 [batch][vocab], holding
- * the last step's logits on return. Synchronises `stream` once per step.
- * On an error, *steps_done (optional) counts the steps whose tokens are in
- * out_tokens; pages already reserved stay with their sequences. */
+ * page_table rebuilds the table, and the step runs as decode_step would
+ * (graph or eager as set by w4_set_graph); the w4_argmax_f16 kernels
+ * (partials in the model's workspace) write each sequence's next token into
+ * the model's staged token slot, which step s + 1 reads, and the host
+ * copies it to out_tokens[s][b] (host int32 [n_steps][batch]) and to
+ * next_tokens (device int32 [batch], 256-byte aligned, caller-owned: the
+ * last chosen tokens on return). Step s + 1's positions and page table are
+ * staged while step s runs; the host waits once per step for the chosen
+ * tokens and stops with W4_ERANGE on a row with no non-NaN logit, before
+ * running another step. logits: device fp16 [batch][vocab], 256-byte
+ * aligned, holding the last step's logits on return. On an error,
+ * *steps_done (optional) counts the steps whose tokens are in out_tokens;
+ * pages already reserved stay with their sequences. */
 int  w4_generate_greedy(w4_model* model, w4_kv_pool* pool, const int32_t* seqs,
                         const int32_t* first_tokens, const int32_t* first_positions,
                         int32_t batch, int32_t n_steps, uint16_t* logits, int32_t* next_tokens,

@@ -798,7 +798,12 @@ W4_EXPORT void* w4_model_buffer(w4_model* m, int32_t which, int32_t* row_stride)
 // step and feeds each chosen token back). Every step grows each sequence's
 // pages through the pool when its new position starts a page ("The Three
 // Critical Bugs", Bug 1: logical position -> physical page), builds the page
-// table, runs decode_step and takes the argmax of the logits on the device.
+// table, runs the step and takes the argmax of the logits on the device,
+// straight into the staged token slot that the next step's embedding reads.
+// Positions, and so page growth, do not depend on the chosen tokens: step
+// s + 1's positions, page table and context lengths are validated and staged
+// while step s still runs, and the host waits once per step only for the
+// chosen tokens (to stop on a row with no choice before running another step).
 W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* seqs,
                                  const int32_t* first_tokens, const int32_t* first_positions,
                                  int32_t batch, int32_t n_steps, uint16_t* logits,
@@ -812,8 +817,10 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
       (n_steps > 0 && !out_tokens))
     return fail(W4_EINVAL, "w4_generate_greedy: null pointer");
   if (n_steps < 0) return fail(W4_EINVAL, "w4_generate_greedy: n_steps %d < 0", n_steps);
-  if (!aligned256(next_tokens))
-    return fail(W4_EALIGN, "w4_generate_greedy: next_tokens not 256-byte aligned");
+  if (!m->weights.embed || !m->weights.lm_head || !m->weights.final_norm)
+    return fail(W4_EINVAL, "w4_generate_greedy: model has no embedding / final norm / lm_head");
+  if (!aligned256(next_tokens) || !aligned256(logits))
+    return fail(W4_EALIGN, "w4_generate_greedy: next_tokens or logits not 256-byte aligned");
   const int64_t cap = (int64_t)m->max_pages * kPage;
   for (int b = 0; b < batch; ++b) {
     const int32_t p0 = first_positions[b];
@@ -830,29 +837,46 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
                   seqs[b], have, p0);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  std::vector<int32_t> tok(first_tokens, first_tokens + batch), pos(first_positions, first_positions + batch);
+  if (n_steps == 0) return W4_OK;
+  std::vector<int32_t> pos(first_positions, first_positions + batch);
   std::vector<int32_t> ctx(batch), pt((size_t)batch * m->max_pages);
-  for (int step = 0; step < n_steps; ++step) {
+  // validates and stages the positions of the next step (tokens: host array
+  // for the first step, else already in the staged slot)
+  auto stage_step = [&](const int32_t* tokens) -> int {
     for (int b = 0; b < batch; ++b) {
       ctx[b] = pos[b] + 1;
-      rc = kv_seq_reserve(pool, seqs[b], ctx[b]);
-      if (rc) return rc;
+      int r = kv_seq_reserve(pool, seqs[b], ctx[b]);
+      if (r) return r;
     }
-    rc = page_table(pool, seqs, batch, m->max_pages, pt.data());
+    int r = page_table(pool, seqs, batch, m->max_pages, pt.data());
+    if (r) return r;
+    r = validate_inputs(m, tokens, pos.data(), pt.data(), ctx.data(), batch);
+    if (r) return r;
+    return stage_inputs(m, tokens, pos.data(), pt.data(), ctx.data(), batch, s);
+  };
+  rc = stage_step(first_tokens);
+  if (rc) return rc;
+  int32_t* tok_dev = m->at<int32_t>(m->L.tokens);
+  for (int step = 0; step < n_steps; ++step) {
+    rc = run_step(m, staged(m), batch, logits, s, nullptr);
     if (rc) return rc;
-    rc = decode_step(m, tok.data(), pos.data(), pt.data(), ctx.data(), batch, logits, stream);
-    if (rc) return rc;
-    W4_HIP(launch_argmax_f16(logits, batch, m->cfg.vocab, m->ws + m->L.amax, next_tokens, s));
+    W4_HIP(launch_argmax_f16(logits, batch, m->cfg.vocab, m->ws + m->L.amax, tok_dev, s));
+    // the next step's inputs are staged first: the copy of the chosen tokens
+    // into pageable host memory may block until the step has finished
+    int stage_rc = W4_OK;
+    if (step + 1 < n_steps) {
+      for (int b = 0; b < batch; ++b) ++pos[b];
+      stage_rc = stage_step(nullptr);
+    }
     int32_t* row = out_tokens + (size_t)step * batch;
-    W4_HIP(hipMemcpyAsync(row, next_tokens, batch * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    W4_HIP(hipMemcpyAsync(next_tokens, tok_dev, batch * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+    W4_HIP(hipMemcpyAsync(row, tok_dev, batch * sizeof(int32_t), hipMemcpyDeviceToHost, s));
     W4_HIP(hipStreamSynchronize(s));
-    for (int b = 0; b < batch; ++b) {
+    for (int b = 0; b < batch; ++b)
       if (row[b] < 0)
         return fail(W4_ERANGE, "w4_generate_greedy: step %d, sequence %d: every logit is NaN", step, b);
-      tok[b] = row[b];
-      ++pos[b];
-    }
     if (steps_done) *steps_done = step + 1;
+    if (stage_rc) return stage_rc;
   }
   return W4_OK;
 }
