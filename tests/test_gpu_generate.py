@@ -161,3 +161,29 @@ def test_generation_errors():
     with pytest.raises(w4.W4Error, match="ERANGE"):      # first token outside the vocabulary
         dm.model.w4_generate_greedy(pool, [0], [SMALL.vocab], p0, 1, logits, nxt)
     torch.cuda.synchronize()
+
+
+def test_generation_full_size_matches_decode_step():
+    """The 28-layer Qwen2.5-7B-shape model, batch 1, the loop as the benchmark
+    runs it (start 16 tokens before the 2048-token context ends, so the pool
+    grows at position 2032): after two steps the logits equal a separate
+    decode_step of the second step's inputs bit for bit, the chosen tokens
+    are the host argmax of those logits (lowest index), and the sequence
+    holds 128 pages."""
+    w = wl.step_b1()
+    print("building the 28-layer model", flush=True)
+    dm = DeviceModel(w)
+    p0 = (w.ctx_lens - 16).astype(np.int32)
+    pool = w4.KvPool(w.num_pages, 1)
+    pool.kv_seq_reserve(0, int(p0[0]))
+    assert pool.kv_seq_pages(0) == 127
+    toks, last = run_generation(dm, pool, w, p0, 2)
+    assert pool.kv_seq_pages(0) == 128
+    assert og.greedy_token(last[0].astype(np.float64)) == toks[1, 0]
+    pt = pool.page_table([0], w.max_pages)
+    logits = torch.empty((1, w.shape.vocab), dtype=torch.float16, device="cuda")
+    dm.model.decode_step(toks[0], p0 + 1, pt, p0 + 2, logits)
+    torch.cuda.synchronize()
+    again = to_np16(logits)
+    assert np.array_equal(again.view(np.uint16), last.view(np.uint16))
+    assert dm.model.w4_device_errors() == 0
