@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
 GEN_STEPS = 16            # greedy generation steps timed after the step itself
 ARGMAX_CALLS = 20         # greedy-choice calls per timed graph replay
+COPY_BYTES = 1 << 30      # plain copy timed for the measured streaming rate
 METRIC = "decode ms/token + effective HBM GB/s (% of peak), Qwen2.5-7B-shape W4A16"
 
 
@@ -285,6 +286,17 @@ def main():
            "argmax_GBps": round(B * sh.vocab * 2 / (argmax_ms * 1e-3) / 1e9, 1),
            "argmax_bytes_per_call": B * sh.vocab * 2}
 
+    # ---- measured streaming rate of this GPU: a plain device-to-device copy
+    # of 1 GiB (reads 1 GiB, writes 1 GiB), for the step's share of what a
+    # simple streaming kernel reaches on the same box
+    src = torch.empty((COPY_BYTES // 2,), dtype=torch.float16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_ms = timed(lambda: dst.copy_(src), 10)
+    copy_GBps = 2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+
     cpu = None if args.no_cpu else cpu_baseline(w)
 
     tok_s = B * 1e3 / ms
@@ -310,6 +322,8 @@ def main():
         "effective_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "pct_of_peak": round(100 * step_bytes / (ms * 1e-3) / PEAK_HBM, 2),
         "bytes_per_step": int(step_bytes),
+        "measured_copy_GBps": round(copy_GBps, 1),
+        "pct_of_measured_copy": round(100 * step_bytes / (ms * 1e-3) / 1e9 / copy_GBps, 2),
         "ms_per_step_p10_p50_p90": [round(float(v), 4) for v in pct],
         "ms_per_step_host_inputs": round(host_ms, 4),
         "ms_per_step_eager": round(eager_ms, 4),
