@@ -340,7 +340,9 @@ int  paged_attention_decode(const uint16_t* q, const void* k_pool, const void* v
  * fp16 [batch][vocab]; out: device int32 [batch]; 1 <= batch <= 65535.
  * workspace: device, >= w4_argmax_workspace_bytes(batch, vocab) (per-chunk
  * partials; at most 512 bytes per row), caller-owned. Asynchronous on
- * `stream`; W4_EINVAL on a null pointer, a bad size or a short workspace. */
+ * `stream`; W4_EINVAL on a null pointer, a bad size or a short workspace,
+ * W4_EALIGN if logits, workspace or out is not 256-byte aligned (rows of an
+ * odd vocab start unaligned inside the buffer; that is handled). */
 size_t w4_argmax_workspace_bytes(int32_t batch, int32_t vocab);   /* 0 on bad sizes */
 int  w4_argmax_f16(const uint16_t* logits, int32_t batch, int32_t vocab, void* workspace,
                    size_t ws_bytes, int32_t* out, void* stream);

@@ -98,3 +98,24 @@ def test_kernel_entry_argument_errors():
     assert L.paged_attention_decode(*args, need - 1, 0x7000, None) == w4.W4_EINVAL
     args[1] = 0x2008
     assert L.paged_attention_decode(*args, need, 0x7000, None) == w4.W4_EALIGN
+
+
+def test_argmax_argument_checks_return_before_device_work():
+    """w4_argmax_f16 validates on the host and enqueues nothing on an error
+    (the addresses below are never dereferenced)."""
+    import ctypes
+    import w4a16_paged_kv_amd as w4
+    lib = w4.lib()
+    assert w4.w4_argmax_workspace_bytes(0, 10) == 0
+    assert w4.w4_argmax_workspace_bytes(1, 0) == 0
+    assert w4.w4_argmax_workspace_bytes(2, 152064) == 2 * 64 * 8
+    assert w4.w4_argmax_workspace_bytes(3, 7) == 3 * 8
+    a = 1 << 20                                   # aligned fake addresses
+    ok = lib.w4_argmax_f16
+    assert ok(None, 1, 10, a, 64, a, None) == w4.W4_EINVAL
+    assert ok(a, 0, 10, a, 64, a, None) == w4.W4_EINVAL
+    assert ok(a, 1, 0, a, 64, a, None) == w4.W4_EINVAL
+    assert ok(a + 2, 1, 10, a, 64, a, None) == w4.W4_EALIGN
+    assert ok(a, 1, 10, a + 8, 64, a, None) == w4.W4_EALIGN
+    assert ok(a, 2, 152064, a, 2 * 64 * 8 - 1, a, None) == w4.W4_EINVAL
+    assert b"workspace" in lib.w4_last_error()

@@ -151,6 +151,8 @@ W4_EXPORT int w4_argmax_f16(const uint16_t* logits, int32_t batch, int32_t vocab
   if (!logits || !out || !workspace) return w4::fail(W4_EINVAL, "w4_argmax_f16: null pointer");
   if (batch < 1 || batch > 65535 || vocab < 1)
     return w4::fail(W4_EINVAL, "w4_argmax_f16: batch %d (1..65535) or vocab %d (>= 1)", batch, vocab);
+  if (!w4::aligned256(logits) || !w4::aligned256(workspace) || !w4::aligned256(out))
+    return w4::fail(W4_EALIGN, "w4_argmax_f16: logits, workspace or out not 256-byte aligned");
   const size_t need = w4::argmax_workspace_bytes(batch, vocab);
   if (ws_bytes < need)
     return w4::fail(W4_EINVAL, "w4_argmax_f16: workspace %zu bytes < %zu", ws_bytes, need);
