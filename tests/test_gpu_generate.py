@@ -88,17 +88,20 @@ def run_generation(dm, pool, w, p0, n, graph=True):
     return toks, to_np16(logits)
 
 
-def test_generation_matches_oracle():
-    """Two sequences, 20 steps from positions 29 and 13 (pages grow at 32, 48
-    and 16, 32; the pool ends exactly full). Teacher-forced with the GPU's
+@pytest.mark.parametrize("starts,n,wid", [([29, 13], 20, 31), ([0, 16, 5], 18, 33)])
+def test_generation_matches_oracle(starts, n, wid):
+    """20 steps from positions 29 and 13 (pages grow at 32, 48 and 16, 32),
+    or 18 steps of three sequences: one with no prior context (its first page
+    is reserved by the first step), one starting exactly on a page boundary,
+    one mid-page. The pool ends exactly full. Teacher-forced with the GPU's
     tokens, the oracle confirms every choice: the chosen token's oracle logit is
     the maximum up to the logits' tolerance, and it is the oracle's own argmax
     wherever the oracle's top two are further apart than that. The last
     step's logits and every generated K/V slot of layer 0 are checked against
     the oracle; an eager rerun gives the same tokens and bit-identical logits."""
-    n = 20
-    p0 = np.array([29, 13], dtype=np.int32)
-    w = wl.custom("gen_small", 31, SMALL, p0 + n, layers=3, lm_head=True, gamma="random")
+    p0 = np.array(starts, dtype=np.int32)
+    print(f"generation from {starts}, {n} steps", flush=True)
+    w = wl.custom("gen_small", wid, SMALL, p0 + n, layers=3, lm_head=True, gamma="random")
     dm, pool = setup_generation(w, p0)
     toks, last = run_generation(dm, pool, w, p0, n)
     print("generated", toks.T.tolist())
