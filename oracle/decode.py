@@ -3,6 +3,12 @@
 Rounding: ``r`` is IEEE binary16 round-to-nearest-even; every other operation
 is float64. With ``exact=True`` no rounding is applied anywhere (used to
 compare against the dense brute force at 1e-9).
+
+``mirror=True`` moves the rounding points: it also rounds the gate and up
+projections before SiLU and q/k before RoPE. It is an equally plausible
+fp16 reading of the pages, used only to measure how far two faithful
+placements of the roundings drift apart over a whole layer or step (the
+envelope a fused GPU computation is held to). Off by default.
 """
 from __future__ import annotations
 
@@ -177,32 +183,35 @@ def lse_merge(parts) -> np.ndarray:
 
 # ---------------------------------------------------------------- layers
 
-def qkv_stage(x: np.ndarray, w, pos: int, shape, exact: bool = False):
+def qkv_stage(x: np.ndarray, w, pos: int, shape, exact: bool = False, mirror: bool = False):
     """xn = rmsnorm(x, gamma_attn); then qkv_from_normed(xn)."""
     xn = rmsnorm(np.asarray(x, dtype=np.float64), w.attn_norm, shape.eps, exact)
-    return qkv_from_normed(xn, w, pos, shape, exact)
+    return qkv_from_normed(xn, w, pos, shape, exact, mirror)
 
 
-def qkv_from_normed(xn: np.ndarray, w, pos: int, shape, exact: bool = False):
+def qkv_from_normed(xn: np.ndarray, w, pos: int, shape, exact: bool = False, mirror: bool = False):
     """[q; k; v] = W_qkv xn (+ bias); returns (r(RoPE(q)) [Hq, D],
     r(RoPE(k)) [Hkv, D], r(v) [Hkv, D]) at position pos. q and k are rotated
-    unrounded and rounded once afterwards."""
+    unrounded and rounded once afterwards (mirror: also rounded before)."""
     sh = shape
     xn = np.asarray(xn, dtype=np.float64)
     if xn.ndim == 2:   # a batch: one position per row
         y_all = gemv_w4(w.qkv_q, w.qkv_s, xn)
-        outs = [_split_qkv(y_all[b], w, int(np.asarray(pos)[b]), sh, exact) for b in range(xn.shape[0])]
+        outs = [_split_qkv(y_all[b], w, int(np.asarray(pos)[b]), sh, exact, mirror)
+                for b in range(xn.shape[0])]
         return tuple(np.stack(t) for t in zip(*outs))
-    return _split_qkv(gemv_w4(w.qkv_q, w.qkv_s, xn), w, pos, sh, exact)
+    return _split_qkv(gemv_w4(w.qkv_q, w.qkv_s, xn), w, pos, sh, exact, mirror)
 
 
-def _split_qkv(y, w, pos, sh, exact):
+def _split_qkv(y, w, pos, sh, exact, mirror=False):
     if w.qkv_bias is not None:
         y = y + np.asarray(w.qkv_bias, dtype=np.float64)
     nq, nkv = sh.q_rows, sh.kv_rows
     q = y[:nq].reshape(sh.n_heads, sh.head_dim)
     k = y[nq:nq + nkv].reshape(sh.n_kv_heads, sh.head_dim)
     v = r16(y[nq + nkv:].reshape(sh.n_kv_heads, sh.head_dim), exact)
+    if mirror:
+        q, k = r16(q, exact), r16(k, exact)
     return rope(q, pos, sh.rope_base, exact), rope(k, pos, sh.rope_base, exact), v
 
 
@@ -213,16 +222,18 @@ def oproj_stage(x: np.ndarray, o: np.ndarray, w, exact: bool = False) -> np.ndar
     return r16(x + gemv_w4(w.o_q, w.o_s, o), exact)
 
 
-def gate_up_stage(x1: np.ndarray, w, shape, exact: bool = False) -> np.ndarray:
+def gate_up_stage(x1: np.ndarray, w, shape, exact: bool = False, mirror: bool = False) -> np.ndarray:
     """xn2 = rmsnorm(x1, gamma_mlp); then gate_up_from_normed(xn2)."""
     xn2 = rmsnorm(np.asarray(x1, dtype=np.float64), w.mlp_norm, shape.eps, exact)
-    return gate_up_from_normed(xn2, w, shape, exact)
+    return gate_up_from_normed(xn2, w, shape, exact, mirror)
 
 
-def gate_up_from_normed(xn2: np.ndarray, w, shape, exact: bool = False) -> np.ndarray:
-    """h = r(silu(W_gate xn2) * (W_up xn2)); g and u unrounded."""
+def gate_up_from_normed(xn2: np.ndarray, w, shape, exact: bool = False, mirror: bool = False) -> np.ndarray:
+    """h = r(silu(W_gate xn2) * (W_up xn2)); g and u unrounded (mirror: rounded)."""
     gu = gemv_w4(w.gate_up_q, w.gate_up_s, np.asarray(xn2, dtype=np.float64))
     g, u = gu[..., :shape.ffn], gu[..., shape.ffn:]
+    if mirror:
+        g, u = r16(g, exact), r16(u, exact)
     return r16(silu(g) * u, exact)
 
 
@@ -233,7 +244,8 @@ def down_stage(x1: np.ndarray, h: np.ndarray, w, exact: bool = False) -> np.ndar
 
 
 def decode_layer(x: np.ndarray, w, k_pool: np.ndarray, v_pool: np.ndarray,
-                 page_table_row: np.ndarray, ctx: int, shape, exact: bool = False) -> np.ndarray:
+                 page_table_row: np.ndarray, ctx: int, shape, exact: bool = False,
+                 mirror: bool = False) -> np.ndarray:
     """One decoder layer for one sequence; returns the new residual x [H] and
     updates the (float64) pools in place with the token's K and V.
 
@@ -247,13 +259,14 @@ def decode_layer(x: np.ndarray, w, k_pool: np.ndarray, v_pool: np.ndarray,
       xn2 = rmsnorm(x1, gamma_mlp)
       h = r(silu(W_gate xn2) * (W_up xn2))
       return r(x1 + W_down h)
+    (mirror: g, u and the pre-RoPE q, k rounded too)
     """
     pos = ctx - 1
-    q, k, v = qkv_stage(x, w, pos, shape, exact)
+    q, k, v = qkv_stage(x, w, pos, shape, exact, mirror)
     kv_write(k_pool, v_pool, page_table_row, pos, k, v)
     o = attention_decode(q, k_pool, v_pool, page_table_row, ctx, exact)
     x1 = oproj_stage(x, o, w, exact)
-    h = gate_up_stage(x1, w, shape, exact)
+    h = gate_up_stage(x1, w, shape, exact, mirror)
     return down_stage(x1, h, w, exact)
 
 

@@ -22,7 +22,7 @@ def pools_f64(w: "wl.Workload", layer: int) -> Tuple[np.ndarray, np.ndarray]:
 
 def layer_batch(w: "wl.Workload", layer: int, x_in: np.ndarray,
                 pools: Optional[Tuple[np.ndarray, np.ndarray]] = None,
-                weights=None, exact: bool = False):
+                weights=None, exact: bool = False, mirror: bool = False):
     """Run one layer for every sequence of the batch. Returns (x_out [B, H],
     k_pool, v_pool) with the pools (float64) holding the written slots."""
     sh = w.shape
@@ -30,7 +30,7 @@ def layer_batch(w: "wl.Workload", layer: int, x_in: np.ndarray,
     kp, vp = pools if pools is not None else pools_f64(w, layer)
     out = np.empty((w.batch, sh.hidden), dtype=np.float64)
     for b in range(w.batch):
-        out[b] = od.decode_layer(x_in[b], lw, kp, vp, w.page_tables[b], int(w.ctx_lens[b]), sh, exact)
+        out[b] = od.decode_layer(x_in[b], lw, kp, vp, w.page_tables[b], int(w.ctx_lens[b]), sh, exact, mirror)
     return out, kp, vp
 
 
@@ -59,7 +59,8 @@ def lm_head_rows(w: "wl.Workload", xf: np.ndarray, rows: Optional[np.ndarray] = 
 
 
 def step(w: "wl.Workload", layers: Optional[int] = None, logits_rows: Optional[np.ndarray] = None,
-         keep_residuals: bool = False, progress=None, exact: bool = False) -> Dict[str, np.ndarray]:
+         keep_residuals: bool = False, progress=None, exact: bool = False,
+         mirror: bool = False) -> Dict[str, np.ndarray]:
     """Full decode step: x = E[token]; decoder layers; final RMSNorm; lm_head.
 
     Returns {"logits": [B, n_rows], "x_final": [B, H], "residuals": [L+1, B, H]?}.
@@ -71,7 +72,7 @@ def step(w: "wl.Workload", layers: Optional[int] = None, logits_rows: Optional[n
     x = wl.embedding_rows(w.workload_id, sh, tokens).astype(np.float64)
     res = [x.copy()] if keep_residuals else None
     for l in range(nl):
-        x, _, _ = layer_batch(w, l, x, exact=exact)
+        x, _, _ = layer_batch(w, l, x, exact=exact, mirror=mirror)
         if keep_residuals:
             res.append(x.copy())
         if progress:

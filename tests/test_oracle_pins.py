@@ -170,6 +170,108 @@ def test_silu_limits():
     assert od.silu(1.0) == pytest.approx(1 / (1 + math.exp(-1)), rel=1e-15)
 
 
+# ------------------------------------------------------------------ rounding placement
+# Where the fp16 roundings sit (RMSNorm and lm_head "kept in FP16", fp16
+# activations: "How to build your own LLM runtime from scratch",
+# Architectural decisions and optimizations). The reading: one rounding per
+# stored tensor -- r(RMSNorm(x)) as a whole, v rounded, q and k rotated
+# unrounded and rounded once after RoPE, gate and up unrounded before SiLU,
+# h = r(silu(g) u), each residual add x + W y rounded once. Each hand example
+# below has inputs chosen (exact binary fractions) so that moving one rounding
+# changes the fp16 result; the expected values were worked out to 60 digits
+# (decimal arithmetic, cos 1 and sin 1 by their series) and are written here
+# as literals, with the value the other placement would give beside them.
+
+def _hand_layer(hidden, qkv_rows=None, gate_up=None, o=None, down=None):
+    """LayerWeights of a hand example: each given matrix as (codes, scales)."""
+    z = lambda n, k: (np.zeros((n, k), np.int8), np.zeros((n, 1), np.float16))
+    qkv = qkv_rows or z(6, hidden)
+    gu = gate_up or z(2, hidden)
+    oo = o or z(hidden, 2)
+    dd = down or z(hidden, 2)
+    one = np.ones(hidden, np.float16)
+    return wl.LayerWeights(np.asarray(qkv[0], np.int8), np.asarray(qkv[1], np.float16),
+                           np.asarray(oo[0], np.int8), np.asarray(oo[1], np.float16),
+                           np.asarray(gu[0], np.int8), np.asarray(gu[1], np.float16),
+                           np.asarray(dd[0], np.int8), np.asarray(dd[1], np.float16), one, one)
+
+
+HAND = wl.Shape(hidden=2, n_heads=1, n_kv_heads=1, head_dim=2, ffn=1, vocab=1, n_layers=1)
+
+
+def test_rounding_q_k_rotated_unrounded_v_rounded_once():
+    """xn = (1, 2^-13). q = k = (a, b) with a = 1 + 5 2^-13 (not an fp16 value;
+    r(a) = 1 + 2^-10) and b = 0.6416015625; v = (a, 2^-13). D = 2 and pos = 1,
+    so the one RoPE pair turns by 1 radian: q'_0 = a cos 1 - b sin 1 =
+    7.4292...e-4 cancels, and rounding a first would move it by ~400 ulps."""
+    codes = [[1, 5], [1, 0], [1, 5], [1, 0], [1, 5], [0, 1]]
+    scales = [[1.0], [0.6416015625], [1.0], [0.6416015625], [1.0], [1.0]]
+    lw = _hand_layer(2, qkv_rows=(codes, scales))
+    xn = np.array([1.0, 2.0 ** -13])
+    q, k, v = od.qkv_from_normed(xn, lw, 1, HAND)
+    rotated = [0.0007429122924804688, 1.1884765625]    # r(a cos1 - b sin1), r(b cos1 + a sin1)
+    assert q.tolist() == [rotated] and k.tolist() == [rotated]
+    assert v.tolist() == [[1.0009765625, 2.0 ** -13]]   # r(a) = 1 + 2^-10
+    # the other placement (q, k rounded before RoPE) gives a different q'_0
+    qm, km, vm = od.qkv_from_normed(xn, lw, 1, HAND, mirror=True)
+    assert qm.tolist() == [[0.0009407997131347656, 1.1884765625]] and km.tolist() == qm.tolist()
+    assert vm.tolist() == v.tolist()
+
+
+def test_rounding_gate_and_up_unrounded_before_silu():
+    """xn2 = (1.25, 2^-9); gate codes (-8, -6), up codes (6, 5), scales 1:
+    g = -10.01171875 (r(g) = -10.015625), u = 7.509765625 (r(u) = 7.5078125).
+    h = r(silu(g) u) with silu(g) = g / (1 + e^-g) = -4.4921...e-4."""
+    lw = _hand_layer(2, gate_up=([[-8, -6], [6, 5]], [[1.0], [1.0]]))
+    xn2 = np.array([1.25, 2.0 ** -9])
+    h = od.gate_up_from_normed(xn2, lw, HAND)
+    assert h.tolist() == [-0.0033740997314453125]
+    # g rounded first: seven fp16 steps away (-0.003360748291015625); u
+    # rounded first: one step (-0.0033721923828125); both rounded (the mirror)
+    assert od.gate_up_from_normed(xn2, lw, HAND, mirror=True).tolist() == [-0.003360748291015625]
+
+
+@pytest.mark.parametrize("stage", ["oproj", "down"])
+def test_rounding_residual_add_rounds_once(stage):
+    """x = 1, W y = 2^-11 + 2^-24 (codes (1, 1), scale 1, y = (2^-11, 2^-24)).
+    One rounding of x + W y = 1 + 2^-11 + 2^-24 (just past the tie) gives
+    1 + 2^-10; rounding W y first (to 2^-11) would leave a tie that rounds to
+    even, 1.0."""
+    w = ([[1, 1]], [[1.0]])
+    lw = _hand_layer(1, o=w, down=w)
+    x = np.array([1.0])
+    y = np.array([2.0 ** -11, 2.0 ** -24])
+    out = od.oproj_stage(x, y, lw) if stage == "oproj" else od.down_stage(x, y, lw)
+    assert out.tolist() == [1.0009765625]
+
+
+def test_rounding_rmsnorm_rounds_once():
+    """x = (3, 4), eps = 0: x / rms = (3, 4) / sqrt(12.5) = (0.84852.., 1.13137..);
+    times gamma = 0.513671875 and rounded once: (0.435791015625, 0.5810546875).
+    Rounding x / rms first would give (0.43603515625, 0.58154296875)."""
+    g = np.full(2, 0.513671875)
+    assert od.rmsnorm(np.array([3.0, 4.0]), g, 0.0).tolist() == [0.435791015625, 0.5810546875]
+
+
+def test_mirror_is_off_by_default_and_exact_mode_ignores_it():
+    """mirror only adds roundings: in exact mode it changes nothing, and on a
+    real layer the two placements stay within a few fp16 steps of each other."""
+    w = wl.custom("mirror", 92, TINY7, [40], gamma="random")
+    lw = w.layer(0, bias=True)
+    x = w.x_in()[0].astype(np.float64)
+    outs = {}
+    for exact in (True, False):
+        for mirror in (False, True):
+            kp, vp = (a.astype(np.float64) for a in w.kv(0))
+            outs[exact, mirror] = od.decode_layer(x, lw, kp, vp, w.page_tables[0], 40, TINY7, exact, mirror)
+    assert np.array_equal(outs[True, False], outs[True, True])
+    ref = outs[True, False]
+    rms = np.sqrt((ref ** 2).mean())
+    for mirror in (False, True):   # fp16 rounding of intermediates only: small against the outputs' scale
+        assert np.abs(outs[False, mirror] - ref).max() <= 1e-2 * rms
+    assert not np.array_equal(outs[False, False], outs[False, True])
+
+
 # ------------------------------------------------------------------ attention
 
 def _pool_from_logical(k_log, v_log, perm):
