@@ -22,16 +22,31 @@ def pools_f64(w: "wl.Workload", layer: int) -> Tuple[np.ndarray, np.ndarray]:
 
 def layer_batch(w: "wl.Workload", layer: int, x_in: np.ndarray,
                 pools: Optional[Tuple[np.ndarray, np.ndarray]] = None,
-                weights=None, exact: bool = False, mirror: bool = False):
-    """Run one layer for every sequence of the batch. Returns (x_out [B, H],
-    k_pool, v_pool) with the pools (float64) holding the written slots."""
+                weights=None, exact: bool = False, mirror: bool = False,
+                rows: Optional[np.ndarray] = None):
+    """Run one layer for the sequences `rows` of the batch (default: all);
+    x_in [len(rows), H]. Returns (x_out [len(rows), H], k_pool, v_pool) with
+    the pools (float64) holding the written slots.
+
+    The steps of decode.decode_layer, each applied to the whole batch at once
+    where it is per-row (RMSNorm, projections, RoPE, SiLU-mul, residuals) and
+    per sequence for the page writes and the attention; every sequence owns
+    its pages and slots, so writing all new K/V before any attention equals
+    running the sequences one after another."""
     sh = w.shape
     lw = weights if weights is not None else w.layer(layer)
     kp, vp = pools if pools is not None else pools_f64(w, layer)
-    out = np.empty((w.batch, sh.hidden), dtype=np.float64)
-    for b in range(w.batch):
-        out[b] = od.decode_layer(x_in[b], lw, kp, vp, w.page_tables[b], int(w.ctx_lens[b]), sh, exact, mirror)
-    return out, kp, vp
+    rows = np.arange(w.batch) if rows is None else np.asarray(rows)
+    x = np.asarray(x_in, dtype=np.float64).reshape(len(rows), sh.hidden)
+    pos = w.positions[rows]
+    q, k, v = od.qkv_stage(x, lw, pos, sh, exact, mirror)
+    for i, b in enumerate(rows):
+        od.kv_write(kp, vp, w.page_tables[b], int(pos[i]), k[i], v[i])
+    o = np.stack([od.attention_decode(q[i], kp, vp, w.page_tables[b], int(w.ctx_lens[b]), exact)
+                  for i, b in enumerate(rows)])
+    x1 = od.oproj_stage(x, o.reshape(len(rows), -1), lw, exact)
+    h = od.gate_up_stage(x1, lw, sh, exact, mirror)
+    return od.down_stage(x1, h, lw, exact), kp, vp
 
 
 def attention_batch(w: "wl.Workload", q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,

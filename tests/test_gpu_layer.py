@@ -3,7 +3,8 @@ o-proj + residual, gate/up SiLU-mul, down + residual) against the oracle.
 
 Two kinds of check: operation by operation with the GPU's own inputs fed to
 each oracle stage (tests/staged.py; isolates each kernel), and the whole
-layer end to end where the result is insensitive enough to compare directly.
+layer end to end: element by element where the result is insensitive
+enough, else within the envelope of the oracle's two fp16 placements.
 """
 import os
 
@@ -14,7 +15,7 @@ import torch
 import workloads as wl
 from oracle import runs
 from tests.gpu_util import assert_close, to_np16
-from tests.staged import staged_layer
+from tests.staged import check_envelope, staged_layer
 from workloads.device import DeviceModel, to_dev, v_pages_host
 
 pytestmark = pytest.mark.gpu
@@ -77,20 +78,19 @@ def test_layer_full_shape_staged():
     staged(wl.layer_full())
 
 
-def test_layer_full_shape_end_to_end_rate():
+def test_layer_full_shape_end_to_end_envelope():
     """Whole layer against the oracle's own chain. A 1-ulp difference in an
-    intermediate fp16 rounding can reach an output that cancels to near zero,
-    so here the share of outputs within tolerance is reported and bounded."""
+    intermediate fp16 rounding can reach an output that cancels to near
+    zero, so the GPU is held to the envelope of two faithful placements:
+    it may disagree with the oracle no more than the oracle's mirror
+    placement does (share outside the tolerance and largest error)."""
     w = wl.layer_full()
     dm = DeviceModel(w)
     got = run_layer(dm, w.x_in())
-    ref, _, _ = runs.layer_batch(w, 0, w.x_in().astype(np.float64))
-    err = np.abs(got.astype(np.float64) - ref)
-    ok = err <= 2e-3 + 1e-2 * np.abs(ref)
-    print(f"layer_full end to end: {ok.mean() * 100:.2f}% within tolerance, max err {err.max():.3g}, "
-          f"rms output {np.sqrt((ref ** 2).mean()):.3g}")
-    assert ok.mean() > 0.9
-    assert err.max() < 1e-2 * np.sqrt((ref ** 2).mean())
+    x = w.x_in().astype(np.float64)
+    ref, _, _ = runs.layer_batch(w, 0, x)
+    mir, _, _ = runs.layer_batch(w, 0, x, mirror=True)
+    check_envelope(got, ref, mir, "layer_full x_out")
 
 
 @pytest.mark.parametrize("ctx", [[1], [17], [33, 64, 7], [100, 1, 48, 200, 16, 31, 2, 90]])

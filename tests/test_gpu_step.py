@@ -34,21 +34,10 @@ def step(dm, graph=True, inputs=None):
 def test_small_step_matches_oracle(ctx):
     """Every operation of all three layers, the final norm and every lm_head
     row against its oracle stage (GPU inputs fed in), decode_step bit-identical
-    to that op-by-op chain; then the whole step against the oracle's own chain,
-    where a 1-ulp difference in an intermediate fp16 rounding can reach a logit
-    that cancels to near zero: the share within tolerance and the largest
-    error relative to the logits' rms are bounded instead."""
+    to that op-by-op chain and, end to end, within the envelope of the
+    oracle's two fp16 placements."""
     full_check(wl.custom("small_step", 30, SMALL, ctx, layers=3, lm_head=True, gamma="random"),
-               check_layers={0, 1, 2}, n_rows=SMALL.vocab)
-    dm = small_model(ctx)
-    got = step(dm, graph=False).astype(np.float64)
-    ref = runs.step(dm.w)["logits"]
-    err = np.abs(got - ref)
-    ok = err <= 2e-3 + 1e-2 * np.abs(ref)
-    print(f"small step {ctx} end to end: {ok.mean() * 100:.2f}% of logits within tolerance, "
-          f"max err {err.max():.3g}, rms logit {np.sqrt((ref ** 2).mean()):.3g}")
-    assert ok.mean() > 0.99
-    assert err.max() < 1e-2 * np.sqrt((ref ** 2).mean())
+               check_layers={0, 1, 2}, chains=True)
 
 
 def test_graph_equals_eager_and_replays_are_deterministic():

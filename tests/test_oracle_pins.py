@@ -418,6 +418,24 @@ def test_three_step_stateful_run_crossing_a_page():
         x = got / 8.0
 
 
+def test_batched_layer_equals_sequences_one_by_one():
+    """runs.layer_batch applies the per-row stages to the whole batch at once:
+    it must equal decode_layer run for each sequence in turn (exact mode to
+    1e-12, and the written page slots), including ragged contexts."""
+    from oracle import runs
+    w = wl.custom("tinyb", 93, TINY7, [33, 5, 16, 40], gamma="random")
+    lw = w.layer(0, bias=True)
+    x = w.x_in().astype(np.float64)
+    got, kp, vp = runs.layer_batch(w, 0, x, weights=lw, exact=True)
+    kp2, vp2 = (a.astype(np.float64) for a in w.kv(0))
+    for b in range(w.batch):
+        ref = od.decode_layer(x[b], lw, kp2, vp2, w.page_tables[b], int(w.ctx_lens[b]), TINY7, exact=True)
+        assert np.allclose(got[b], ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(kp, kp2, rtol=0, atol=1e-12) and np.allclose(vp, vp2, rtol=0, atol=1e-12)
+    sub, _, _ = runs.layer_batch(w, 0, x[[3, 1]], weights=lw, exact=True, rows=[3, 1])
+    assert np.allclose(sub, got[[3, 1]], rtol=1e-12, atol=1e-12)
+
+
 def test_layer_outputs_are_fp16_values():
     w = wl.layer_mini()
     x = w.x_in().astype(np.float64)

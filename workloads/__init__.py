@@ -39,6 +39,7 @@ K_CACHE, V_CACHE = 6, 7
 X_IN, PAGE_TABLE, CTX, TOKENS = 8, 9, 10, 11
 EMBED, LM_HEAD, FINAL_NORM = 12, 13, 14
 Q_ATTN, QKV_BIAS = 15, 16
+FORCED_ROW = 17
 
 ROW_CHUNK = 4096   # row chunk of the per-chunk streams (embedding, lm_head)
 
@@ -240,6 +241,15 @@ class Workload:
         """Attention-only workloads: queries fp16 [B, Hq, D]."""
         sh = self.shape
         return f16_normal(rng(self.workload_id, 0, Q_ATTN), (self.batch, sh.n_heads, sh.head_dim))
+
+
+def forced_rows(workload_id: int, layer: int, rows, hidden: int) -> np.ndarray:
+    """Finite stand-in residual rows fp16 N(0, 1) [len(rows), hidden], one
+    stream per (layer, row): fed to a layer in place of a sequence whose
+    residual stream has overflowed fp16, so that layer can still be compared
+    for that sequence (rows are independent of each other)."""
+    return np.stack([f16_normal(rng(workload_id, layer, FORCED_ROW, int(b)), hidden) for b in rows]) \
+        if len(rows) else np.zeros((0, hidden), np.float16)
 
 
 def _make(name, wid, shape, ctx_lens, layers, lm_head, gamma="ones") -> Workload:
