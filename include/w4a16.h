@@ -139,6 +139,10 @@ int pack_weights_f16(const uint16_t* w, int32_t n, int32_t k, void* out, size_t 
  */
 typedef struct w4_kv_pool w4_kv_pool;
 
+/* Handles (pools here, models below) are tracked while live: a call with a
+ * destroyed handle returns W4_ESTATE (counters: -1) and touches nothing, and
+ * destroying a handle twice, or NULL, does nothing. (An address the library
+ * later hands out again to a new handle is that new handle.) */
 int  kv_pool_create(int32_t num_pages, int32_t max_seqs, w4_kv_pool** out);
 void kv_pool_destroy(w4_kv_pool* pool);
 /* Allocate n pages into out_ids[n] (host). All or nothing: W4_ENOPAGES if
@@ -209,29 +213,26 @@ typedef struct w4_model w4_model;
 size_t w4_workspace_bytes(const w4_config* cfg, int32_t max_batch, int32_t max_pages_per_seq);
 
 /* Bind weights, KV cache and workspace (all caller-owned device memory; the
- * pointers are kept, not copied) into a model. Zero-fills the workspace
+ * pointers are kept, not copied) into a model: the KV cache and activation
+ * buffers are allocated once, up front, by the caller [H100-guide], and
+ * every pointer must be 256-byte aligned ([H100-bug], Bug 2: misaligned
+ * intermediate buffers). The model is the decoder of [RT-arch]: per layer
+ * an RMSNorm, the INT4 qkv projection, GQA attention over the paged cache,
+ * the INT4 o projection, a second RMSNorm and the INT4 gate/up/down
+ * projections, then an FP16 RMSNorm and lm_head. Zero-fills the workspace
  * with a kernel on the default stream and waits for it. num_pages and
- * max_pages_per_seq are at most 2^26 (W4_EINVAL otherwise). */
+ * max_pages_per_seq are at most 2^26 (W4_EINVAL otherwise). W4_EHIP if the
+ * HIP runtime fails (no handle is returned). */
 int  w4_model_create(const w4_config* cfg, const w4_weights* weights, void* kv_cache,
                      int32_t num_pages, void* workspace, size_t ws_bytes, int32_t max_batch,
                      int32_t max_pages_per_seq, w4_model** out);
+/* Releases the model's captured graphs and its handle (the caller's device
+ * memory is untouched). NULL or an already destroyed model: no-op. */
 void w4_model_destroy(w4_model* model);
 /* 1: decode_step captures its kernel sequence into a hipGraph on first use
  * (per batch size and output/input pointers) and replays it afterwards
  * [H100-graph]; 0: launch kernel by kernel. Default 1. */
 int  w4_set_graph(w4_model* model, int enabled);
-/* 1: batch-1 decode_step runs each decoder layer as one persistent launch
- * (one 1024-thread workgroup per CU; the layer's five operations meet at
- * grid barriers, the next operation's first weight loads issued before each
- * barrier), with the per-operation kernels' device code and work split, so
- * the results are bit-identical to mode 0; batch > 1 and decode_layer always
- * use the per-operation kernels. Replaces the step's CUDA-graph capture
- * (the step is then 30 launches). W4_EINVAL if this configuration has no
- * persistent instantiation or the device cannot keep one such workgroup on
- * every CU. Default 0. A barrier wait is bounded: a launch whose workgroups
- * lose each other counts one device error (w4_device_errors) instead of
- * hanging. */
-int  w4_set_persistent(w4_model* model, int enabled);
 
 /* One decode step for `batch` sequences. tokens, positions, ctx_lens: host
  * int32 [batch]; page_tables: host int32 [batch * max_pages_per_seq].
@@ -267,8 +268,11 @@ int  w4_validate_step(const w4_config* cfg, int32_t num_pages, int32_t max_batch
 int64_t w4_device_errors(w4_model* model, void* stream);
 
 /* One decoder layer (no embedding, no lm_head): x_out = layer(x_in), with the
- * KV write of every sequence. x_in, x_out: device fp16 [batch][H] (may be
- * the same buffer). positions/page_tables/ctx_lens: host, as decode_step. */
+ * KV write of every sequence -- the layer of [RT-arch] (FP16 RMSNorm, INT4
+ * group-128 projections, GQA 7:1 attention over 16-token pages through the
+ * page table [H100-kv]). x_in, x_out: device fp16 [batch][H] (may be the
+ * same buffer). positions/page_tables/ctx_lens: host, validated and staged
+ * as for decode_step (W4_ERANGE / W4_EINVAL / W4_EALIGN as there). */
 int  decode_layer(w4_model* model, int32_t layer, const uint16_t* x_in, uint16_t* x_out,
                   const int32_t* positions, const int32_t* page_tables, const int32_t* ctx_lens,
                   int32_t batch, void* stream);

@@ -80,3 +80,18 @@ def test_device_inputs_match_host_inputs():
     torch.cuda.synchronize()
     assert np.array_equal(a.view(np.uint16), to_np16(logits).view(np.uint16))
     assert dm.model.w4_device_errors() == 0
+
+
+def test_destroyed_model_handle_is_rejected():
+    """A destroyed model is refused (W4_ESTATE, -1 for the error count), and a
+    second destroy does nothing."""
+    import w4a16_paged_kv_amd as w4
+    dm = small_model([10])
+    h = dm.model.handle
+    lib = w4.lib()
+    lib.w4_model_destroy(h)
+    dm.model.handle = None
+    assert lib.w4_set_graph(h, 1) == w4.W4_ESTATE
+    assert lib.w4_device_errors(h, None) == -1
+    assert lib.w4_model_buffer(h, w4.BUF_X, None) is None
+    lib.w4_model_destroy(h)

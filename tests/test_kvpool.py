@@ -1,4 +1,6 @@
 """KV page pool against a plain Python set model (CPU only)."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -79,3 +81,20 @@ def test_sequence_growth_and_page_table():
 def test_cache_bytes():
     cfg = w4.make_config(3584, 28, 4, 128, 18944, 152064, 28)
     assert w4.kv_cache_bytes(cfg, 128) == 2 * 28 * 128 * 4 * 16 * 128 * 2
+
+
+def test_destroyed_pool_is_rejected_and_double_destroy_is_harmless():
+    """A destroyed handle is not used: calls report W4_ESTATE (or -1 for the
+    counters) instead of reading freed memory, and destroying twice is a
+    no-op."""
+    lib = w4.lib()
+    h = ctypes.c_void_p()
+    assert lib.kv_pool_create(16, 2, ctypes.byref(h)) == w4.W4_OK
+    lib.kv_pool_destroy(h)
+    ids = np.zeros(4, np.int32)
+    assert lib.kv_alloc_pages(h, 2, ids.ctypes.data) == w4.W4_ESTATE
+    assert lib.kv_free_count(h) == -1
+    assert lib.kv_seq_reserve(h, 0, 20) == w4.W4_ESTATE
+    assert lib.kv_seq_pages(h, 0) == -1
+    lib.kv_pool_destroy(h)
+    lib.kv_pool_destroy(None)

@@ -16,7 +16,9 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
+# W4A16_LIB selects another build of the same library (the host-sanitizer
+# build the CPU tests run under); by default the in-tree libw4a16.so.
+LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libw4a16.so")
 
 W4_OK, W4_EINVAL, W4_ERANGE, W4_EALIGN, W4_ENOPAGES, W4_EHIP, W4_ESTATE = range(7)
 ERROR_NAMES = {1: "EINVAL", 2: "ERANGE", 3: "EALIGN", 4: "ENOPAGES", 5: "EHIP", 6: "ESTATE"}
@@ -71,7 +73,6 @@ _SIGS = {
                                 c_size_t, c_int32, c_int32, POINTER(c_void_p)]),
     "w4_model_destroy": (None, [c_void_p]),
     "w4_set_graph": (c_int, [c_void_p, c_int]),
-    "w4_set_persistent": (c_int, [c_void_p, c_int]),
     "decode_step": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     "decode_step_device": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
     "w4_device_errors": (c_int64, [c_void_p, c_void_p]),
@@ -284,9 +285,6 @@ class Model:
 
     def w4_set_graph(self, enabled: bool) -> None:
         _check(lib().w4_set_graph(self.handle, int(enabled)))
-
-    def w4_set_persistent(self, enabled: bool) -> None:
-        _check(lib().w4_set_persistent(self.handle, int(enabled)))
 
     def decode_step(self, tokens, positions, page_tables, ctx_lens, logits, stream=None) -> None:
         """Host int32 arrays (tokens/positions/ctx_lens [B], page_tables [B, max_pages]) -> logits."""

@@ -1,5 +1,4 @@
-// Paged-attention decode as device code (one work item on one workgroup),
-// shared by the attention kernel and the persistent layer kernel.
+// Paged-attention decode as device code (one work item on one workgroup).
 //
 // The KV cache is split into 16-token pages addressed through a page table
 // ("Building a Custom LLM Inference Runtime on H100", The KV Cache and

@@ -7,8 +7,9 @@
 //
 // Batch 1 is a bandwidth-bound GEMV. It still runs on the matrix cores: the
 // packed block is laid out as the B operand of v_mfma_f32_16x16x32_f16, the
-// dequantisation is exact with one AND-OR and one packed subtract per weight
-// pair, and the MFMA does the multiply-accumulate (gemv_b1.h). Batches 2..16
+// codes dequantise exactly with one AND-OR and one packed subtract per weight
+// pair (half of them as 16q, met by activations staged divided by 16), and
+// the MFMA does the multiply-accumulate (gemv_b1.h). Batches 2..16
 // turn each projection into a skinny dense contraction on the same
 // instruction.
 #include <hip/hip_runtime.h>
@@ -75,9 +76,8 @@ __device__ __forceinline__ void store_xs(const uint16_t* xs, int k, uint16_t* ds
 // ------------------------------------------------------------ batch 1
 // One launch per projection: S wavefronts per tile on TW tiles (S TW <= 8),
 // or kRangeWaves contiguous runs when S == 1; any further wavefronts only
-// help stage the activations. IT activation words per thread: the same
-// decomposition and arithmetic as the projection phases of the persistent
-// layer kernel. The activation loads go out first, then the first weight
+// help stage the activations. IT activation words per thread. The
+// activation loads go out first, then the first weight
 // batch, so the prologue waits for the activations only (the vector-memory
 // counter is in order).
 template <int EPI, int S, int IT>
@@ -549,8 +549,7 @@ static void launch_b1(const GemvArgs& a, int tw, int nt, hipStream_t s) {
 
 // The workgroup is its working wavefronts (S * TW, or kRangeWaves when
 // S == 1; at least four), unless the activation row then needs more than
-// kMaxIt words per thread; then it has kB1Threads threads like the
-// persistent kernel's phases. The staged
+// kMaxIt words per thread; then it has kB1Threads threads. The staged
 // row and every product are the same either way, and so is the RMSNorm sum
 // when the row fits one pass of the threads (8 * nt >= k: each thread then
 // holds one word, the words past k are zero).

@@ -1,6 +1,5 @@
-// Batch-1 W4A16 GEMV as device code: the pieces the per-projection kernel
-// and the persistent layer kernel share (activation staging, the MFMA block
-// product, fused epilogues and the per-wavefront streaming worker).
+// Batch-1 W4A16 GEMV as device code: activation staging, the MFMA block
+// product, fused epilogues and the per-wavefront streaming worker.
 //
 // Weights: symmetric group-wise INT4, group 128 along the input dimension,
 // dequantised value q * s ("How to build your own LLM runtime from
@@ -10,8 +9,7 @@
 // Activations and outputs cross workgroups (and XCDs, whose L2 caches are
 // not coherent with each other): every activation load and every output
 // store here is device-coherent (sc1), which costs nothing measurable for
-// these few kilobytes and lets the same code run inside one launch that
-// spans several operations.
+// these few kilobytes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -195,12 +193,15 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i,
 // l >> 4), so batch 1 runs on the matrix cores too: A carries the activation
 // row (A rows 1..15 are don't-care) and D row 0 comes out in lanes 0..15.
 //
-// Dequantisation stays exact: 0x6400 | u is 1024 + u in fp16 (ulp 1), so
-// OR-ing a nibble pair masked with 0x000F000F into 0x64006400 and
+// The dequantised codes are exact: 0x6400 | u is 1024 + u in fp16 (ulp 1),
+// so OR-ing a nibble pair masked with 0x000F000F into 0x64006400 and
 // subtracting 1032 gives (q, q'); the pair four bits higher (mask 0x00F000F0)
 // gives 16q after subtracting 1152, and the activations paired with those
-// slots are staged divided by 16. One AND-OR and one packed subtract per
-// weight pair; the multiply-accumulate runs on the matrix cores.
+// slots are staged divided by 16. That quotient is exact for |x| >= 2^-10;
+// below, x / 16 is an fp16 subnormal rounded to a multiple of 2^-24 (an
+// error of at most 2^-25 per activation, before the 16q weight and the
+// scale). One AND-OR and one packed subtract per weight pair; the
+// multiply-accumulate runs on the matrix cores.
 //
 // A workgroup of WAVES wavefronts covers WAVES/S tiles; the S wavefronts of a
 // tile take its 128-column groups round-robin (K split inside the workgroup),
@@ -256,7 +257,8 @@ __device__ __forceinline__ uint32_t quad_perm(uint32_t v, int ctrl_is_odd) {
 
 // Slot group sg = wd of the natural word xv held by this lane (e = wd % 2),
 // built from the words of its 4-lane quad; the slots of odd r are divided
-// by 16 (exact fp16 scaling). All four lanes of the quad must take part.
+// by 16 (exact for |x| >= 2^-10, rounded to the fp16 subnormal grid below).
+// All four lanes of the quad must take part.
 __device__ __forceinline__ u4_t slot_word(const u4_t xv, int e) {
   const h2_t sc = e ? (h2_t){(_Float16)0.0625f, (_Float16)0.0625f} : (h2_t){(_Float16)1.0f, (_Float16)1.0f};
   // words j0 (lanes {0,0,2,2} of the quad) and j0 + 1 (lanes {1,1,3,3})
@@ -273,8 +275,8 @@ __device__ __forceinline__ u4_t slot_word(const u4_t xv, int e) {
 }
 
 // Stages the row: with NORM it becomes fp16(x * rsqrt(mean(x^2) + eps) *
-// gamma) (RMSNorm in FP16); the slots of odd r are divided by 16 (exact
-// fp16 scaling). The natural-order (normalised) row also goes to xn_out if
+// gamma) (RMSNorm in FP16); the slots of odd r are divided by 16 (see
+// slot_word). The natural-order (normalised) row also goes to xn_out if
 // given. Ends with a barrier. Requires kpad <= 8 * IT * NT, NT <= 1024 and
 // red[16] 16-byte aligned.
 template <int IT, bool NORM>
@@ -398,9 +400,9 @@ __device__ __forceinline__ QkvPre qkv_pre(const GemvArgs& a, int vb, int tw) {
   return p;
 }
 
-// Threads of a batch-1 GEMV workgroup as a phase of the persistent layer
-// kernel; the per-projection launch runs only the S * TW working
-// wavefronts (same decomposition, same results).
+// Threads of a batch-1 GEMV workgroup whose activation row needs more than
+// kMaxIt words per thread at S * TW wavefronts (same decomposition, same
+// results).
 constexpr int kB1Threads = 1024;
 
 // Batch-1 work split. TW = ceil(tiles / 256) tiles per workgroup, so a

@@ -5,8 +5,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <thread>
+#include <unordered_set>
 #include <vector>
 
 #include "w4_internal.h"
@@ -26,6 +28,30 @@ int fail(int code, const char* fmt, ...) {
 }
 
 void clear_error() { g_error.clear(); }
+
+// Never destroyed: handles may be released from static destructors or
+// interpreter shutdown after this file's statics would be gone.
+static std::mutex& handles_mu() {
+  static auto* m = new std::mutex;
+  return *m;
+}
+static std::unordered_set<const void*>& handles() {
+  static auto* s = new std::unordered_set<const void*>;
+  return *s;
+}
+void handle_register(const void* h) {
+  std::lock_guard<std::mutex> g(handles_mu());
+  handles().insert(h);
+}
+bool handle_release(const void* h) {
+  std::lock_guard<std::mutex> g(handles_mu());
+  return handles().erase(h) > 0;
+}
+bool handle_live(const void* h) {
+  if (!h) return false;
+  std::lock_guard<std::mutex> g(handles_mu());
+  return handles().count(h) > 0;
+}
 
 // Runs f(begin, end) over [0, n) on up to hardware_concurrency threads.
 template <class F>
@@ -208,12 +234,11 @@ struct w4_kv_pool {
   std::vector<int32_t> free_list;        // stack of free page ids
   std::vector<int32_t> owner;            // per page: -2 free, -1 allocated, >= 0 sequence
   std::vector<std::vector<int32_t>> seqs;
-  bool alive = true;
 };
 
 static constexpr int32_t kFree = -2, kLoose = -1;
 
-static bool pool_ok(const w4_kv_pool* p) { return p && p->alive; }
+static bool pool_ok(const w4_kv_pool* p) { return handle_live(p); }
 
 W4_EXPORT int kv_pool_create(int32_t num_pages, int32_t max_seqs, w4_kv_pool** out) {
   clear_error();
@@ -227,13 +252,13 @@ W4_EXPORT int kv_pool_create(int32_t num_pages, int32_t max_seqs, w4_kv_pool** o
   for (int32_t i = 0; i < num_pages; ++i) p->free_list[i] = num_pages - 1 - i;
   p->owner.assign(num_pages, kFree);
   p->seqs.resize(max_seqs);
+  handle_register(p);
   *out = p;
   return W4_OK;
 }
 
 W4_EXPORT void kv_pool_destroy(w4_kv_pool* p) {
-  if (!p) return;
-  p->alive = false;
+  if (!handle_release(p)) return;  // null, already destroyed or never created
   delete p;
 }
 

@@ -22,7 +22,7 @@
 namespace w4 {
 
 struct WsLayout {
-  size_t err, counters, bar, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, kpart, kcount, amax,
+  size_t err, counters, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, kpart, kcount, amax,
       total;
   int xn_stride, o_stride, h_stride, max_splits;
 };
@@ -42,7 +42,6 @@ static WsLayout ws_layout(const w4_config& c, int max_batch, int max_pages) {
   L.max_splits = ceil_div(max_pages, 4);
   L.err = take(256);
   L.counters = take((size_t)max_batch * c.n_kv_heads * 4);
-  L.bar = take(persistent_bar_words(kMaxPersistGrid) * 4);
   L.tokens = take((size_t)max_batch * 4);
   L.positions = take((size_t)max_batch * 4);
   L.ctx = take((size_t)max_batch * 4);
@@ -99,8 +98,6 @@ struct w4_model {
   uint8_t* ws = nullptr;
   WsLayout L;
   bool use_graph = true;
-  int persist_grid = 0;        // workgroups of the persistent layer kernel (0: unavailable)
-  bool use_persistent = false;
   hipStream_t cap_stream = nullptr;
   // key: batch, logits, device-input pointers (null for host inputs)
   typedef std::tuple<int, const void*, const void*, const void*, const void*, const void*> Key;
@@ -273,27 +270,6 @@ static int enqueue_op(w4_model* m, int op, int l, const uint16_t* x_in, uint16_t
   return fail(W4_EINVAL, "unknown layer op %d", op);
 }
 
-// One decoder layer (batch 1) as a single persistent launch: the same
-// kernels' device code and splits, workgroups meeting at grid barriers.
-static int enqueue_layer_persistent(w4_model* m, int l, uint16_t* x, const StepInputs& in, hipStream_t s) {
-  const w4_config& c = m->cfg;
-  LayerPhases t{};
-  t.qkv = qkv_args(m, l, x, 1);
-  t.qkv.xn_out = nullptr;
-  t.attn = attn_args(m, l, in, 1);
-  t.o = oproj_args(m, l, x, x, 1);
-  t.gate_up = gate_up_args(m, l, x, 1);
-  t.gate_up.xn_out = nullptr;
-  t.down = down_args(m, l, x, 1);
-  t.tw_q = w4_b1_split(t.qkv.tiles, t.qkv.groups).tw;
-  t.tw_o = w4_b1_split(t.o.tiles, t.o.groups).tw;
-  t.tw_g = w4_b1_split(t.gate_up.tiles, t.gate_up.groups).tw;
-  t.tw_d = w4_b1_split(t.down.tiles, t.down.groups).tw;
-  t.bar = m->at<uint32_t>(m->L.bar);
-  W4_LAUNCH(launch_persistent(t, c, m->persist_grid, s));
-  return W4_OK;
-}
-
 // Enqueues one decoder layer: x_out = layer(x_in) for `batch` sequences.
 static int enqueue_layer(w4_model* m, int l, const uint16_t* x_in, uint16_t* x_out,
                          const StepInputs& in, int batch, hipStream_t s) {
@@ -364,9 +340,8 @@ static int enqueue_step(w4_model* m, const StepInputs& in, int batch, uint16_t* 
   uint16_t* x = m->at<uint16_t>(m->L.x);
   int rc0 = enqueue_plan(m, in.tokens, in, batch, s);
   if (rc0) return rc0;
-  const bool persistent = m->use_persistent && batch == 1;
   for (int l = 0; l < c.n_layers; ++l) {
-    int rc = persistent ? enqueue_layer_persistent(m, l, x, in, s) : enqueue_layer(m, l, x, x, in, batch, s);
+    int rc = enqueue_layer(m, l, x, x, in, batch, s);
     if (rc) return rc;
   }
   return enqueue_lm_head(m, x, batch, logits, s);
@@ -428,8 +403,7 @@ static StepInputs staged(w4_model* m) {
 // Runs the step eagerly or through a graph captured once per key.
 static int run_step(w4_model* m, const StepInputs& in, int batch, uint16_t* logits,
                     hipStream_t s, const void* key_inputs) {
-  // the persistent path is a handful of launches already: no capture needed
-  if (!m->use_graph || (m->use_persistent && batch == 1)) return enqueue_step(m, in, batch, logits, s);
+  if (!m->use_graph) return enqueue_step(m, in, batch, logits, s);
   w4_model::Key key(batch, logits, key_inputs ? in.tokens : nullptr,
                     key_inputs ? in.positions : nullptr, key_inputs ? in.page_tables : nullptr,
                     key_inputs ? in.ctx_lens : nullptr);
@@ -455,7 +429,7 @@ static int run_step(w4_model* m, const StepInputs& in, int batch, uint16_t* logi
 }
 
 static int check_model(const w4_model* m, int batch) {
-  if (!m) return fail(W4_ESTATE, "null model");
+  if (!handle_live(m)) return fail(W4_ESTATE, "null or destroyed model");
   if (batch < 1 || batch > m->max_batch)
     return fail(W4_EINVAL, "batch %d outside [1, %d]", batch, m->max_batch);
   return W4_OK;
@@ -532,13 +506,13 @@ W4_EXPORT int w4_model_create(const w4_config* cfg, const w4_weights* weights, v
     delete m;
     return fail(W4_EHIP, "w4_model_create: %s", hipGetErrorString(e));
   }
-  m->persist_grid = std::min(persistent_grid(m->cfg), kMaxPersistGrid);
+  handle_register(m);
   *out = m;
   return W4_OK;
 }
 
 W4_EXPORT void w4_model_destroy(w4_model* m) {
-  if (!m) return;
+  if (!handle_release(m)) return;  // null, already destroyed or never created
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   delete m;
@@ -546,17 +520,8 @@ W4_EXPORT void w4_model_destroy(w4_model* m) {
 
 W4_EXPORT int w4_set_graph(w4_model* m, int enabled) {
   clear_error();
-  if (!m) return fail(W4_ESTATE, "null model");
+  if (!handle_live(m)) return fail(W4_ESTATE, "null or destroyed model");
   m->use_graph = enabled != 0;
-  return W4_OK;
-}
-
-W4_EXPORT int w4_set_persistent(w4_model* m, int enabled) {
-  clear_error();
-  if (!m) return fail(W4_ESTATE, "null model");
-  if (enabled && m->persist_grid == 0)
-    return fail(W4_EINVAL, "w4_set_persistent: no persistent kernel for this configuration or device");
-  m->use_persistent = enabled != 0;
   return W4_OK;
 }
 
@@ -598,7 +563,7 @@ W4_EXPORT int decode_step_device(w4_model* m, const int32_t* tokens, const int32
 
 W4_EXPORT int64_t w4_device_errors(w4_model* m, void* stream) {
   clear_error();
-  if (!m) return -1;
+  if (!handle_live(m)) return -1;
   uint32_t v = 0;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return -1;
   if (hipMemcpy(&v, m->ws + m->L.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return -1;
@@ -776,7 +741,7 @@ W4_EXPORT int w4_model_run_op(w4_model* m, int32_t op, int32_t layer, int32_t ba
 }
 
 W4_EXPORT void* w4_model_buffer(w4_model* m, int32_t which, int32_t* row_stride) {
-  if (!m) return nullptr;
+  if (!handle_live(m)) return nullptr;
   const WsLayout& L = m->L;
   const w4_config& c = m->cfg;
   size_t off;

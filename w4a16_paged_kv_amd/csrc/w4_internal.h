@@ -18,6 +18,15 @@ namespace w4 {
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
+// Registry of live handles (KV pools, models): a handle is registered when
+// created and removed when destroyed, so a call with a destroyed handle is
+// refused (W4_ESTATE) instead of touching freed memory, and a second
+// destroy does nothing. An address handed out again to a new handle counts
+// as that new handle.
+void handle_register(const void* h);
+bool handle_release(const void* h);   // true if h was live (and is now removed)
+bool handle_live(const void* h);
+
 #define W4_HIP(call)                                                                     \
   do {                                                                                   \
     hipError_t e_ = (call);                                                              \
@@ -158,24 +167,6 @@ inline size_t w4_rows_kpart_floats(const RowsPlan& p, int tiles) {
 inline size_t w4_rows_kcount_words(const RowsPlan& p, int tiles) {
   return p.ch > 1 ? (size_t)ceil_div(tiles, p.tw) : 0;
 }
-
-// The persistent layer kernel (persistent.hip): one launch per decoder
-// layer, its five operations' arguments passed by value like those of the
-// per-operation kernels (the kernel reads each field from the argument
-// segment where it needs it).
-struct LayerPhases {
-  GemvArgs qkv, o, gate_up, down;
-  AttnArgs attn;
-  int32_t tw_q, tw_o, tw_g, tw_d;  // tiles per workgroup of each projection
-  uint32_t* bar;                   // barrier words, zero-initialised once
-};
-
-constexpr uint32_t kPersistEpochs = 8;  // grid barriers one launch may use (4)
-constexpr int kMaxPersistGrid = 1024;    // workgroups (one per CU) the barrier words provide for
-size_t persistent_bar_words(int grid);
-size_t persistent_lds_bytes(const w4_config& c);
-int persistent_grid(const w4_config& c);  // co-resident workgroups (one per CU), or 0 if unsupported
-hipError_t launch_persistent(const LayerPhases& t, const w4_config& c, int grid, hipStream_t s);
 
 // Launchers (return hipGetLastError of the launch).
 hipError_t launch_w4_gemv(int epi, const GemvArgs& a, hipStream_t s);
