@@ -332,6 +332,24 @@ int  paged_attention_decode(const uint16_t* q, const void* k_pool, const void* v
                             int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                             int32_t num_pages, int32_t max_pages, void* workspace,
                             size_t ws_bytes, uint16_t* out, void* stream);
+/* paged_attention_decode for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and results, with no workspace argument. The
+ * split partials, arrival counters and error count live in a device array
+ * the library holds on each GPU it runs on, for the life of the process, of
+ * paged_attention_noalloc_max_bytes() = 16 MiB; a call that needs more
+ * (paged_attention_workspace_bytes(...) above that) fails with W4_EINVAL
+ * before any device work. Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library call. The counters are cleared by a fill kernel on
+ * `stream` before each launch; the array keeps the last call's contents.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on
+ * one GPU (other streams, other threads) race: serialise them. Other
+ * arguments, layouts and errors as paged_attention_decode. */
+size_t paged_attention_noalloc_max_bytes(void);
+int  paged_attention_decode_noalloc(const uint16_t* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                                    int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int32_t num_pages, int32_t max_pages, uint16_t* out, void* stream);
 
 /* ------------------------------------------------------ greedy generation
  * The token loop around the decode step ("Building a Custom LLM Inference

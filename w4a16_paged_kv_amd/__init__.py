@@ -87,6 +87,9 @@ _SIGS = {
     "paged_attention_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "paged_attention_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                        c_int32, c_int32, c_int32, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "paged_attention_noalloc_max_bytes": (c_size_t, []),
+    "paged_attention_decode_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                               c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "w4_argmax_workspace_bytes": (c_size_t, [c_int32, c_int32]),
     "w4_argmax_f16": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
     "w4_generate_greedy": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
@@ -371,3 +374,13 @@ def paged_attention_decode(q, k_pool, v_pool, page_tables, ctx_lens, n_heads: in
                                         max_pages, _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _ptr(out),
                                         _stream(stream)))
+
+
+def paged_attention_decode_noalloc(q, k_pool, v_pool, page_tables, ctx_lens, n_heads: int, n_kv_heads: int,
+                                   head_dim: int, num_pages: int, out, stream=None) -> None:
+    """paged_attention_decode with the library's own per-device scratch (no workspace)."""
+    batch, max_pages = page_tables.shape
+    _check(lib().paged_attention_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_tables),
+                                                _ptr(ctx_lens), batch, n_heads, n_kv_heads, head_dim,
+                                                num_pages, max_pages, _ptr(out), _stream(stream)))
+

@@ -3,6 +3,8 @@
 // attn_item in attn_item.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "attn_item.h"
 
 namespace w4 {
@@ -66,4 +68,60 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStrea
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------- allocation-free standalone call
+// paged_attention_decode_noalloc keeps the split partials, arrival counters
+// and error count in this file-scope device array instead of a caller's
+// workspace. Each GPU holds its own copy for the life of the process; its
+// address on a device comes from hipGetSymbolAddress once, with that device
+// current (the array's name in host code is only a host-side stand-in).
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+static std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device.
+static int scratch_address(void** out) {
+  int dev = 0;
+  W4_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(W4_EINVAL, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    W4_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4_OK;
+}
+
 }  // namespace w4
+
+using namespace w4;
+
+W4_EXPORT size_t paged_attention_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+W4_EXPORT int paged_attention_decode_noalloc(const uint16_t* q, const void* k_pool, const void* v_pool,
+                                             const int32_t* page_tables, const int32_t* ctx_lens,
+                                             int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                             int32_t head_dim, int32_t num_pages, int32_t max_pages,
+                                             uint16_t* out, void* stream) {
+  clear_error();
+  const size_t need = paged_attention_workspace_bytes(batch, n_heads, n_kv_heads, head_dim, max_pages);
+  if (need == 0 || num_pages < 1)
+    return fail(W4_EINVAL, "paged_attention_decode_noalloc: unsupported shape batch=%d heads=%d/%d "
+                "head_dim=%d max_pages=%d num_pages=%d", batch, n_heads, n_kv_heads, head_dim, max_pages,
+                num_pages);
+  if (need > kNoallocScratchBytes)
+    return fail(W4_EINVAL, "paged_attention_decode_noalloc: this call needs %zu bytes of scratch, more than the "
+                "%zu the library holds per device; use paged_attention_decode with a workspace", need,
+                kNoallocScratchBytes);
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  return attention_standalone("paged_attention_decode_noalloc", q, k_pool, v_pool, page_tables, ctx_lens,
+                              batch, n_heads, n_kv_heads, head_dim, num_pages, max_pages, ws,
+                              kNoallocScratchBytes, out, stream);
+}
+

@@ -651,25 +651,27 @@ W4_EXPORT size_t paged_attention_workspace_bytes(int32_t batch, int32_t n_heads,
   return attn_ws_layout(batch, n_heads, n_kv_heads, head_dim, max_pages, &off, &ms, &pps);
 }
 
-W4_EXPORT int paged_attention_decode(const uint16_t* q, const void* k_pool, const void* v_pool,
-                                     const int32_t* page_tables, const int32_t* ctx_lens,
-                                     int32_t batch, int32_t n_heads, int32_t n_kv_heads,
-                                     int32_t head_dim, int32_t num_pages, int32_t max_pages,
-                                     void* workspace, size_t ws_bytes, uint16_t* out,
-                                     void* stream) {
-  clear_error();
+namespace w4 {
+// The standalone attention call on a scratch region ws of ws_bytes (the
+// caller's workspace, or the allocation-free entry point's device array):
+// validation, the counter clear, the launch. `who` names the entry point in
+// messages.
+int attention_standalone(const char* who, const uint16_t* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t num_pages,
+                         int32_t max_pages, void* workspace, size_t ws_bytes, uint16_t* out,
+                         void* stream) {
   if (!q || !k_pool || !v_pool || !page_tables || !ctx_lens || !workspace || !out)
-    return fail(W4_EINVAL, "paged_attention_decode: null pointer");
+    return fail(W4_EINVAL, "%s: null pointer", who);
   const size_t need = paged_attention_workspace_bytes(batch, n_heads, n_kv_heads, head_dim, max_pages);
   if (need == 0 || num_pages < 1)
-    return fail(W4_EINVAL, "paged_attention_decode: unsupported shape batch=%d heads=%d/%d "
-                "head_dim=%d max_pages=%d num_pages=%d", batch, n_heads, n_kv_heads, head_dim,
-                max_pages, num_pages);
+    return fail(W4_EINVAL, "%s: unsupported shape batch=%d heads=%d/%d head_dim=%d max_pages=%d num_pages=%d",
+                who, batch, n_heads, n_kv_heads, head_dim, max_pages, num_pages);
   if (ws_bytes < need)
-    return fail(W4_EINVAL, "paged_attention_decode: workspace %zu < %zu bytes", ws_bytes, need);
+    return fail(W4_EINVAL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
   const void* ptrs[] = {q, k_pool, v_pool, page_tables, ctx_lens, workspace, out};
   for (const void* p : ptrs)
-    if (!aligned256(p)) return fail(W4_EALIGN, "paged_attention_decode: pointer not 256-byte aligned");
+    if (!aligned256(p)) return fail(W4_EALIGN, "%s: pointer not 256-byte aligned", who);
   size_t poff;
   int max_splits, pps;
   attn_ws_layout(batch, n_heads, n_kv_heads, head_dim, max_pages, &poff, &max_splits, &pps);
@@ -699,6 +701,19 @@ W4_EXPORT int paged_attention_decode(const uint16_t* q, const void* k_pool, cons
   at.err = reinterpret_cast<uint32_t*>(ws) + (size_t)batch * n_kv_heads;
   W4_LAUNCH(launch_attention(at, head_dim, n_heads / n_kv_heads, s));
   return W4_OK;
+}
+}  // namespace w4
+
+W4_EXPORT int paged_attention_decode(const uint16_t* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* page_tables, const int32_t* ctx_lens,
+                                     int32_t batch, int32_t n_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, int32_t num_pages, int32_t max_pages,
+                                     void* workspace, size_t ws_bytes, uint16_t* out,
+                                     void* stream) {
+  clear_error();
+  return attention_standalone("paged_attention_decode", q, k_pool, v_pool, page_tables, ctx_lens, batch,
+                              n_heads, n_kv_heads, head_dim, num_pages, max_pages, workspace, ws_bytes, out,
+                              stream);
 }
 
 // ------------------------------------------------------ per-operation access

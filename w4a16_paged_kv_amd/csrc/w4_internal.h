@@ -178,6 +178,12 @@ hipError_t launch_embed_plan(const TokenPlanArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t s);
 bool attention_supported(int head_dim, int group);
+// paged_attention_decode on a given scratch region (see model.cpp).
+int attention_standalone(const char* who, const uint16_t* q, const void* k_pool, const void* v_pool,
+                         const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
+                         int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, int32_t num_pages,
+                         int32_t max_pages, void* workspace, size_t ws_bytes, uint16_t* out,
+                         void* stream);
 
 // Pages per attention split for a batch / context size: enough workgroups to
 // cover the chip, each split at least one page per wavefront (eight pages).
