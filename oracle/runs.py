@@ -13,6 +13,7 @@ import numpy as np
 
 import workloads as wl
 from . import decode as od
+from . import prefill as op
 
 
 def pools_f64(w: "wl.Workload", layer: int) -> Tuple[np.ndarray, np.ndarray]:
@@ -97,3 +98,27 @@ def step(w: "wl.Workload", layers: Optional[int] = None, logits_rows: Optional[n
     if keep_residuals:
         out["residuals"] = np.stack(res)
     return out
+
+
+def prefill_run(w: "wl.Workload", tokens: np.ndarray, start: int = 0, layers: Optional[int] = None,
+                exact: bool = False, mirror: bool = False, keep_pools: bool = False):
+    """Prefill of the prompt `tokens` for sequence 0 of the workload (its page
+    table row), positions start .. start + n - 1, over the workload's
+    generated pages. Returns {"logits": [V] of the last token, "x": [n, H]
+    final residual rows, "pools": [(k_pool, v_pool)] per layer (keep_pools)}."""
+    sh = w.shape
+    nl = sh.n_layers if layers is None else layers
+    x = wl.embedding_rows(w.workload_id, sh, np.asarray(tokens)).astype(np.float64)
+    pt = w.page_tables[0]
+    pools = []
+    for l in range(nl):
+        kp, vp = pools_f64(w, l)
+        x = op.prefill_layer(x, w.layer(l), kp, vp, pt, start, sh, exact, mirror)
+        if keep_pools:
+            pools.append((kp, vp))
+    xf = od.rmsnorm(x[-1:], w.final_norm(), sh.eps, exact)
+    out = {"logits": lm_head_rows(w, xf, exact=exact)[0], "x": x}
+    if keep_pools:
+        out["pools"] = pools
+    return out
+

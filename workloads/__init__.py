@@ -40,6 +40,7 @@ X_IN, PAGE_TABLE, CTX, TOKENS = 8, 9, 10, 11
 EMBED, LM_HEAD, FINAL_NORM = 12, 13, 14
 Q_ATTN, QKV_BIAS = 15, 16
 FORCED_ROW = 17
+PROMPT = 18
 
 ROW_CHUNK = 4096   # row chunk of the per-chunk streams (embedding, lm_head)
 
@@ -224,6 +225,10 @@ class Workload:
     def tokens(self) -> np.ndarray:
         return rng(self.workload_id, 0, TOKENS).integers(0, self.shape.vocab, self.batch).astype(np.int32)
 
+    def prompt_tokens(self, n: int) -> np.ndarray:
+        """Prompt token ids for prefill: n ids uniform over [0, vocab)."""
+        return rng(self.workload_id, 0, PROMPT).integers(0, self.shape.vocab, n).astype(np.int32)
+
     def x_in(self) -> np.ndarray:
         """Layer input activations fp16 [B, H] (single-layer workloads)."""
         return f16_normal(rng(self.workload_id, 0, X_IN), (self.batch, self.shape.hidden))
@@ -288,8 +293,14 @@ def step_b16() -> Workload:
     return _make("step_b16", 4, QWEN7B, _uniform_ctx(4, 16, 1024, 4096), QWEN7B.n_layers, True)
 
 
+def prefill_512() -> Workload:
+    """Prefill of a 512-token prompt (positions 0..511, 32 shuffled pages) through
+    the full 28-layer model + final norm + lm_head of the last token."""
+    return _make("prefill_512", 5, QWEN7B, [512], QWEN7B.n_layers, True)
+
+
 WORKLOADS = {"layer_mini": layer_mini, "layer_full": layer_full, "step_b1": step_b1,
-             "attn_stress": attn_stress, "step_b16": step_b16}
+             "attn_stress": attn_stress, "step_b16": step_b16, "prefill_512": prefill_512}
 
 
 def custom(name: str, wid: int, shape: Shape, ctx_lens, layers: int = 1, lm_head: bool = False,
