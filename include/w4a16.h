@@ -277,6 +277,61 @@ int  decode_layer(w4_model* model, int32_t layer, const uint16_t* x_in, uint16_t
                   const int32_t* positions, const int32_t* page_tables, const int32_t* ctx_lens,
                   int32_t batch, void* stream);
 
+/* ----------------------------------------------------------------- prefill
+ * A prompt through the model at once, before decoding ("How to build your
+ * own LLM runtime from scratch", Key performance metrics: time to first
+ * token of a 512-token prompt). Prompt token i sits at position start + i of
+ * one sequence; every prompt row gets the decode step's arithmetic at its
+ * position (FP16 RMSNorm per row, INT4 group-128 projections as M-row GEMMs
+ * on the matrix cores, RoPE, causal GQA attention over positions [0, its
+ * own] read through the page table [H100-kv], SiLU-gated MLP, residuals),
+ * its K/V is written into every layer's cache at page page_table[p / 16],
+ * slot p % 16 [H100-bug, Bug 1], and the logits of the last prompt token
+ * (after the FP16 final RMSNorm and lm_head) come out: decode_step then
+ * continues at position start + n_tokens. Positions below start must
+ * already hold the sequence's K/V (prior context, or nothing when start = 0).
+ *
+ * tokens: host int32 [n_tokens], each in [0, vocab); page_table: host int32
+ * [max_pages_per_seq of the model], entries p < ceil((start + n_tokens) / 16)
+ * in [0, num_pages) (W4_ERANGE otherwise; start + n_tokens <= 16
+ * max_pages_per_seq); workspace: device, caller-owned, >=
+ * w4_prefill_workspace_bytes(cfg, n_tokens, max_pages_per_seq) (every
+ * row's residual, normalised, query and attention-output rows, its F-wide
+ * MLP row and RoPE table: 67 KB per token for the Qwen2.5-7B shape);
+ * logits: device fp16 [vocab]. The inputs are staged into
+ * the workspace and the host waits for that copy (the call then returns with
+ * the kernels enqueued on `stream`); it runs eagerly (no graph). */
+size_t w4_prefill_workspace_bytes(const w4_config* cfg, int32_t max_tokens, int32_t max_pages_per_seq);
+int  w4_prefill(w4_model* model, const int32_t* tokens, int32_t n_tokens, int32_t start,
+                const int32_t* page_table, void* workspace, size_t ws_bytes, uint16_t* logits, void* stream);
+/* For tests and profiling: the byte offset in a prefill workspace (sized for
+ * n_tokens and max_pages_per_seq) of the fp16 rows [n_tokens][*row_stride]
+ * the last w4_prefill left there: W4_BUF_X the final residual rows,
+ * W4_BUF_Q / W4_BUF_O the last layer's queries (after RoPE) and attention
+ * outputs, W4_BUF_H its MLP rows, W4_BUF_XN its second RMSNorm output; -1 on
+ * bad arguments. */
+int64_t w4_prefill_buffer(const w4_config* cfg, int32_t n_tokens, int32_t max_pages_per_seq, int32_t which,
+                          int32_t* row_stride);
+
+/* Copies between natural-layout K/V rows and one layer of a KV cache laid out
+ * as above (K slices [16][D], V slices in the P V operand order), so callers
+ * can fill pages from K/V computed elsewhere or read them back ([H100-kv]:
+ * the cache is addressed through the page table). Token i of the call sits
+ * at position start + i, in page page_table[(start + i) / 16], slot
+ * (start + i) % 16. k, v: device fp16 [n_tokens][Hkv][D]; page_table: device
+ * int32 [max_pages], start + n_tokens <= 16 max_pages (W4_ERANGE otherwise);
+ * kv_cache: device, the model's [L][2][num_pages][Hkv][16 D] cache; only
+ * cfg->n_layers, n_kv_heads and head_dim (64 or 128) are read.
+ * Device-resident page ids are not validated on the host: a token whose
+ * page id is outside [0, num_pages) is skipped (nothing read or written).
+ * Asynchronous on `stream`; W4_EINVAL / W4_EALIGN on bad arguments. */
+int  kv_write_pages(const w4_config* cfg, void* kv_cache, int32_t num_pages, int32_t layer,
+                    const int32_t* page_table, int32_t max_pages, int32_t start, int32_t n_tokens,
+                    const uint16_t* k, const uint16_t* v, void* stream);
+int  kv_read_pages(const w4_config* cfg, const void* kv_cache, int32_t num_pages, int32_t layer,
+                   const int32_t* page_table, int32_t max_pages, int32_t start, int32_t n_tokens, uint16_t* k,
+                   uint16_t* v, void* stream);
+
 /* ---------------------------------------------------- per-operation access
  * For tests and profiling: run the step one operation at a time on the
  * model's own residual buffer (W4_BUF_X), with inputs staged by
@@ -307,7 +362,8 @@ void* w4_model_buffer(w4_model* model, int32_t which, int32_t* row_stride);
 /* ------------------------------------------------------- standalone kernels */
 /* y = fp16(W x) for a w4g128-packed W (role PLAIN rows in physical order),
  * fp32 accumulation. x: device fp16 [batch][k]; y: device fp16 [batch][n];
- * 1 <= batch <= 16. */
+ * 1 <= batch <= 2^20: batches 1..16 run the decode kernels, larger ones the
+ * prefill GEMM (the projections of w4_prefill). */
 int  w4_gemv(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
              int32_t batch, void* stream);
 /* y = fp16(W x) for a pack_weights_f16 W, fp32 accumulation, batch 1..16. */

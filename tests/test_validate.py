@@ -88,7 +88,8 @@ def test_model_create_argument_errors_before_device_work():
 def test_kernel_entry_argument_errors():
     L = w4.lib()
     assert L.w4_gemv(0x1000, 0x2000, 0x3000, 16, 12, 1, None) == w4.W4_EINVAL          # k % 8
-    assert L.w4_gemv(0x1000, 0x2000, 0x3000, 16, 128, 17, None) == w4.W4_EINVAL        # batch
+    assert L.w4_gemv(0x1000, 0x2000, 0x3000, 16, 128, 0, None) == w4.W4_EINVAL         # batch
+    assert L.w4_gemv(0x1000, 0x2000, 0x3000, 16, 128, (1 << 20) + 1, None) == w4.W4_EINVAL
     assert L.w4_gemv(0x1010, 0x2000, 0x3000, 16, 128, 1, None) == w4.W4_EALIGN
     assert L.w4_gemv_f16(None, 0x2000, 0x3000, 16, 128, 1, None) == w4.W4_EINVAL
     need = L.paged_attention_workspace_bytes(2, 28, 4, 128, 8)
@@ -119,3 +120,19 @@ def test_argmax_argument_checks_return_before_device_work():
     assert ok(a, 1, 10, a + 8, 64, a, None) == w4.W4_EALIGN
     assert ok(a, 2, 152064, a, 2 * 64 * 8 - 1, a, None) == w4.W4_EINVAL
     assert b"workspace" in lib.w4_last_error()
+
+
+def test_prefill_and_kv_copy_argument_errors():
+    """Host checks of the prefill and KV page-copy entry points (no device work)."""
+    L = w4.lib()
+    cfg = w4.make_config(448, 7, 1, 64, 1536, 5000, 2, 1e-6, 1e6)
+    import ctypes
+    assert L.w4_prefill_workspace_bytes(ctypes.byref(cfg), 512, 32) > 0
+    assert L.w4_prefill_workspace_bytes(ctypes.byref(cfg), 0, 32) == 0
+    assert L.w4_prefill(None, None, 1, 0, None, None, 0, None, None) == w4.W4_ESTATE      # no model
+    args = (0x1000, 4, 0)   # kv_cache, num_pages, layer
+    assert L.kv_write_pages(ctypes.byref(cfg), *args, 0x2000, 2, 20, 13, 0x3000, 0x4000, None) == w4.W4_ERANGE
+    assert L.kv_write_pages(ctypes.byref(cfg), *args, 0x2000, 2, 0, 8, 0x3010, 0x4000, None) == w4.W4_EALIGN
+    assert L.kv_read_pages(ctypes.byref(cfg), 0x1000, 4, 2, 0x2000, 2, 0, 8, 0x3000, 0x4000, None) == w4.W4_EINVAL
+    assert L.kv_read_pages(None, 0x1000, 4, 0, 0x2000, 2, 0, 8, 0x3000, 0x4000, None) == w4.W4_EINVAL
+

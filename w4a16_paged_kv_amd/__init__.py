@@ -87,6 +87,13 @@ _SIGS = {
     "paged_attention_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int32]),
     "paged_attention_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                        c_int32, c_int32, c_int32, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "w4_prefill_workspace_bytes": (c_size_t, [POINTER(w4_config), c_int32, c_int32]),
+    "w4_prefill_buffer": (c_int64, [POINTER(w4_config), c_int32, c_int32, c_int32, POINTER(c_int32)]),
+    "w4_prefill": (c_int, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "kv_write_pages": (c_int, [POINTER(w4_config), c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int32,
+                               c_void_p, c_void_p, c_void_p]),
+    "kv_read_pages": (c_int, [POINTER(w4_config), c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int32,
+                              c_void_p, c_void_p, c_void_p]),
     "paged_attention_noalloc_max_bytes": (c_size_t, []),
     "paged_attention_decode_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                                c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
@@ -286,6 +293,17 @@ class Model:
 
     __del__ = close
 
+    def w4_prefill(self, tokens, start: int, page_table, workspace, logits, stream=None) -> None:
+        """Prompt tokens (host int32 [n]) at positions start.. through the model;
+        page_table: host int32 [max_pages]; logits: device fp16 [vocab] of the
+        last prompt token; workspace: device bytes >= w4_prefill_workspace_bytes."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        pt = np.ascontiguousarray(page_table, dtype=np.int32).reshape(-1)
+        if pt.size != self.max_pages:
+            raise ValueError(f"page_table has {pt.size} entries, the model {self.max_pages}")
+        _check(lib().w4_prefill(self.handle, _ptr(t), t.size, start, _ptr(pt), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _ptr(logits), _stream(stream)))
+
     def w4_set_graph(self, enabled: bool) -> None:
         _check(lib().w4_set_graph(self.handle, int(enabled)))
 
@@ -383,4 +401,31 @@ def paged_attention_decode_noalloc(q, k_pool, v_pool, page_tables, ctx_lens, n_h
     _check(lib().paged_attention_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_tables),
                                                 _ptr(ctx_lens), batch, n_heads, n_kv_heads, head_dim,
                                                 num_pages, max_pages, _ptr(out), _stream(stream)))
+
+
+def w4_prefill_workspace_bytes(cfg: w4_config, max_tokens: int, max_pages: int) -> int:
+    return lib().w4_prefill_workspace_bytes(ctypes.byref(cfg), max_tokens, max_pages)
+
+
+def kv_write_pages(cfg: w4_config, kv_cache, num_pages: int, layer: int, page_table, start: int, k, v,
+                   stream=None) -> None:
+    """k, v: device fp16 [n][Hkv][D] -> layer `layer` of kv_cache at positions start..start+n-1."""
+    _check(lib().kv_write_pages(ctypes.byref(cfg), _ptr(kv_cache), num_pages, layer, _ptr(page_table),
+                                page_table.numel(), start, k.shape[0], _ptr(k), _ptr(v), _stream(stream)))
+
+
+def kv_read_pages(cfg: w4_config, kv_cache, num_pages: int, layer: int, page_table, start: int, k, v,
+                  stream=None) -> None:
+    """Inverse of kv_write_pages: fills k, v (device fp16 [n][Hkv][D])."""
+    _check(lib().kv_read_pages(ctypes.byref(cfg), _ptr(kv_cache), num_pages, layer, _ptr(page_table),
+                               page_table.numel(), start, k.shape[0], _ptr(k), _ptr(v), _stream(stream)))
+
+
+def w4_prefill_buffer(cfg: w4_config, n_tokens: int, max_pages: int, which: int):
+    """(byte offset, row stride in fp16 elements) of a prefill workspace buffer."""
+    stride = c_int32()
+    off = lib().w4_prefill_buffer(ctypes.byref(cfg), n_tokens, max_pages, which, ctypes.byref(stride))
+    if off < 0:
+        raise W4Error(W4_EINVAL, "w4_prefill_buffer: bad arguments")
+    return off, stride.value
 

@@ -506,7 +506,7 @@ __global__ __launch_bounds__(256) void embed_plan_kernel(TokenPlanArgs a) {
   const int pos = a.positions[b];
   if (threadIdx.x == 0) {
     const bool pos_ok = pos >= 0 && pos < a.max_pages * kPage;
-    const int page = pos_ok ? a.page_tables[(size_t)b * a.max_pages + (pos >> 4)] : -1;
+    const int page = pos_ok ? a.page_tables[(size_t)b * a.pt_stride + (pos >> 4)] : -1;
     const bool ok = pos_ok && page >= 0 && page < a.num_pages;
     a.slot[b] = ok ? page * kPage + (pos & 15) : -1;
     if (!ok) atomicAdd(a.err, 1u);

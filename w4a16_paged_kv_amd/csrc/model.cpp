@@ -322,6 +322,7 @@ static int enqueue_plan(w4_model* m, const int32_t* tokens, const StepInputs& in
   p.x = m->at<uint16_t>(m->L.x);
   p.positions = in.positions;
   p.page_tables = in.page_tables;
+  p.pt_stride = m->max_pages;
   p.max_pages = m->max_pages;
   p.num_pages = m->num_pages;
   p.head_dim = c.head_dim;
@@ -598,11 +599,15 @@ W4_EXPORT int w4_gemv(const void* packed, const uint16_t* x, uint16_t* y, int32_
                       int32_t batch, void* stream) {
   clear_error();
   if (!packed || !x || !y) return fail(W4_EINVAL, "w4_gemv: null pointer");
-  if (n <= 0 || k <= 0 || k % 8 || batch < 1 || batch > 16)
-    return fail(W4_EINVAL, "w4_gemv: n=%d k=%d (multiple of 8) batch=%d (1..16)", n, k, batch);
+  if (n <= 0 || k <= 0 || k % 8 || batch < 1 || batch > (1 << 20))
+    return fail(W4_EINVAL, "w4_gemv: n=%d k=%d (multiple of 8) batch=%d (1..2^20)", n, k, batch);
   if (!aligned256(packed) || !aligned256(x) || !aligned256(y))
     return fail(W4_EALIGN, "w4_gemv: pointer not 256-byte aligned");
   GemvArgs a = gemv_args(packed, n, k, x, k, nullptr, 0.f, y, n, nullptr, batch);
+  if (batch > 16) {
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_STORE, a, static_cast<hipStream_t>(stream)));
+    return W4_OK;
+  }
   W4_LAUNCH(launch_w4_gemv(EPI_STORE, a, static_cast<hipStream_t>(stream)));
   return W4_OK;
 }
@@ -859,4 +864,244 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
     if (stage_rc) return stage_rc;
   }
   return W4_OK;
+}
+
+// ------------------------------------------------------------------ prefill
+// A prompt through the model at once ("How to build your own LLM runtime from
+// scratch", Key performance metrics: time to first token of a 512-token
+// prompt): every prompt row gets the decode step's arithmetic at its own
+// position (the projections as M-row GEMMs on the matrix cores, RMSNorm per
+// row, causal attention over the pages), every row's K/V goes into the
+// sequence's pages, and the last row's logits come out.
+
+namespace w4 {
+
+struct PfLayout {
+  size_t err, tokens, positions, pt, slot, rope, x, xn, q, o, h, lmxn, total;
+  int xn_stride, o_stride, h_stride;
+};
+
+static PfLayout pf_layout(const w4_config& c, int max_tokens, int max_pages) {
+  PfLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  const size_t n = (size_t)max_tokens;
+  L.xn_stride = (int)round_up(c.hidden, kGroup);
+  L.o_stride = (int)round_up((size_t)c.n_heads * c.head_dim, kGroup);
+  L.h_stride = (int)round_up(c.ffn, kGroup);
+  L.err = take(256);
+  L.tokens = take(n * 4);
+  L.positions = take(n * 4);
+  L.pt = take((size_t)max_pages * 4);
+  L.slot = take(n * 4);
+  L.rope = take(n * (c.head_dim / 2) * 2 * 4);
+  L.x = take(n * c.hidden * 2);
+  L.xn = take(n * L.xn_stride * 2);
+  L.q = take(n * c.n_heads * c.head_dim * 2);
+  L.o = take(n * L.o_stride * 2);
+  L.h = take(n * L.h_stride * 2);
+  L.lmxn = take((size_t)L.xn_stride * 2);
+  L.total = off;
+  return L;
+}
+
+static int enqueue_prefill(w4_model* m, int n, int start, uint8_t* ws, const PfLayout& L, uint16_t* logits,
+                           hipStream_t s) {
+  const w4_config& c = m->cfg;
+  auto at = [&](size_t off) { return ws + off; };
+  uint16_t* x = reinterpret_cast<uint16_t*>(at(L.x));
+  uint16_t* xn = reinterpret_cast<uint16_t*>(at(L.xn));
+  uint16_t* q = reinterpret_cast<uint16_t*>(at(L.q));
+  uint16_t* o = reinterpret_cast<uint16_t*>(at(L.o));
+  uint16_t* h = reinterpret_cast<uint16_t*>(at(L.h));
+  uint32_t* err = reinterpret_cast<uint32_t*>(at(L.err));
+  W4_LAUNCH(launch_fill_u32(err, 1, 0u, s));
+  TokenPlanArgs p{};
+  p.tokens = reinterpret_cast<const int32_t*>(at(L.tokens));
+  p.table = m->weights.embed;
+  p.vocab = c.vocab;
+  p.hidden = c.hidden;
+  p.x = x;
+  p.positions = reinterpret_cast<const int32_t*>(at(L.positions));
+  p.page_tables = reinterpret_cast<const int32_t*>(at(L.pt));
+  p.pt_stride = 0;  // every row reads the one sequence's page table
+  p.max_pages = m->max_pages;
+  p.num_pages = m->num_pages;
+  p.head_dim = c.head_dim;
+  p.rope_base = c.rope_base;
+  p.slot = reinterpret_cast<int32_t*>(at(L.slot));
+  p.rope = reinterpret_cast<float*>(at(L.rope));
+  p.batch = n;
+  p.err = err;
+  W4_LAUNCH(launch_embed_plan(p, s));
+  const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const w4_layer_weights& W = m->layers[l];
+    W4_LAUNCH(launch_rmsnorm_rows(x, c.hidden, W.attn_norm, c.rms_eps, c.hidden, xn, L.xn_stride, n, s));
+    GemvArgs a = gemv_args(W.qkv, qkv_rows, c.hidden, xn, L.xn_stride, nullptr, 0.f, nullptr, 0, nullptr, n);
+    a.qkv.q_out = q;
+    a.qkv.q_stride = c.n_heads * c.head_dim;
+    a.qkv.k_pool = m->k_pool(l);
+    a.qkv.v_pool = m->v_pool(l);
+    a.qkv.bias = W.qkv_bias;
+    a.qkv.slot = p.slot;
+    a.qkv.rope = p.rope;
+    a.qkv.n_heads = c.n_heads;
+    a.qkv.n_kv_heads = c.n_kv_heads;
+    a.qkv.head_dim = c.head_dim;
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_QKV, a, s));
+    PrefillAttnArgs pa{};
+    pa.q = q;
+    pa.q_stride = c.n_heads * c.head_dim;
+    pa.k_pool = m->k_pool(l);
+    pa.v_pool = m->v_pool(l);
+    pa.page_table = p.page_tables;
+    pa.max_pages = m->max_pages;
+    pa.num_pages = m->num_pages;
+    pa.start = start;
+    pa.n = n;
+    pa.n_heads = c.n_heads;
+    pa.n_kv_heads = c.n_kv_heads;
+    pa.out = o;
+    pa.out_stride = L.o_stride;
+    pa.err = err;
+    W4_LAUNCH(launch_prefill_attention(pa, c.head_dim, c.n_heads / c.n_kv_heads, s));
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_RESID, gemv_args(W.o, c.hidden, c.n_heads * c.head_dim, o, L.o_stride,
+                                                          nullptr, 0.f, x, c.hidden, x, n), s));
+    W4_LAUNCH(launch_rmsnorm_rows(x, c.hidden, W.mlp_norm, c.rms_eps, c.hidden, xn, L.xn_stride, n, s));
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_SILU, gemv_args(W.gate_up, 2 * c.ffn, c.hidden, xn, L.xn_stride, nullptr,
+                                                         0.f, h, L.h_stride, nullptr, n), s));
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_RESID, gemv_args(W.down, c.hidden, c.ffn, h, L.h_stride, nullptr, 0.f, x,
+                                                          c.hidden, x, n), s));
+  }
+  F16GemvArgs f{};
+  f.w = static_cast<const uint8_t*>(m->weights.lm_head);
+  f.n = c.vocab;
+  f.k = c.hidden;
+  f.tiles = w4_tiles(c.vocab);
+  f.cblocks = ceil_div(c.hidden, 32);
+  f.x = x + (size_t)(n - 1) * c.hidden;  // the last prompt row
+  f.x_stride = c.hidden;
+  f.gamma = m->weights.final_norm;
+  f.eps = c.rms_eps;
+  f.y = logits;
+  f.y_stride = c.vocab;
+  f.xn_out = reinterpret_cast<uint16_t*>(at(L.lmxn));
+  f.batch = 1;
+  W4_LAUNCH(launch_f16_gemv(f, s));
+  return W4_OK;
+}
+
+}  // namespace w4
+
+W4_EXPORT size_t w4_prefill_workspace_bytes(const w4_config* cfg, int32_t max_tokens, int32_t max_pages) {
+  if (check_config(cfg) || max_tokens < 1 || max_pages < 1 || max_pages > (1 << 26) || max_tokens > (1 << 22))
+    return 0;
+  return pf_layout(*cfg, max_tokens, max_pages).total;
+}
+
+W4_EXPORT int w4_prefill(w4_model* m, const int32_t* tokens, int32_t n_tokens, int32_t start,
+                         const int32_t* page_table, void* workspace, size_t ws_bytes, uint16_t* logits,
+                         void* stream) {
+  clear_error();
+  int rc = check_model(m, 1);
+  if (rc) return rc;
+  if (!tokens || !page_table || !workspace || !logits) return fail(W4_EINVAL, "w4_prefill: null pointer");
+  if (!m->weights.embed || !m->weights.lm_head || !m->weights.final_norm)
+    return fail(W4_EINVAL, "w4_prefill: model has no embedding / final norm / lm_head");
+  if (n_tokens < 1 || n_tokens > (1 << 22)) return fail(W4_EINVAL, "w4_prefill: n_tokens %d outside [1, 2^22]", n_tokens);
+  if (start < 0 || (int64_t)start + n_tokens > (int64_t)m->max_pages * kPage)
+    return fail(W4_ERANGE, "w4_prefill: positions [%d, %lld) outside [0, %lld)", start,
+                (long long)start + n_tokens, (long long)m->max_pages * kPage);
+  if (!aligned256(workspace) || !aligned256(logits))
+    return fail(W4_EALIGN, "w4_prefill: workspace or logits not 256-byte aligned");
+  const PfLayout L = pf_layout(m->cfg, n_tokens, m->max_pages);
+  if (ws_bytes < L.total) return fail(W4_EINVAL, "w4_prefill: workspace %zu < %zu bytes", ws_bytes, L.total);
+  for (int i = 0; i < n_tokens; ++i)
+    if (tokens[i] < 0 || tokens[i] >= m->cfg.vocab)
+      return fail(W4_ERANGE, "w4_prefill: tokens[%d] = %d outside [0, %d)", i, tokens[i], m->cfg.vocab);
+  for (int pg = 0; pg < ceil_div(start + n_tokens, kPage); ++pg)
+    if (page_table[pg] < 0 || page_table[pg] >= m->num_pages)
+      return fail(W4_ERANGE, "w4_prefill: page_table[%d] = %d outside [0, %d)", pg, page_table[pg], m->num_pages);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  std::vector<int32_t> pos(n_tokens);
+  for (int i = 0; i < n_tokens; ++i) pos[i] = start + i;
+  W4_HIP(hipMemcpyAsync(ws + L.tokens, tokens, (size_t)n_tokens * 4, hipMemcpyHostToDevice, s));
+  W4_HIP(hipMemcpyAsync(ws + L.positions, pos.data(), (size_t)n_tokens * 4, hipMemcpyHostToDevice, s));
+  W4_HIP(hipMemcpyAsync(ws + L.pt, page_table, (size_t)m->max_pages * 4, hipMemcpyHostToDevice, s));
+  // the staged arrays must be on the device before the host vector goes away
+  W4_HIP(hipStreamSynchronize(s));
+  return enqueue_prefill(m, n_tokens, start, ws, L, logits, s);
+}
+
+W4_EXPORT int64_t w4_prefill_buffer(const w4_config* cfg, int32_t n_tokens, int32_t max_pages, int32_t which,
+                                    int32_t* row_stride) {
+  if (check_config(cfg) || n_tokens < 1 || max_pages < 1 || n_tokens > (1 << 22) || max_pages > (1 << 26)) return -1;
+  const PfLayout L = pf_layout(*cfg, n_tokens, max_pages);
+  size_t off;
+  int stride;
+  switch (which) {
+    case W4_BUF_X: off = L.x; stride = cfg->hidden; break;
+    case W4_BUF_Q: off = L.q; stride = cfg->n_heads * cfg->head_dim; break;
+    case W4_BUF_O: off = L.o; stride = L.o_stride; break;
+    case W4_BUF_H: off = L.h; stride = L.h_stride; break;
+    case W4_BUF_XN: off = L.xn; stride = L.xn_stride; break;
+    default: return -1;
+  }
+  if (row_stride) *row_stride = stride;
+  return (int64_t)off;
+}
+
+// ------------------------------------------------------------ KV page copies
+
+static int kv_copy(const char* who, const w4_config* cfg, void* kv_cache, int32_t num_pages, int32_t layer,
+                   const int32_t* page_table, int32_t max_pages, int32_t start, int32_t n_tokens, uint16_t* k,
+                   uint16_t* v, bool to_pages, void* stream) {
+  clear_error();
+  if (!cfg || !kv_cache || !page_table || !k || !v) return fail(W4_EINVAL, "%s: null pointer", who);
+  if (cfg->n_kv_heads < 1 || (cfg->head_dim != 64 && cfg->head_dim != 128) || cfg->n_layers < 1)
+    return fail(W4_EINVAL, "%s: unsupported n_kv_heads %d / head_dim %d", who, cfg->n_kv_heads, cfg->head_dim);
+  if (layer < 0 || layer >= cfg->n_layers || num_pages < 1 || max_pages < 1 || start < 0 || n_tokens < 0)
+    return fail(W4_EINVAL, "%s: layer %d (of %d), num_pages %d, max_pages %d, start %d, n_tokens %d", who, layer,
+                cfg->n_layers, num_pages, max_pages, start, n_tokens);
+  if ((int64_t)start + n_tokens > (int64_t)max_pages * kPage)
+    return fail(W4_ERANGE, "%s: positions [%d, %lld) past the page table's %d pages", who, start,
+                (long long)start + n_tokens, max_pages);
+  const void* ptrs[] = {kv_cache, page_table, k, v};
+  for (const void* p : ptrs)
+    if (!aligned256(p)) return fail(W4_EALIGN, "%s: pointer not 256-byte aligned", who);
+  KvCopyArgs a{};
+  const size_t layer_elems = (size_t)num_pages * cfg->n_kv_heads * kPage * cfg->head_dim;
+  a.k_pool = static_cast<uint16_t*>(kv_cache) + (size_t)(2 * layer) * layer_elems;
+  a.v_pool = a.k_pool + layer_elems;
+  a.page_table = page_table;
+  a.num_pages = num_pages;
+  a.n_kv_heads = cfg->n_kv_heads;
+  a.head_dim = cfg->head_dim;
+  a.start = start;
+  a.n = n_tokens;
+  a.k = k;
+  a.v = v;
+  a.to_pages = to_pages ? 1 : 0;
+  W4_LAUNCH(launch_kv_pages(a, static_cast<hipStream_t>(stream)));
+  return W4_OK;
+}
+
+W4_EXPORT int kv_write_pages(const w4_config* cfg, void* kv_cache, int32_t num_pages, int32_t layer,
+                             const int32_t* page_table, int32_t max_pages, int32_t start, int32_t n_tokens,
+                             const uint16_t* k, const uint16_t* v, void* stream) {
+  return kv_copy("kv_write_pages", cfg, kv_cache, num_pages, layer, page_table, max_pages, start, n_tokens,
+                 const_cast<uint16_t*>(k), const_cast<uint16_t*>(v), true, stream);
+}
+
+W4_EXPORT int kv_read_pages(const w4_config* cfg, const void* kv_cache, int32_t num_pages, int32_t layer,
+                            const int32_t* page_table, int32_t max_pages, int32_t start, int32_t n_tokens,
+                            uint16_t* k, uint16_t* v, void* stream) {
+  return kv_copy("kv_read_pages", cfg, const_cast<void*>(kv_cache), num_pages, layer, page_table, max_pages,
+                 start, n_tokens, k, v, false, stream);
 }

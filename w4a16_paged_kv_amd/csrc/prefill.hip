@@ -1,0 +1,428 @@
+// Prefill of a prompt for gfx950: the W4A16 projections as M-row GEMMs on
+// the matrix cores, and causal attention of the prompt rows over the pages.
+//
+// Before decoding, a prompt runs through the model once: every token's K/V
+// goes into the sequence's pages and the last token's logits give the first
+// generated token ("How to build your own LLM runtime from scratch", Key
+// performance metrics: time to first token of a 512-token prompt). Each
+// prompt row gets exactly the decode step's arithmetic at its own position;
+// the rows meet only through the pages (causal attention).
+//
+// Weights are the packed w4g128 blocks the decode step reads (symmetric INT4,
+// group 128 along the input dimension; "How to build your own LLM runtime from
+// scratch", Architectural decisions and optimizations): at M = 512 rows a
+// projection is a dense contraction (gate/up: 139 GFLOP against 70 MB of
+// weights), so the kernel reuses each dequantised block for many rows.
+#include <hip/hip_runtime.h>
+
+#include "attn_item.h"
+#include "gemv_b1.h"
+
+namespace w4 {
+
+// ---------------------------------------------------------------- W4A16 GEMM
+// Workgroup = WM x WN wavefronts; wavefront (wm, wn) computes rows
+// [m0 + 16 MR wm, +16 MR) x weight tiles [t0 + NTW wn, +NTW) as MR x NTW
+// 16x16 blocks of v_mfma_f32_16x16x32_f16 (A = activation rows in the MFMA
+// k-slot order from LDS, B = the lane's 16 bytes of a packed block, exactly
+// dequantised as in the decode GEMV). Per 128-column group the four MFMAs of
+// a block start from zero and the group's fp32 scale is applied to the sum
+// (acc += s * D), so the result is the fp32 sum over groups of exact
+// per-group products, as at batch 1.
+//
+// The activation rows of a group (M_T x 128 fp16) are staged in LDS in slot
+// order (slot_word: each thread converts one natural 8-column word with the
+// words of its 4-lane quad), rows padded by 16 bytes so the 16 rows one
+// ds_read_b128 touches fall in distinct banks; two buffers, the next group's
+// rows and weight blocks loaded while the current group is multiplied.
+constexpr int kPfPad = 8;  // fp16 padding per staged row
+
+template <int WM, int WN, int MR, int NTW>
+struct PfTile {
+  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int kRows = 16 * MR * WM;         // M_T
+  static constexpr int kTiles = NTW * WN;            // weight tiles per workgroup
+  static constexpr int kRowStride = kGroup + kPfPad;  // fp16 per staged row
+  static constexpr int kWords = kRows * 16 / kThreads;  // staged words per thread per group
+  static constexpr size_t kLdsBytes = (size_t)2 * kRows * kRowStride * 2;
+  static_assert(kRows * 16 % kThreads == 0, "whole staging rounds");
+  static_assert(kThreads % 16 == 0, "a thread keeps its word index across rounds");
+};
+
+// The prefill epilogue of one accumulator value: lane l holds weight row
+// l & 15 of tile t for activation row m; its partner (weight row (l & 15) ^ 8)
+// comes from ror8, taken by every lane before any branch.
+template <int EPI>
+__device__ __forceinline__ void pf_epilogue(const GemvArgs& a, int m, int t, int i, float v, float partner) {
+  if (m >= a.batch || t >= a.tiles) return;
+  if (EPI == EPI_QKV) {
+    if (i < 8) {
+      const int pair = qkv_dim0(a.qkv, t, i);
+      const float* cs = a.qkv.rope + ((size_t)m * (a.qkv.head_dim / 2) + pair) * 2;
+      epi_qkv(a, m, t, i, v, partner, cs[0], cs[1], a.qkv.slot[m]);
+    }
+  } else if (EPI == EPI_SILU) {
+    const int o = 8 * t + i;
+    if (i < 8 && o < a.n / 2) st16_agent(a.y + (size_t)m * a.y_stride + o, f2h(v / (1.0f + expf(-v)) * partner));
+  } else {
+    const int row = kTileRows * t + i;
+    if (row < a.n) {
+      if (EPI == EPI_RESID) v += h2f(ld16_agent(a.resid + (size_t)m * a.y_stride + row));
+      st16_agent(a.y + (size_t)m * a.y_stride + row, f2h(v));
+    }
+  }
+}
+
+template <int EPI, int WM, int WN, int MR, int NTW>
+__global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_kernel(GemvArgs a) {
+  using T = PfTile<WM, WN, MR, NTW>;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [2][kRows][kRowStride]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % WM, wn = wave / WM;
+  const int m0 = blockIdx.x * T::kRows;               // M tiles fastest: neighbours share weights
+  const int t0 = blockIdx.y * T::kTiles + wn * NTW;   // this wavefront's first weight tile
+  const int G = a.groups;
+
+  // staging: thread t takes word t % 16 of rows t / 16 + r * (threads / 16)
+  const int sw = threadIdx.x & 15;
+  const int srow0 = threadIdx.x >> 4;
+  constexpr int kRowStep = T::kThreads / 16;
+  const __amdgpu_buffer_rsrc_t rx = coherent_rsrc(a.x);
+  u4_t st[T::kWords];
+  auto stage_load = [&](int g) {
+    const int c = g * kGroup + 8 * sw;
+#pragma unroll
+    for (int r = 0; r < T::kWords; ++r) {
+      const int m = min(m0 + srow0 + r * kRowStep, a.batch - 1);
+      st[r] = ld128_agent(rx, 2 * (m * a.x_stride + min(c, a.k - 8)));
+    }
+  };
+  auto stage_store = [&](int g, int buf) {
+    const int c = g * kGroup + 8 * sw;
+    const int e = sw & 1;
+#pragma unroll
+    for (int r = 0; r < T::kWords; ++r) {
+      const int row = srow0 + r * kRowStep;
+      u4_t v = st[r];
+      if (m0 + row >= a.batch || c >= a.k) v = (u4_t){0u, 0u, 0u, 0u};
+      const u4_t o = slot_word(v, e);  // every lane of the quad takes part
+      *reinterpret_cast<u4_t*>(xs + ((size_t)buf * T::kRows + row) * T::kRowStride + 8 * sw) = o;
+    }
+  };
+
+  // weights: the lane's 16 bytes of block (t, g) and the scale of row lane & 15
+  const u4_t* wbase = reinterpret_cast<const u4_t*>(a.w);
+  const uint16_t* sbase = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024);
+  u4_t wc[NTW], wn_[NTW];
+  uint32_t sc[NTW], sn[NTW];
+  auto w_load = [&](int g, u4_t* wv, uint32_t* sv) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int t = min(t0 + j, a.tiles - 1);
+      const size_t blk = (size_t)t * G + g;
+      wv[j] = __builtin_nontemporal_load(wbase + blk * 64 + lane);
+      sv[j] = sbase[blk * 16 + (lane & 15)];
+    }
+  };
+
+  f4_t acc[MR][NTW];
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = (f4_t){0.f, 0.f, 0.f, 0.f};
+  const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
+
+  stage_load(0);
+  w_load(0, wc, sc);
+  stage_store(0, 0);
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    const bool more = g + 1 < G;
+    if (more) {
+      stage_load(g + 1);
+      w_load(g + 1, wn_, sn);
+    }
+    const uint16_t* xb = xs + ((size_t)buf * T::kRows + 16 * MR * wm + (lane & 15)) * T::kRowStride +
+                         32 * (lane >> 4);
+    f4_t d[MR][NTW];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t mk = (r & 1) ? mhi : mlo;
+      const h2_t bias = (r & 1) ? (h2_t){(_Float16)1152.0f, (_Float16)1152.0f}
+                                : (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+      h8_t bw[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const uint32_t w0 = wc[j][2 * (r >> 1)], w1 = wc[j][2 * (r >> 1) + 1];
+        auto q2 = [&](uint32_t v) { return __builtin_bit_cast(uint32_t, as_h2((v & mk) | 0x64006400u) - bias); };
+        bw[j] = __builtin_bit_cast(h8_t, (u4_t){q2(w0), q2(w0 >> 8), q2(w1), q2(w1 >> 8)});
+      }
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        const h8_t av = __builtin_bit_cast(h8_t, *reinterpret_cast<const u4_t*>(xb + (size_t)16 * i * T::kRowStride + 8 * r));
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          d[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[j], r == 0 ? (f4_t){0.f, 0.f, 0.f, 0.f} : d[i][j],
+                                                           0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const float s = h2f((uint16_t)sc[j]);
+#pragma unroll
+      for (int i = 0; i < MR; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(s, d[i][j][q], acc[i][j][q]);
+    }
+    if (more) {
+      stage_store(g + 1, buf ^ 1);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        wc[j] = wn_[j];
+        sc[j] = sn[j];
+      }
+    }
+    __syncthreads();
+  }
+
+  // lane l holds D[row 4 (l >> 4) + q][weight row l & 15] of each block
+  const int i16 = lane & 15;
+#pragma unroll
+  for (int i = 0; i < MR; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float v = acc[i][j][q];
+        const float partner = ror8(v);
+        const int m = m0 + 16 * MR * wm + 16 * i + 4 * (lane >> 4) + q;
+        pf_epilogue<EPI>(a, m, t0 + j, i16, v, partner);
+      }
+}
+
+template <int EPI, int WM, int WN, int MR, int NTW>
+static hipError_t launch_pf_tile(const GemvArgs& a, hipStream_t s) {
+  using T = PfTile<WM, WN, MR, NTW>;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemm_prefill_kernel<EPI, WM, WN, MR, NTW>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((w4_gemm_prefill_kernel<EPI, WM, WN, MR, NTW>),
+                     dim3(ceil_div(a.batch, T::kRows), ceil_div(a.tiles, T::kTiles)), dim3(T::kThreads),
+                     T::kLdsBytes, s, a);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_pf_epi(const GemvArgs& a, hipStream_t s) {
+  // 128 rows x 128 weight rows per workgroup (2 x 2 wavefronts of 64 x 64);
+  // narrower matrices take 64-row x 128-weight-row tiles (1 x 4 wavefronts
+  // of 64 x 32) so the grid still covers the chip
+  if ((long)ceil_div(a.batch, 128) * ceil_div(a.tiles, 8) >= 256) return launch_pf_tile<EPI, 2, 2, 4, 4>(a, s);
+  return launch_pf_tile<EPI, 1, 4, 4, 2>(a, s);
+}
+
+hipError_t launch_w4_gemm_prefill(int epi, const GemvArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return launch_pf_epi<EPI_STORE>(a, s);
+    case EPI_RESID: return launch_pf_epi<EPI_RESID>(a, s);
+    case EPI_SILU: return launch_pf_epi<EPI_SILU>(a, s);
+    case EPI_QKV: return launch_pf_epi<EPI_QKV>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------- causal attention
+// Work item = (16 prompt rows, query head): one wavefront. Prompt row m sits
+// at position start + m and attends positions [0, start + m] of its
+// sequence, read through the page table (token t of the sequence in page
+// page_table[t / 16], slot t % 16: "Building a Custom LLM Inference Runtime
+// on H100", The Three Critical Bugs, Bug 1). The products run on the
+// matrix cores as in the decode kernel, with the 16 query columns being
+// the item's 16 rows instead of a KV group's heads: S^T = K Q^T
+// (v_mfma_f32_16x16x32_f16, lane l ends with S[token 4 (l >> 4) + j][row
+// l & 15]), base-2 online softmax per row in fp32, O^T = V^T P^T
+// (v_mfma_f32_16x16x16_f16, P entering as two fp16 terms). A token past
+// a row's position scores -inf; V values of tokens past the item's last
+// position are zeroed, so slots not written yet (or poisoned) add nothing.
+// A workgroup holds the GQ heads of one KV head for the same 16 rows, so
+// their K/V loads meet in the cache.
+template <int D, int GQ>
+__global__ __launch_bounds__(GQ * 64) void prefill_attn_kernel(PrefillAttnArgs a) {
+  constexpr int NK = D / 32, NS = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int blk = blockIdx.x, kvh = blockIdx.y;
+  const int h = kvh * GQ + wave;
+  const int r0 = 16 * blk;                       // first prompt row of the item
+  const int last_row = min(r0 + 15, a.n - 1);
+  const int p_last = a.start + last_row;         // the item's last position
+  const int npages = p_last / kPage + 1;
+  const int qi = lane & 15, kc = 8 * (lane >> 4), tk = 4 * (lane >> 4);
+  const int my_pos = a.start + r0 + qi;          // this lane's query row position (for the mask)
+
+  // the 16 rows' queries as the B operand (row qi, dims 32 kk + kc .. + 8)
+  const __amdgpu_buffer_rsrc_t rq = coherent_rsrc(a.q);
+  const int qrow = min(r0 + qi, a.n - 1);
+  u4_t qb[NK];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) qb[kk] = ld128_agent(rq, 2 * (qrow * a.q_stride + h * D + 32 * kk + kc));
+
+  const float scale = kLog2e / sqrtf((float)D);
+  float m_h = -INFINITY, l_h = 0.f;              // softmax state of row qi
+  f4_t acc[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) acc[i] = (f4_t){0.f, 0.f, 0.f, 0.f};
+  const size_t slice = (size_t)kPage * D;
+  u4_t kf[NK], vf[NS / 2], kn[NK], vn[NS / 2];
+  auto load_kv = [&](int p, u4_t* kk, u4_t* vv) {
+    int id = a.page_table[min(p, a.max_pages - 1)];
+    if (id < 0 || id >= a.num_pages) {
+      if (lane == 0) atomicAdd(a.err, 1u);
+      id = 0;
+    }
+    id = __builtin_amdgcn_readfirstlane(id);
+    const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(a.k_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
+    const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(a.v_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) kk[i] = ld128_agent(rk, 2 * (qi * D + 32 * i + kc));
+#pragma unroll
+    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128_agent(rv, 16 * (64 * i + lane));
+  };
+  load_kv(0, kf, vf);
+  for (int p = 0; p < npages; ++p) {
+    if (p + 1 < npages) load_kv(p + 1, kn, vn);
+    f4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, kf[kk]), __builtin_bit_cast(h8_t, qb[kk]),
+                                                  sc, 0, 0, 0);
+    float sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sv[j] = kPage * p + tk + j <= my_pos ? sc[j] * scale : -INFINITY;
+    const float pm = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    const float n_h = fmaxf(m_h, pm);
+    const float al = n_h == -INFINITY ? 1.f : exp2f(m_h - n_h);
+    float pj[4];
+    h4_t ph, pl;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pj[j] = n_h == -INFINITY ? 0.f : exp2f(sv[j] - n_h);
+      ph[j] = (_Float16)pj[j];
+      pl[j] = (_Float16)(pj[j] - (float)ph[j]);
+    }
+    l_h = l_h * al + rows_sum((pj[0] + pj[1]) + (pj[2] + pj[3]));
+    m_h = n_h;
+    const int valid = p_last - kPage * p + 1;    // tokens of this page at or before the item's last position
+    if (valid < kPage) {
+#pragma unroll
+      for (int i = 0; i < NS / 2; ++i) {
+        h8_t v8 = __builtin_bit_cast(h8_t, vf[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (tk + (j & 3) >= valid) v8[j] = (_Float16)0.f;
+        vf[i] = __builtin_bit_cast(u4_t, v8);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const u4_t vp = vf[i >> 1];
+      const h4_t v4 = __builtin_bit_cast(h4_t, (i & 1) ? (u2_t){vp[2], vp[3]} : (u2_t){vp[0], vp[1]});
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, ph, acc[i] * al, 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, pl, acc[i], 0, 0, 0);
+    }
+    if (p + 1 < npages) {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) kf[i] = kn[i];
+#pragma unroll
+      for (int i = 0; i < NS / 2; ++i) vf[i] = vn[i];
+    }
+  }
+  // lane l: O[row l & 15][dim 16 i + 4 (l >> 4) + j]
+  const int row = r0 + qi;
+  if (row < a.n) {
+    const float inv = l_h > 0.f ? 1.0f / l_h : 0.f;
+    uint16_t* out = a.out + (size_t)row * a.out_stride + h * D;
+    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(out);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      h4_t r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = (_Float16)(acc[i][j] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, r), ro, 2 * (16 * i + tk), 0, kPolicySc1);
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_pfa_d(const PrefillAttnArgs& a, int group, hipStream_t s) {
+  const dim3 grid(ceil_div(a.n, 16), a.n_kv_heads);
+  switch (group) {
+    case 1: hipLaunchKernelGGL((prefill_attn_kernel<D, 1>), grid, dim3(64), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), grid, dim3(128), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((prefill_attn_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((prefill_attn_kernel<D, 7>), grid, dim3(448), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((prefill_attn_kernel<D, 8>), grid, dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attention(const PrefillAttnArgs& a, int head_dim, int group, hipStream_t s) {
+  if (head_dim == 64) return launch_pfa_d<64>(a, group, s);
+  if (head_dim == 128) return launch_pfa_d<128>(a, group, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w4
+
+namespace w4 {
+
+// ------------------------------------------------------------ KV page copies
+// Natural-layout K/V rows (token, KV head, D values) to and from the cache's
+// page slices: K slices [16 tokens][D], V slices in the P V operand order of
+// v_slice_offset. One thread per (token, KV head, 8 dims); token i of the
+// call sits at position start + i, in page page_table[pos / 16], slot
+// pos % 16. A page id outside [0, num_pages) skips the token (nothing is
+// read or written for it; the host validates ids it can see).
+__global__ __launch_bounds__(256) void kv_pages_kernel(KvCopyArgs a) {
+  const int per_tok = a.n_kv_heads * (a.head_dim / 8);
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)a.n * per_tok) return;
+  const int tok = (int)(i / per_tok), rem = (int)(i % per_tok);
+  const int kvh = rem / (a.head_dim / 8), d0 = 8 * (rem % (a.head_dim / 8));
+  const int pos = a.start + tok;
+  const int page = a.page_table[pos >> 4];
+  if (page < 0 || page >= a.num_pages) return;
+  const size_t slice = ((size_t)page * a.n_kv_heads + kvh) * kPage * a.head_dim;
+  const int t = pos & 15;
+  const size_t nat = ((size_t)tok * a.n_kv_heads + kvh) * a.head_dim + d0;
+  uint16_t* kp = a.k_pool + slice + (size_t)t * a.head_dim + d0;
+  uint16_t* vp = a.v_pool + slice;
+  if (a.to_pages) {
+    *reinterpret_cast<u4_t*>(kp) = *reinterpret_cast<const u4_t*>(a.k + nat);
+    const u4_t v8 = *reinterpret_cast<const u4_t*>(a.v + nat);
+    const uint16_t* vv = reinterpret_cast<const uint16_t*>(&v8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vp[v_slice_offset(t, d0 + j)] = vv[j];
+  } else {
+    *reinterpret_cast<u4_t*>(a.k + nat) = *reinterpret_cast<const u4_t*>(kp);
+    u4_t v8;
+    uint16_t* vv = reinterpret_cast<uint16_t*>(&v8);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vv[j] = vp[v_slice_offset(t, d0 + j)];
+    *reinterpret_cast<u4_t*>(a.v + nat) = v8;
+  }
+}
+
+hipError_t launch_kv_pages(const KvCopyArgs& a, hipStream_t s) {
+  const long threads = (long)a.n * a.n_kv_heads * (a.head_dim / 8);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_pages_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace w4

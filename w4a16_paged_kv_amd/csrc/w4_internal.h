@@ -80,7 +80,8 @@ struct TokenPlanArgs {
   int32_t vocab, hidden;
   uint16_t* x;                // [B][hidden]
   const int32_t* positions;   // [B]
-  const int32_t* page_tables; // [B][max_pages]
+  const int32_t* page_tables; // [B][pt_stride]: row b at page_tables + b * pt_stride
+  int32_t pt_stride;          // max_pages, or 0 when every row is one sequence (prefill)
   int32_t max_pages, num_pages;
   int32_t head_dim;
   float rope_base;
@@ -146,6 +147,34 @@ struct AttnArgs {
   uint32_t* err;
 };
 
+// Causal attention of n prompt rows of one sequence (prefill.hip): row m at
+// position start + m attends positions [0, start + m] through page_table.
+struct PrefillAttnArgs {
+  const uint16_t* q;          // [n][q_stride], heads of D values (after RoPE)
+  int32_t q_stride;
+  const uint16_t* k_pool;     // [P][Hkv][16][D]
+  const uint16_t* v_pool;     // [P][Hkv][16 * D], slices in P V operand order
+  const int32_t* page_table;  // [max_pages] of the sequence
+  int32_t max_pages, num_pages;
+  int32_t start, n;
+  int32_t n_heads, n_kv_heads;
+  uint16_t* out;              // [n][out_stride]
+  int32_t out_stride;
+  uint32_t* err;
+};
+
+// Copies between natural-layout K/V rows [n][Hkv][D] and one layer's pages.
+struct KvCopyArgs {
+  uint16_t* k_pool;           // [P][Hkv][16][D]
+  uint16_t* v_pool;           // [P][Hkv][16 * D], P V operand order
+  const int32_t* page_table;  // device [>= ceil((start + n) / 16)]
+  int32_t num_pages, n_kv_heads, head_dim;
+  int32_t start, n;
+  uint16_t* k;                // [n][Hkv][D]
+  uint16_t* v;
+  int32_t to_pages;           // 1: rows -> pages, 0: pages -> rows
+};
+
 // Batch-1 GEMV work split (policy in gemv_b1.h): S wavefronts per tile, TW
 // tiles per 1024-thread workgroup, IT activation words per thread.
 struct B1Split {
@@ -177,6 +206,11 @@ hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16
 hipError_t launch_embed_plan(const TokenPlanArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t s);
+// Prefill (prefill.hip): a.batch = prompt rows (any count); epilogues as the
+// decode projections, with row m's token plan entries for EPI_QKV.
+hipError_t launch_w4_gemm_prefill(int epi, const GemvArgs& a, hipStream_t s);
+hipError_t launch_prefill_attention(const PrefillAttnArgs& a, int head_dim, int group, hipStream_t s);
+hipError_t launch_kv_pages(const KvCopyArgs& a, hipStream_t s);
 bool attention_supported(int head_dim, int group);
 // paged_attention_decode on a given scratch region (see model.cpp).
 int attention_standalone(const char* who, const uint16_t* q, const void* k_pool, const void* v_pool,
