@@ -7,7 +7,10 @@ W4A16 weights, fp16 lm_head), batch 1, 2048-token context. One step = one
 decode_step over all layers + lm_head for the batch, inputs already resident
 in HBM. Prints one JSON line: ms/token, tokens/s, effective HBM GB/s against
 the 8 TB/s peak, the roofline of the dominant kernel and the CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload. Two more workloads are timed
+on the same weights and reported under their own keys: the batch-16 step
+(step_b16: 16 sequences, contexts 1024..4096) and the prefill of a
+512-token prompt (prefill_512: time to first token).
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+PEAK_MFMA_F16 = 2.5e15     # MI355X dense fp16 matrix peak, flop/s
 GEN_STEPS = 16            # greedy generation steps timed after the step itself
 ARGMAX_CALLS = 20         # greedy-choice calls per timed graph replay
 COPY_BYTES = 1 << 30      # plain copy timed for the measured streaming rate
@@ -53,6 +57,34 @@ def op_bytes(sh, batch, ctx_lens):
         "lm_head": V * H * 2 + H * 2 + B * (H * 2 + V * 2),
     }
     return per
+
+
+def prefill_flops(sh, n):
+    """Multiply-add work of a prefill of n tokens from position 0 (2 flops per
+    multiply-add): every projection for every row, causal attention (scores
+    and P V over 1 + 2 + ... + n positions per head), the last row's lm_head."""
+    H, F, D, Hq, Hkv = sh.hidden, sh.ffn, sh.head_dim, sh.n_heads, sh.n_kv_heads
+    per_row = (Hq + 2 * Hkv) * D * H + H * Hq * D + 2 * F * H + H * F
+    attn = 2 * Hq * D * (n * (n + 1) // 2)
+    return 2 * sh.n_layers * (n * per_row + attn) + 2 * sh.vocab * H
+
+
+def attach(dm, w):
+    """A second model on dm's uploaded weights, with workload w's KV pages,
+    page tables and its own workspace (timing only: the weights' values are
+    random draws either way)."""
+    import torch
+    import w4a16_paged_kv_amd as w4
+    from workloads.device import upload_kv
+    sh = w.shape
+    kv = torch.empty((sh.n_layers, 2, w.num_pages, sh.n_kv_heads, 16, sh.head_dim), dtype=torch.float16,
+                     device="cuda")
+    for l in range(sh.n_layers):
+        upload_kv(w, kv, l)
+    ws = torch.empty(w4.w4_workspace_bytes(dm.cfg, w.batch, w.max_pages), dtype=torch.uint8, device="cuda")
+    m = w4.Model(dm.cfg, dm.layers, kv, w.num_pages, ws, w.batch, w.max_pages, dm.embed, dm.final_norm,
+                 dm.lm_head)
+    return m, kv, ws
 
 
 def launches_per_step(name, sh):
@@ -133,6 +165,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="step_b1", choices=["step_b1", "step_b16"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the batch-16 step and the prefill")
     ap.add_argument("--op-reps", type=int, default=20)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run three plain device copies of MIB MiB each, so that HBM byte "
@@ -297,6 +330,59 @@ def main():
     del src, dst
     torch.cuda.empty_cache()
 
+    # ---- batch-16 step on the same weights (graph replay, device inputs)
+    b16 = None
+    if args.workload == "step_b1" and not args.no_extra:
+        w16 = wl.step_b16()
+        m16, kv16, ws16 = attach(dm, w16)
+        t16, p16, pt16, c16 = w16.tokens(), w16.positions, w16.page_tables, w16.ctx_lens
+        dev16 = [torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda() for a in (t16, p16, pt16, c16)]
+        lg16 = torch.empty((w16.batch, sh.vocab), dtype=torch.float16, device="cuda")
+        s16 = lambda: m16.decode_step_device(*dev16, lg16)
+        for _ in range(5):
+            s16()
+        ms16 = timed(s16, max(10, args.steps // 4))
+        bytes16 = sum(op_bytes(sh, w16.batch, c16).values())
+        b16 = {"ms_per_step": round(ms16, 4), "ms_per_token": round(ms16 / w16.batch, 4),
+               "tokens_per_s": round(w16.batch * 1e3 / ms16, 1), "bytes_per_step": int(bytes16),
+               "effective_GBps": round(bytes16 / (ms16 * 1e-3) / 1e9, 1),
+               "pct_of_peak": round(100 * bytes16 / (ms16 * 1e-3) / PEAK_HBM, 2),
+               "ctx": {"min": int(c16.min()), "max": int(c16.max()), "sum": int(c16.sum())},
+               "graph": True, "inputs": "device"}
+        m16.close()
+        del kv16, ws16, dev16, lg16
+        print(f"[bench] step_b16 {ms16:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # ---- prefill of a 512-token prompt (time to first token), same weights
+    pf = None
+    if args.workload == "step_b1" and not args.no_extra:
+        wp = wl.prefill_512()
+        mp, kvp, wsp = attach(dm, wp)
+        n = int(wp.ctx_lens[0])
+        ptok = wp.prompt_tokens(n)
+        pws = torch.empty(w4.w4_prefill_workspace_bytes(dm.cfg, n, wp.max_pages), dtype=torch.uint8, device="cuda")
+        plog = torch.empty(sh.vocab, dtype=torch.float16, device="cuda")
+        run_pf = lambda: mp.w4_prefill(ptok, 0, wp.page_tables[0], pws, plog)
+        for _ in range(2):
+            run_pf()
+        torch.cuda.synchronize()
+        reps = 10
+        t = time.perf_counter()
+        for _ in range(reps):
+            run_pf()
+        torch.cuda.synchronize()
+        ttft = (time.perf_counter() - t) / reps * 1e3
+        gpu_ms = timed(run_pf, reps)
+        fl = prefill_flops(sh, n)
+        pf = {"tokens": n, "ttft_ms": round(ttft, 3), "clock": "host, prompt on the host to logits on the device",
+              "gpu_ms": round(gpu_ms, 3), "flop": int(fl),
+              "TFLOPs": round(fl / (gpu_ms * 1e-3) / 1e12, 1),
+              "pct_of_mfma_peak": round(100 * fl / (gpu_ms * 1e-3) / PEAK_MFMA_F16, 2),
+              "tokens_per_s": round(n * 1e3 / ttft, 1)}
+        mp.close()
+        del kvp, wsp, pws, plog
+        print(f"[bench] prefill_512 {ttft:.3f} ms", file=sys.stderr, flush=True)
+
     cpu = None if args.no_cpu else cpu_baseline(w)
 
     tok_s = B * 1e3 / ms
@@ -336,6 +422,8 @@ def main():
                      "traffic": read_traffic(dom, digest), "bytes_per_launch": int(dom_bytes),
                      "us_per_launch": round(op_ms[dom] * 1e3, 2), "source_digest": digest},
         "generate": gen,
+        "step_b16": b16,
+        "prefill_512": pf,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
