@@ -51,23 +51,34 @@ def test_graph_equals_eager_and_replays_are_deterministic():
 
 def test_graph_replays_follow_changing_inputs():
     """One captured graph, new tokens / contexts / page tables every call: each
-    replay equals an eager run of the same inputs."""
+    of 1000 replays equals an eager run of the same inputs ("Building a Custom
+    LLM Inference Runtime on H100", The Three Critical Bugs, Bug 3: inputs
+    are staged before the launch, never inside the captured graph)."""
     dm = small_model([60, 30])
-    w = dm.w
+    w, m = dm.w, dm.model
     rs = np.random.default_rng(3)
-    for it in range(6):
-        ctx = rs.integers(1, 64, 2).astype(np.int32)
+    out_g = torch.empty((2, SMALL.vocab), dtype=torch.float16, device="cuda")   # one output: one graph
+    out_e = torch.empty_like(out_g)
+    snap = torch.empty_like(dm.kv_cache)
+    for it in range(1000):
+        c0 = int(rs.integers(1, 16 * w.max_pages + 1))
+        room = min(w.max_pages, w.num_pages - (c0 + 15) // 16)     # pages left for the second sequence
+        ctx = np.array([c0, rs.integers(1, 16 * room + 1)], np.int32)
         pt = np.full_like(w.page_tables, -1)
         perm = rs.permutation(w.num_pages).astype(np.int32)
         n0, n1 = (ctx + 15) // 16
         pt[0, :n0] = perm[:n0]
         pt[1, :n1] = perm[n0:n0 + n1]
-        inputs = (rs.integers(0, SMALL.vocab, 2).astype(np.int32), ctx - 1, pt, ctx)
-        snap = dm.kv_cache.clone()
-        g = step(dm, True, inputs)
+        toks = rs.integers(0, SMALL.vocab, 2).astype(np.int32)
+        snap.copy_(dm.kv_cache)
+        m.w4_set_graph(True)
+        m.decode_step(toks, ctx - 1, pt, ctx, out_g)
         dm.kv_cache.copy_(snap)
-        e = step(dm, False, inputs)
-        assert np.array_equal(g.view(np.uint16), e.view(np.uint16)), f"replay {it}"
+        m.w4_set_graph(False)
+        m.decode_step(toks, ctx - 1, pt, ctx, out_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)), f"replay {it}"
+    assert m.w4_device_errors() == 0
 
 
 def test_device_inputs_match_host_inputs():
