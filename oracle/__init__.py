@@ -31,4 +31,10 @@ Modules:
   packing  -- reads the packed weight formats of the library back into (q, s)
   generate -- greedy token loop over ``decode`` (argmax, positions advancing
               across page boundaries, optional teacher forcing)
+  prefill  -- a prompt through the model at once (every row the decode step
+              of its token at its position; causal attention over the pages)
+  quantize -- the symmetric INT4 group-128 quantiser (fp16 -> q, s)
+  w4a8     -- the W4A8 variant of the projections (INT8 activations, integer
+              inner sums), measured against the W4A16 path
+  runs     -- whole synthetic workloads through the above
 """
