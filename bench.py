@@ -383,6 +383,37 @@ def main():
         del kvp, wsp, pws, plog
         print(f"[bench] prefill_512 {ttft:.3f} ms", file=sys.stderr, flush=True)
 
+    # ---- the W4A8 variant against the W4A16 arithmetic (same one-wavefront-
+    # per-tile decomposition) and the step's own projection kernel, on this
+    # layer-0 weights' gate/up and down shapes
+    variants = None
+    if args.workload == "step_b1" and not args.no_extra:
+        variants = {}
+        lw0 = w.layer(0)
+        for name, (qq, ss), n_, k_ in (("gate_up", (lw0.gate_up_q, lw0.gate_up_s), 2 * sh.ffn, sh.hidden),
+                                       ("down", (lw0.down_q, lw0.down_s), sh.hidden, sh.ffn)):
+            packed = torch.from_numpy(w4.pack_weights_w4g128(qq, ss)).cuda()
+            for bsz in ((1, 16) if name == "gate_up" else (1,)):
+                xv = torch.randn((bsz, k_), device="cuda").half()
+                yv = torch.empty((bsz, n_), dtype=torch.float16, device="cuda")
+                res = {}
+                for label, fn in (("w4a8_us", lambda: w4.w4_gemv_variant(packed, xv, yv, n_, k_, bsz, True)),
+                                  ("w4a16_same_split_us", lambda: w4.w4_gemv_variant(packed, xv, yv, n_, k_, bsz, False)),
+                                  ("w4a16_decode_kernel_us", lambda: w4.w4_gemv(packed, xv, yv, n_, k_, bsz))):
+                    fn()                      # first call outside the capture (launch attributes)
+                    torch.cuda.synchronize()
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        for _ in range(10):
+                            fn()
+                    g.replay()
+                    res[label] = round(timed(g.replay, args.op_reps) / 10 * 1e3, 2)
+                    del g
+                res["bytes"] = int(w4_bytes(n_, k_))
+                variants[f"{name}_b{bsz}"] = res
+            del packed
+        print(f"[bench] variants {variants}", file=sys.stderr, flush=True)
+
     cpu = None if args.no_cpu else cpu_baseline(w)
 
     tok_s = B * 1e3 / ms
@@ -424,6 +455,7 @@ def main():
         "generate": gen,
         "step_b16": b16,
         "prefill_512": pf,
+        "w4a8_variant": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

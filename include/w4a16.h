@@ -366,6 +366,20 @@ void* w4_model_buffer(w4_model* model, int32_t which, int32_t* row_stride);
  * prefill GEMM (the projections of w4_prefill). */
 int  w4_gemv(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
              int32_t batch, void* stream);
+/* The W4A8 variant and its same-decomposition W4A16 twin (measurement of
+ * the pages' finding that INT8 activations lost to the INT4 unpack on
+ * Hopper, "How to build your own LLM runtime from scratch", Architectural
+ * decisions and optimizations). y = W x for a w4g128-packed W (role PLAIN)
+ * with one wavefront per 16-row tile; int8_activations = 1: each row of x is
+ * quantised to INT8 (s_x = max|x| / 127, x_q = round-half-even(x / s_x) in
+ * float32, clamped to +-127) and multiplied on the INT8 matrix cores with
+ * exact integer group sums, y = fp16(s_x sum_g s_g sum q x_q); 0: the W4A16
+ * arithmetic of w4_gemv (fp16 activations, fp32 accumulation). x: device fp16
+ * [batch][k]; y: device fp16 [batch][n]; 1 <= batch <= 16 and the staged rows
+ * must fit the LDS ((batch + 1) * ceil(k / 128) * 128 bytes, twice that for
+ * fp16, at most about 160 KiB: W4_EINVAL otherwise). */
+int  w4_gemv_variant(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
+                     int32_t batch, int32_t int8_activations, void* stream);
 /* y = fp16(W x) for a pack_weights_f16 W, fp32 accumulation, batch 1..16. */
 int  w4_gemv_f16(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
                  int32_t batch, void* stream);

@@ -88,6 +88,7 @@ _SIGS = {
     "paged_attention_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                        c_int32, c_int32, c_int32, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
     "w4_prefill_workspace_bytes": (c_size_t, [POINTER(w4_config), c_int32, c_int32]),
+    "w4_gemv_variant": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "w4_prefill_buffer": (c_int64, [POINTER(w4_config), c_int32, c_int32, c_int32, POINTER(c_int32)]),
     "w4_prefill": (c_int, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
     "kv_write_pages": (c_int, [POINTER(w4_config), c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int32,
@@ -428,4 +429,11 @@ def w4_prefill_buffer(cfg: w4_config, n_tokens: int, max_pages: int, which: int)
     if off < 0:
         raise W4Error(W4_EINVAL, "w4_prefill_buffer: bad arguments")
     return off, stride.value
+
+
+def w4_gemv_variant(packed, x, y, n: int, k: int, batch: int = 1, int8_activations: bool = True,
+                    stream=None) -> None:
+    """W4A8 (int8_activations) or same-decomposition W4A16 GEMV, batch 1..16."""
+    _check(lib().w4_gemv_variant(_ptr(packed), _ptr(x), _ptr(y), n, k, batch, int(int8_activations),
+                                 _stream(stream)))
 

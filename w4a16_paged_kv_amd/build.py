@@ -22,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["host.cpp", "model.cpp", "gemv.hip", "attention.hip", "sample.hip", "prefill.hip"]
+SOURCES = ["host.cpp", "model.cpp", "gemv.hip", "attention.hip", "sample.hip", "prefill.hip", "w4a8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

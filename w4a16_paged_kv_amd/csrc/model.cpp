@@ -612,6 +612,33 @@ W4_EXPORT int w4_gemv(const void* packed, const uint16_t* x, uint16_t* y, int32_
   return W4_OK;
 }
 
+W4_EXPORT int w4_gemv_variant(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
+                              int32_t batch, int32_t int8_activations, void* stream) {
+  clear_error();
+  if (!packed || !x || !y) return fail(W4_EINVAL, "w4_gemv_variant: null pointer");
+  if (n <= 0 || k <= 0 || k % 8 || batch < 1 || batch > 16)
+    return fail(W4_EINVAL, "w4_gemv_variant: n=%d k=%d (multiple of 8) batch=%d (1..16)", n, k, batch);
+  if (!aligned256(packed) || !aligned256(x) || !aligned256(y))
+    return fail(W4_EALIGN, "w4_gemv_variant: pointer not 256-byte aligned");
+  const size_t lds = w4ax_lds_bytes(w4_groups(k), batch, int8_activations != 0);
+  if (lds > (size_t)160 * 1024)
+    return fail(W4_EINVAL, "w4_gemv_variant: %d rows of %d columns need %zu bytes of LDS (at most 160 KiB)", batch,
+                k, lds);
+  W4AxArgs a{};
+  a.w = static_cast<const uint8_t*>(packed);
+  a.n = n;
+  a.k = k;
+  a.tiles = w4_tiles(n);
+  a.groups = w4_groups(k);
+  a.x = x;
+  a.x_stride = k;
+  a.y = y;
+  a.y_stride = n;
+  a.batch = batch;
+  W4_LAUNCH(launch_w4ax_gemv(a, int8_activations != 0, static_cast<hipStream_t>(stream)));
+  return W4_OK;
+}
+
 W4_EXPORT int w4_gemv_f16(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, int32_t k,
                           int32_t batch, void* stream) {
   clear_error();

@@ -163,6 +163,19 @@ struct PrefillAttnArgs {
   uint32_t* err;
 };
 
+// The W4A8 / same-split W4A16 variant GEMV (w4a8.hip): one wavefront per tile.
+struct W4AxArgs {
+  const uint8_t* w;       // packed w4g128 weights
+  int32_t n, k, tiles, groups;
+  const uint16_t* x;      // fp16 [batch][x_stride]
+  int32_t x_stride;
+  uint16_t* y;            // fp16 [batch][y_stride]
+  int32_t y_stride;
+  int32_t batch;          // 1..16
+};
+size_t w4ax_lds_bytes(int groups, int batch, bool int8);
+hipError_t launch_w4ax_gemv(const W4AxArgs& a, bool int8, hipStream_t s);
+
 // Copies between natural-layout K/V rows [n][Hkv][D] and one layer's pages.
 struct KvCopyArgs {
   uint16_t* k_pool;           // [P][Hkv][16][D]
