@@ -376,17 +376,30 @@ __device__ __forceinline__ float mfma_block_b1(const u4_t w, const uint16_t* __r
   return mfma_block(w, xl, mlo, mhi)[0];
 }
 
-// The QKV epilogue's per-thread RoPE rotation and the token's K/V slot
-// (token plan, written by an earlier launch): thread i < tw * 8 of virtual
-// workgroup vb rotates pair i % 8 of tile vb * tw + i / 8.
+// What a batch-1 epilogue thread reads besides the products, loaded at the
+// start of the launch so the epilogue does not wait on memory: the QKV
+// epilogue's RoPE rotation and the token's K/V slot (token plan, written by
+// an earlier launch; thread i < tw * 8 of virtual workgroup vb rotates pair
+// i % 8 of tile vb * tw + i / 8), and the residual element of a residual
+// epilogue (thread i < tw * 16 adds row 16 (vb * tw + i / 16) + i % 16; the
+// residual is written only by that same thread, after this read).
 struct QkvPre {
   float c, s;
   int slot;
+  float resid;
 };
 
 template <int EPI>
 __device__ __forceinline__ QkvPre qkv_pre(const GemvArgs& a, int vb, int tw) {
-  QkvPre p{1.f, 0.f, -1};
+  QkvPre p{1.f, 0.f, -1, 0.f};
+  if (EPI == EPI_RESID) {
+    // every thread loads, from a clamped address (no branch around the load,
+    // which would make the compiler wait for it here); only the epilogue's
+    // threads use the value
+    const int tt = min(vb * tw + (int)threadIdx.x / 16, a.tiles - 1);
+    const int row = min(kTileRows * tt + (int)threadIdx.x % 16, a.n - 1);
+    p.resid = h2f(ld16_agent(a.resid + row));
+  }
   if (EPI == EPI_QKV && (int)threadIdx.x < tw * 8) {
     const int tt = vb * tw + threadIdx.x / 8;
     if (tt < a.tiles) {
@@ -519,7 +532,10 @@ struct GemvB1 {
         const int i = threadIdx.x % per;
         if (EPI == EPI_QKV)
           epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], pre.c, pre.s, pre.slot);
-        else
+        else if (EPI == EPI_RESID) {
+          const int row = kTileRows * tt + i;
+          if (row < a.n) st16_agent(a.y + row, f2h(vals[tl * 16 + i] + pre.resid));
+        } else
           epilogue<EPI>(a, 0, tt, i, vals + tl * 16);
       }
     }
@@ -640,7 +656,10 @@ struct GemvB1Range {
         const int i = threadIdx.x % per;
         if (EPI == EPI_QKV)
           epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], pre.c, pre.s, pre.slot);
-        else
+        else if (EPI == EPI_RESID) {
+          const int row = kTileRows * tt + i;
+          if (row < a.n) st16_agent(a.y + row, f2h(vals[tl * 16 + i] + pre.resid));
+        } else
           epilogue<EPI>(a, 0, tt, i, vals + tl * 16);
       }
     }
