@@ -23,31 +23,25 @@ namespace w4 {
 // ---------------------------------------------------------------- W4A16 GEMM
 // Workgroup = WM x WN wavefronts; wavefront (wm, wn) computes rows
 // [m0 + 16 MR wm, +16 MR) x weight tiles [t0 + NTW wn, +NTW) as MR x NTW
-// 16x16 blocks of v_mfma_f32_16x16x32_f16 (A = activation rows in the MFMA
-// k-slot order from LDS, B = the lane's 16 bytes of a packed block, exactly
-// dequantised as in the decode GEMV). Per 128-column group the four MFMAs of
-// a block start from zero and the group's fp32 scale is applied to the sum
-// (acc += s * D), so the result is the fp32 sum over groups of exact
-// per-group products, as at batch 1.
+// 16x16 blocks of v_mfma_f32_16x16x32_f16 (A = activation rows from LDS,
+// B = the lane's 16 bytes of a packed block, exactly dequantised as in the
+// decode GEMV). Per 128-column group the four MFMAs of a block start from
+// zero and the group's fp32 scale is applied to the sum (acc += s * D), so
+// the result is the fp32 sum over groups of exact per-group products, as at
+// batch 1.
 //
-// The activation rows of a group (M_T x 128 fp16) are staged in LDS in slot
-// order (slot_word: each thread converts one natural 8-column word with the
-// words of its 4-lane quad), rows padded by 16 bytes so the 16 rows one
-// ds_read_b128 touches fall in distinct banks; two buffers, the next group's
-// rows and weight blocks loaded while the current group is multiplied.
-constexpr int kPfPad = 8;  // fp16 padding per staged row
-
-template <int WM, int WN, int MR, int NTW>
-struct PfTile {
-  static constexpr int kThreads = WM * WN * 64;
-  static constexpr int kRows = 16 * MR * WM;         // M_T
-  static constexpr int kTiles = NTW * WN;            // weight tiles per workgroup
-  static constexpr int kRowStride = kGroup + kPfPad;  // fp16 per staged row
-  static constexpr int kWords = kRows * 16 / kThreads;  // staged words per thread per group
-  static constexpr size_t kLdsBytes = (size_t)2 * kRows * kRowStride * 2;
-  static_assert(kRows * 16 % kThreads == 0, "whole staging rounds");
-  static_assert(kThreads % 16 == 0, "a thread keeps its word index across rounds");
-};
+// The operands move by the 16-byte global-to-LDS loads of gfx950
+// (global_load_lds_dwordx4: lane L's 16 bytes land at the LDS base + 16 L)
+// into a ring of three stages, each holding one 128-column group: the
+// activation rows in natural order (row r's 16-byte word w at physical slot
+// w ^ (r & 15), so the 16 rows one ds_read_b128 touches are in distinct
+// banks), the workgroup's packed weight blocks, and each wavefront's scales.
+// Two groups are in flight while one is multiplied, with no registers spent
+// on staging. The activation operand of MFMA r is picked from two natural
+// words by register choice (the packed nibble order: 32-bit pairs e and
+// e + 2 of words j0 and j0 + 1, e = r % 2, j0 = 2 (r / 2)); for odd r the
+// weight nibbles are shifted down before the AND-OR, so they come out as q
+// (not 16 q) and the activations need no scaling.
 
 // The prefill epilogue of one accumulator value: lane l holds weight row
 // l & 15 of tile t for activation row m; its partner (weight row (l & 15) ^ 8)
@@ -73,57 +67,78 @@ __device__ __forceinline__ void pf_epilogue(const GemvArgs& a, int m, int t, int
   }
 }
 
+template <int WM, int WN, int MR, int NTW>
+struct PfRing {
+  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int kRows = 16 * MR * WM;
+  static constexpr int kTiles = NTW * WN;
+  static constexpr int kABytes = kRows * kGroup * 2;
+  static constexpr int kWBytes = kTiles * 1024;
+  static constexpr int kSBytes = WM * WN * 256;        // one 4-byte load per lane of each wavefront
+  static constexpr int kStage = kABytes + kWBytes + kSBytes;
+  static constexpr int kAInst = kABytes / (kThreads * 16);
+  static constexpr int kWInst = kWBytes / (kThreads * 16);
+  static constexpr int kInst = kAInst + kWInst + 1;    // vector-memory instructions per stage per thread
+  static_assert(kABytes % (kThreads * 16) == 0 && kWBytes % (kThreads * 16) == 0, "whole DMA rounds");
+  static_assert(NTW * 32 <= 256, "a wavefront's scales fit one 4-byte load");
+  static_assert(kInst < 64, "vmcnt range");
+};
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
+}
+// lane L's 4 bytes land at the LDS base + 4 L
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt with vmcnt <= N and no wait on the other counters (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <int EPI, int WM, int WN, int MR, int NTW>
-__global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_kernel(GemvArgs a) {
-  using T = PfTile<WM, WN, MR, NTW>;
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [2][kRows][kRowStride]
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_dma_kernel(GemvArgs a) {
+  using T = PfRing<WM, WN, MR, NTW>;
+  __shared__ __align__(16) uint8_t ring0[T::kStage];
+  __shared__ __align__(16) uint8_t ring1[T::kStage];
+  __shared__ __align__(16) uint8_t ring2[T::kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
-  const int m0 = blockIdx.x * T::kRows;               // M tiles fastest: neighbours share weights
-  const int t0 = blockIdx.y * T::kTiles + wn * NTW;   // this wavefront's first weight tile
+  const int m0 = blockIdx.x * T::kRows;
+  const int tg0 = blockIdx.y * T::kTiles;              // the workgroup's first weight tile
   const int G = a.groups;
+  const uint8_t* wsrc = a.w;
+  const uint8_t* ssrc = a.w + (size_t)a.tiles * G * 1024;
+  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x);
 
-  // staging: thread t takes word t % 16 of rows t / 16 + r * (threads / 16)
-  const int sw = threadIdx.x & 15;
-  const int srow0 = threadIdx.x >> 4;
-  constexpr int kRowStep = T::kThreads / 16;
-  const __amdgpu_buffer_rsrc_t rx = coherent_rsrc(a.x);
-  u4_t st[T::kWords];
-  auto stage_load = [&](int g) {
-    const int c = g * kGroup + 8 * sw;
+  // one stage's loads: A (row r, physical word p <- logical word p ^ (r & 15)),
+  // W (the workgroup's blocks in tile order), S (word l % 8 of tile (l / 8) % NTW
+  // of the wavefront's tiles: every lane loads, so every wavefront issues the same
+  // count of loads on every path; lanes past 8 NTW repeat words nobody reads)
+  auto issue = [&](int g, uint8_t* st) {
 #pragma unroll
-    for (int r = 0; r < T::kWords; ++r) {
-      const int m = min(m0 + srow0 + r * kRowStep, a.batch - 1);
-      st[r] = ld128_agent(rx, 2 * (m * a.x_stride + min(c, a.k - 8)));
+    for (int i = 0; i < T::kAInst; ++i) {
+      const int ci = tid + i * T::kThreads;            // 16-byte chunk of the A region
+      const int r = ci >> 4, p = ci & 15;
+      const int m = min(m0 + r, a.batch - 1);
+      const int col = min(g * kGroup + 8 * (p ^ (r & 15)), a.k - 8);
+      dma16(xsrc + 2 * ((size_t)m * a.x_stride + col), st + 16 * (ci - lane));
     }
-  };
-  auto stage_store = [&](int g, int buf) {
-    const int c = g * kGroup + 8 * sw;
-    const int e = sw & 1;
 #pragma unroll
-    for (int r = 0; r < T::kWords; ++r) {
-      const int row = srow0 + r * kRowStep;
-      u4_t v = st[r];
-      if (m0 + row >= a.batch || c >= a.k) v = (u4_t){0u, 0u, 0u, 0u};
-      const u4_t o = slot_word(v, e);  // every lane of the quad takes part
-      *reinterpret_cast<u4_t*>(xs + ((size_t)buf * T::kRows + row) * T::kRowStride + 8 * sw) = o;
+    for (int i = 0; i < T::kWInst; ++i) {
+      const int ci = tid + i * T::kThreads;
+      const int t = min(tg0 + (ci >> 6), a.tiles - 1);
+      dma16(wsrc + ((size_t)t * G + g) * 1024 + 16 * (ci & 63), st + T::kABytes + 16 * (ci - lane));
     }
-  };
-
-  // weights: the lane's 16 bytes of block (t, g) and the scale of row lane & 15
-  const u4_t* wbase = reinterpret_cast<const u4_t*>(a.w);
-  const uint16_t* sbase = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024);
-  u4_t wc[NTW], wn_[NTW];
-  uint32_t sc[NTW], sn[NTW];
-  auto w_load = [&](int g, u4_t* wv, uint32_t* sv) {
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int t = min(t0 + j, a.tiles - 1);
-      const size_t blk = (size_t)t * G + g;
-      wv[j] = __builtin_nontemporal_load(wbase + blk * 64 + lane);
-      sv[j] = sbase[blk * 16 + (lane & 15)];
+    {
+      const int t = min(tg0 + wn * NTW + ((lane >> 3) & (NTW - 1)), a.tiles - 1);
+      dma4(ssrc + ((size_t)t * G + g) * 32 + 4 * (lane & 7), st + T::kABytes + T::kWBytes + wave * 256);
     }
   };
 
@@ -132,64 +147,104 @@ __global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_kernel(GemvArgs 
   for (int i = 0; i < MR; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = (f4_t){0.f, 0.f, 0.f, 0.f};
-  const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
+  const uint32_t mlo = vgpr_const(kMaskLo);
+  const h2_t bias = (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+  const int x15 = lane & 15, c4 = 4 * (lane >> 4);   // row within a block, first word of the lane's chunk
 
-  stage_load(0);
-  w_load(0, wc, sc);
-  stage_store(0, 0);
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    const bool more = g + 1 < G;
-    if (more) {
-      stage_load(g + 1);
-      w_load(g + 1, wn_, sn);
-    }
-    const uint16_t* xb = xs + ((size_t)buf * T::kRows + 16 * MR * wm + (lane & 15)) * T::kRowStride +
-                         32 * (lane >> 4);
-    f4_t d[MR][NTW];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t mk = (r & 1) ? mhi : mlo;
-      const h2_t bias = (r & 1) ? (h2_t){(_Float16)1152.0f, (_Float16)1152.0f}
-                                : (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
-      h8_t bw[NTW];
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const uint32_t w0 = wc[j][2 * (r >> 1)], w1 = wc[j][2 * (r >> 1) + 1];
-        auto q2 = [&](uint32_t v) { return __builtin_bit_cast(uint32_t, as_h2((v & mk) | 0x64006400u) - bias); };
-        bw[j] = __builtin_bit_cast(h8_t, (u4_t){q2(w0), q2(w0 >> 8), q2(w1), q2(w1 >> 8)});
-      }
-#pragma unroll
-      for (int i = 0; i < MR; ++i) {
-        const h8_t av = __builtin_bit_cast(h8_t, *reinterpret_cast<const u4_t*>(xb + (size_t)16 * i * T::kRowStride + 8 * r));
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          d[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[j], r == 0 ? (f4_t){0.f, 0.f, 0.f, 0.f} : d[i][j],
-                                                           0, 0, 0);
-      }
-    }
+  auto compute = [&](const uint8_t* st) {
+    const uint8_t* A = st + (size_t)(16 * MR * wm + x15) * (kGroup * 2);
+    const uint8_t* W = st + T::kABytes + (size_t)(wn * NTW) * 1024 + 16 * lane;
+    const uint16_t* S = reinterpret_cast<const uint16_t*>(st + T::kABytes + T::kWBytes + wave * 256);
+    u4_t wv[NTW];
+    float sc[NTW];
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-      const float s = h2f((uint16_t)sc[j]);
+      wv[j] = *reinterpret_cast<const u4_t*>(W + j * 1024);
+      sc[j] = h2f(S[j * 16 + x15]);
+    }
+    f4_t d[MR][NTW];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {               // word pairs (0, 1) and (2, 3) of the chunk
+      u4_t w0[MR], w1[MR];
+#pragma unroll
+      for (int i = 0; i < MR; ++i) {
+        const uint8_t* row = A + (size_t)16 * i * (kGroup * 2);
+        w0[i] = *reinterpret_cast<const u4_t*>(row + 16 * ((c4 + 2 * jj) ^ x15));
+        w1[i] = *reinterpret_cast<const u4_t*>(row + 16 * ((c4 + 2 * jj + 1) ^ x15));
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * jj + e;
+        h8_t bw[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const uint32_t p0 = wv[j][2 * jj], p1 = wv[j][2 * jj + 1];
+          auto q2 = [&](uint32_t v) { return __builtin_bit_cast(uint32_t, as_h2((v & mlo) | 0x64006400u) - bias); };
+          bw[j] = e ? __builtin_bit_cast(h8_t, (u4_t){q2(p0 >> 4), q2(p0 >> 12), q2(p1 >> 4), q2(p1 >> 12)})
+                    : __builtin_bit_cast(h8_t, (u4_t){q2(p0), q2(p0 >> 8), q2(p1), q2(p1 >> 8)});
+        }
+#pragma unroll
+        for (int i = 0; i < MR; ++i) {
+          const h8_t av = __builtin_bit_cast(h8_t, (u4_t){w0[i][e], w0[i][e + 2], w1[i][e], w1[i][e + 2]});
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+            d[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[j], r == 0 ? (f4_t){0.f, 0.f, 0.f, 0.f} : d[i][j],
+                                                             0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int i = 0; i < MR; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(s, d[i][j][q], acc[i][j][q]);
-    }
-    if (more) {
-      stage_store(g + 1, buf ^ 1);
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        wc[j] = wn_[j];
-        sc[j] = sn[j];
-      }
-    }
-    __syncthreads();
-  }
+        for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(sc[j], d[i][j][q], acc[i][j][q]);
+  };
 
-  // lane l holds D[row 4 (l >> 4) + q][weight row l & 15] of each block
+  // Ring of three stages: group g in ring g % 3, two groups in flight. Every
+  // stage issues exactly kInst loads per thread (past the last group they
+  // reload group G - 1 into the slot no later stage reads), so one wait form
+  // holds everywhere: at stage g the loads of g + 1 are the only ones newer
+  // than those of g. Columns at or past k (a partial last group) are zeroed
+  // in LDS before the last group is multiplied, as the decode GEMV zeroes them.
+  const bool ragged = (a.k & (kGroup - 1)) != 0;
+  auto stage = [&](int g, uint8_t* cur, uint8_t* nxt) {
+    // this thread's loads of stage g are done; after the barrier every
+    // thread's are, and every wavefront has consumed its reads of stage
+    // g - 1 (whose ring slot the next loads overwrite). A bare s_barrier:
+    // __syncthreads() would also wait for the loads still in flight.
+    wait_vm<T::kInst>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (ragged && g == G - 1) {                     // uniform across the workgroup
+#pragma unroll
+      for (int i = 0; i < T::kAInst; ++i) {
+        const int ci = tid + i * T::kThreads;
+        const int r = ci >> 4, p = ci & 15;
+        if (g * kGroup + 8 * (p ^ (r & 15)) >= a.k) *reinterpret_cast<u4_t*>(cur + 16 * ci) = (u4_t){0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    issue(min(g + 2, G - 1), nxt);
+    compute(cur);
+  };
+  issue(0, ring0);
+  issue(min(1, G - 1), ring1);
+  int g = 0;
+  for (; g + 3 <= G; g += 3) {
+    stage(g, ring0, ring2);
+    stage(g + 1, ring1, ring0);
+    stage(g + 2, ring2, ring1);
+  }
+  if (g < G) {                                       // nested, so no path reads a slot still being filled
+    stage(g, ring0, ring2);
+    if (g + 1 < G) stage(g + 1, ring1, ring0);
+  }
+  wait_vm<0>();                                      // no load may land in LDS after the workgroup ends
+
   const int i16 = lane & 15;
+  const int t0 = tg0 + wn * NTW;
 #pragma unroll
   for (int i = 0; i < MR; ++i)
 #pragma unroll
@@ -205,14 +260,9 @@ __global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_kernel(GemvArgs 
 
 template <int EPI, int WM, int WN, int MR, int NTW>
 static hipError_t launch_pf_tile(const GemvArgs& a, hipStream_t s) {
-  using T = PfTile<WM, WN, MR, NTW>;
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&w4_gemm_prefill_kernel<EPI, WM, WN, MR, NTW>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::kLdsBytes);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((w4_gemm_prefill_kernel<EPI, WM, WN, MR, NTW>),
-                     dim3(ceil_div(a.batch, T::kRows), ceil_div(a.tiles, T::kTiles)), dim3(T::kThreads),
-                     T::kLdsBytes, s, a);
+  using T = PfRing<WM, WN, MR, NTW>;
+  hipLaunchKernelGGL((w4_gemm_prefill_dma_kernel<EPI, WM, WN, MR, NTW>),
+                     dim3(ceil_div(a.batch, T::kRows), ceil_div(a.tiles, T::kTiles)), dim3(T::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
