@@ -37,11 +37,11 @@ namespace w4 {
 // w ^ (r & 15), so the 16 rows one ds_read_b128 touches are in distinct
 // banks), the workgroup's packed weight blocks, and each wavefront's scales.
 // Two groups are in flight while one is multiplied, with no registers spent
-// on staging. The activation operand of MFMA r is picked from two natural
-// words by register choice (the packed nibble order: 32-bit pairs e and
-// e + 2 of words j0 and j0 + 1, e = r % 2, j0 = 2 (r / 2)); for odd r the
-// weight nibbles are shifted down before the AND-OR, so they come out as q
-// (not 16 q) and the activations need no scaling.
+// on staging. MFMA r takes word r of the lane's 16 weight bytes, dequantised
+// in natural column order (the nibbles of columns 2i and 2i + 1 sit at bits
+// 4i and 16 + 4i, so the word shifted right by 4i and masked gives that pair
+// as one fp16x2), so its activation operand is the row's natural 16-byte
+// word 4 (lane / 16) + r, read from LDS as is.
 
 // The prefill epilogue of one accumulator value: lane l holds weight row
 // l & 15 of tile t for activation row m; its partner (weight row (l & 15) ^ 8)
@@ -164,33 +164,21 @@ __global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_dma_kernel(GemvA
     }
     f4_t d[MR][NTW];
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {               // word pairs (0, 1) and (2, 3) of the chunk
-      u4_t w0[MR], w1[MR];
+    for (int r = 0; r < 4; ++r) {                  // MFMA r: word r of the lane's 16-byte chunk
+      h8_t bw[NTW];
 #pragma unroll
-      for (int i = 0; i < MR; ++i) {
-        const uint8_t* row = A + (size_t)16 * i * (kGroup * 2);
-        w0[i] = *reinterpret_cast<const u4_t*>(row + 16 * ((c4 + 2 * jj) ^ x15));
-        w1[i] = *reinterpret_cast<const u4_t*>(row + 16 * ((c4 + 2 * jj + 1) ^ x15));
+      for (int j = 0; j < NTW; ++j) {
+        const uint32_t p = wv[j][r];
+        auto q2 = [&](uint32_t v) { return __builtin_bit_cast(uint32_t, as_h2((v & mlo) | 0x64006400u) - bias); };
+        bw[j] = __builtin_bit_cast(h8_t, (u4_t){q2(p), q2(p >> 4), q2(p >> 8), q2(p >> 12)});
       }
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = 2 * jj + e;
-        h8_t bw[NTW];
+      for (int i = 0; i < MR; ++i) {
+        const h8_t av = *reinterpret_cast<const h8_t*>(A + (size_t)16 * i * (kGroup * 2) + 16 * ((c4 + r) ^ x15));
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const uint32_t p0 = wv[j][2 * jj], p1 = wv[j][2 * jj + 1];
-          auto q2 = [&](uint32_t v) { return __builtin_bit_cast(uint32_t, as_h2((v & mlo) | 0x64006400u) - bias); };
-          bw[j] = e ? __builtin_bit_cast(h8_t, (u4_t){q2(p0 >> 4), q2(p0 >> 12), q2(p1 >> 4), q2(p1 >> 12)})
-                    : __builtin_bit_cast(h8_t, (u4_t){q2(p0), q2(p0 >> 8), q2(p1), q2(p1 >> 8)});
-        }
-#pragma unroll
-        for (int i = 0; i < MR; ++i) {
-          const h8_t av = __builtin_bit_cast(h8_t, (u4_t){w0[i][e], w0[i][e + 2], w1[i][e], w1[i][e + 2]});
-#pragma unroll
-          for (int j = 0; j < NTW; ++j)
-            d[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[j], r == 0 ? (f4_t){0.f, 0.f, 0.f, 0.f} : d[i][j],
-                                                             0, 0, 0);
-        }
+        for (int j = 0; j < NTW; ++j)
+          d[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[j], r == 0 ? (f4_t){0.f, 0.f, 0.f, 0.f} : d[i][j],
+                                                           0, 0, 0);
       }
     }
 #pragma unroll
