@@ -25,10 +25,13 @@ SMALL = wl.Shape(hidden=448, n_heads=7, n_kv_heads=1, head_dim=64, ffn=1536, voc
 
 @pytest.mark.parametrize("n,k,m", [(576, 448, 37), (3072, 448, 17), (448, 1536, 130), (40, 200, 300),
                                    (4608, 3584, 512), (3584, 3584, 512), (37888, 3584, 512),
-                                   (3584, 18944, 512), (3584, 3584, 129)])
+                                   (3584, 18944, 512), (3584, 3584, 129), (40000, 200, 300),
+                                   (33000, 1000, 257)])
 def test_prefill_gemm_matches_oracle(n, k, m):
-    """w4_gemv with more than 16 rows runs the prefill GEMM (128 x 128 or
-    64 x 128 tiles, partial row tiles, a partial last group at k = 448)."""
+    """w4_gemv with more than 16 rows runs the prefill GEMM: 32-row tiles with
+    a three-stage ring, or (1024 and more 64-row workgroups: the gate/up shape,
+    40000 x 200 and 33000 x 1000) 64-row tiles with a two-stage ring; partial
+    row tiles, partial last groups (k = 448, 200, 1000)."""
     print(f"prefill gemm n={n} k={k} rows={m}", flush=True)
     q, s = wl.int4_matrix(81, 0, 0, n, k)
     x = wl.f16_normal(wl.rng(81, 0, 1), (m, k))

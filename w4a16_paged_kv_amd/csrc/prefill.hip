@@ -30,18 +30,18 @@ namespace w4 {
 // the result is the fp32 sum over groups of exact per-group products, as at
 // batch 1.
 //
-// The operands move by the 16-byte global-to-LDS loads of gfx950
-// (global_load_lds_dwordx4: lane L's 16 bytes land at the LDS base + 16 L)
-// into a ring of three stages, each holding one 128-column group: the
+// The operands move by the 16-byte buffer-to-LDS loads of gfx950
+// (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at the LDS base + 16 L)
+// into a ring of two or three stages, each holding one 128-column group: the
 // activation rows in natural order (row r's 16-byte word w at physical slot
 // w ^ (r & 15), so the 16 rows one ds_read_b128 touches are in distinct
 // banks), the workgroup's packed weight blocks, and each wavefront's scales.
-// Two groups are in flight while one is multiplied, with no registers spent
-// on staging. MFMA r takes word r of the lane's 16 weight bytes, dequantised
-// in natural column order (the nibbles of columns 2i and 2i + 1 sit at bits
-// 4i and 16 + 4i, so the word shifted right by 4i and masked gives that pair
-// as one fp16x2), so its activation operand is the row's natural 16-byte
-// word 4 (lane / 16) + r, read from LDS as is.
+// One or two groups are in flight while one is multiplied, with no registers
+// spent on staging. MFMA r takes word r of the lane's 16 weight bytes,
+// dequantised in natural column order (the nibbles of columns 2i and 2i + 1
+// sit at bits 4i and 16 + 4i: a mask of the word, or of the word shifted by
+// 8, gives each pair as one fp16x2), so its activation operand is the row's
+// natural 16-byte word 4 (lane / 16) + r, read from LDS as is.
 
 // The prefill epilogue of one accumulator value: lane l holds weight row
 // l & 15 of tile t for activation row m; its partner (weight row (l & 15) ^ 8)
@@ -67,7 +67,7 @@ __device__ __forceinline__ void pf_epilogue(const GemvArgs& a, int m, int t, int
   }
 }
 
-template <int WM, int WN, int MR, int NTW>
+template <int WM, int WN, int MR, int NTW, int NS>
 struct PfRing {
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int kRows = 16 * MR * WM;
@@ -82,17 +82,22 @@ struct PfRing {
   static_assert(kABytes % (kThreads * 16) == 0 && kWBytes % (kThreads * 16) == 0, "whole DMA rounds");
   static_assert(NTW * 32 <= 256, "a wavefront's scales fit one 4-byte load");
   static_assert(kInst < 64, "vmcnt range");
+  static_assert(NS == 2 || NS == 3, "two or three stages");
 };
 
-typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef __attribute__((address_space(3))) void* lptr_t;
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 16, 0, 0);
+// A raw buffer of `bytes` bytes at base: loads at or past the end read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
-// lane L's 4 bytes land at the LDS base + 4 L
-__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_base, 4, 0, 0);
+// buffer-to-LDS copies: lane L's 16 (4) bytes at voffset + soffset land at the
+// LDS base + 16 L (4 L)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lptr_t)lds_base, 4, voff, soff, 0, 0);
 }
 
 // s_waitcnt with vmcnt <= N and no wait on the other counters (gfx9 encoding)
@@ -101,45 +106,62 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int EPI, int WM, int WN, int MR, int NTW>
-__global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_dma_kernel(GemvArgs a) {
-  using T = PfRing<WM, WN, MR, NTW>;
+// WPE: wavefronts per SIMD the register allocation must allow.
+template <int EPI, int WM, int WN, int MR, int NTW, int NS, int WPE>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void w4_gemm_prefill_dma_kernel(GemvArgs a) {
+  using T = PfRing<WM, WN, MR, NTW, NS>;
+  // separate arrays, so the compiler's wait analysis tells the slot being
+  // filled from the slot being read
   __shared__ __align__(16) uint8_t ring0[T::kStage];
   __shared__ __align__(16) uint8_t ring1[T::kStage];
-  __shared__ __align__(16) uint8_t ring2[T::kStage];
+  __shared__ __align__(16) uint8_t ring2[NS == 3 ? T::kStage : 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
-  const int m0 = blockIdx.x * T::kRows;
+  const int m0 = blockIdx.x * T::kRows;                // row blocks fastest: neighbours share weights
   const int tg0 = blockIdx.y * T::kTiles;              // the workgroup's first weight tile
   const int G = a.groups;
-  const uint8_t* wsrc = a.w;
-  const uint8_t* ssrc = a.w + (size_t)a.tiles * G * 1024;
-  const uint8_t* xsrc = reinterpret_cast<const uint8_t*>(a.x);
+  // Buffer resources rebased at the workgroup's first row and first tile:
+  // every offset fits 32 bits at any batch, a group advances through the
+  // scalar offset alone (no per-load address arithmetic), and the hardware's
+  // range check drops reads past the last row's end (the columns of a partial
+  // last group are zeroed in LDS anyway).
+  const int rows = min(T::kRows, a.batch - m0);      // real rows of this workgroup
+  const int ntl = min(T::kTiles, a.tiles - tg0);      // real tiles of this workgroup
+  const __amdgpu_buffer_rsrc_t rx =
+      range_rsrc(reinterpret_cast<const uint8_t*>(a.x) + 2 * (size_t)m0 * a.x_stride,
+                 2 * ((rows - 1) * a.x_stride + a.k));
+  const __amdgpu_buffer_rsrc_t rw = range_rsrc(a.w + (size_t)tg0 * G * 1024, ntl * G * 1024);
+  const __amdgpu_buffer_rsrc_t rs = range_rsrc(a.w + (size_t)a.tiles * G * 1024 + (size_t)tg0 * G * 32, ntl * G * 32);
 
-  // one stage's loads: A (row r, physical word p <- logical word p ^ (r & 15)),
-  // W (the workgroup's blocks in tile order), S (word l % 8 of tile (l / 8) % NTW
-  // of the wavefront's tiles: every lane loads, so every wavefront issues the same
+  // per-thread load offsets, fixed across groups: A (row r, physical word p
+  // <- logical word p ^ (r & 15); rows past the last repeat it), W (the
+  // workgroup's blocks in tile order), S (word l % 8 of tile (l / 8) % NTW of
+  // the wavefront's tiles: every lane loads, so every wavefront issues the same
   // count of loads on every path; lanes past 8 NTW repeat words nobody reads)
+  uint32_t voa[T::kAInst], vow[T::kWInst];
+#pragma unroll
+  for (int i = 0; i < T::kAInst; ++i) {
+    const int ci = tid + i * T::kThreads;              // 16-byte chunk of the A region
+    const int r = ci >> 4, p = ci & 15;
+    voa[i] = 2 * (min(r, rows - 1) * a.x_stride + 8 * (p ^ (r & 15)));
+  }
+#pragma unroll
+  for (int i = 0; i < T::kWInst; ++i) {
+    const int ci = tid + i * T::kThreads;
+    vow[i] = min(ci >> 6, ntl - 1) * G * 1024 + 16 * (ci & 63);
+  }
+  const uint32_t vos = min(wn * NTW + ((lane >> 3) & (NTW - 1)), ntl - 1) * G * 32 + 4 * (lane & 7);
+
   auto issue = [&](int g, uint8_t* st) {
 #pragma unroll
-    for (int i = 0; i < T::kAInst; ++i) {
-      const int ci = tid + i * T::kThreads;            // 16-byte chunk of the A region
-      const int r = ci >> 4, p = ci & 15;
-      const int m = min(m0 + r, a.batch - 1);
-      const int col = min(g * kGroup + 8 * (p ^ (r & 15)), a.k - 8);
-      dma16(xsrc + 2 * ((size_t)m * a.x_stride + col), st + 16 * (ci - lane));
-    }
+    for (int i = 0; i < T::kAInst; ++i)
+      dma16(rx, voa[i], g * kGroup * 2, st + 16 * (wave * 64 + i * T::kThreads));
 #pragma unroll
-    for (int i = 0; i < T::kWInst; ++i) {
-      const int ci = tid + i * T::kThreads;
-      const int t = min(tg0 + (ci >> 6), a.tiles - 1);
-      dma16(wsrc + ((size_t)t * G + g) * 1024 + 16 * (ci & 63), st + T::kABytes + 16 * (ci - lane));
-    }
-    {
-      const int t = min(tg0 + wn * NTW + ((lane >> 3) & (NTW - 1)), a.tiles - 1);
-      dma4(ssrc + ((size_t)t * G + g) * 32 + 4 * (lane & 7), st + T::kABytes + T::kWBytes + wave * 256);
-    }
+    for (int i = 0; i < T::kWInst; ++i)
+      dma16(rw, vow[i], g * 1024, st + T::kABytes + 16 * (wave * 64 + i * T::kThreads));
+    dma4(rs, vos, g * 32, st + T::kABytes + T::kWBytes + wave * 256);
   };
 
   f4_t acc[MR][NTW];
@@ -147,8 +169,16 @@ __global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_dma_kernel(GemvA
   for (int i = 0; i < MR; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = (f4_t){0.f, 0.f, 0.f, 0.f};
-  const uint32_t mlo = vgpr_const(kMaskLo);
+  const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
   const h2_t bias = (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+  const h2_t sixteenth = (h2_t){(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2_t bias16 = (h2_t){(_Float16)72.0f, (_Float16)72.0f};
+  // nibble pair at bits (0, 16) of v: 1024 + u - 1032 = q; at bits (4, 20):
+  // (1024 + 16 u) / 16 - 72 = q (both exact in fp16)
+  auto qlo = [&](uint32_t v) { return __builtin_bit_cast(uint32_t, as_h2((v & mlo) | 0x64006400u) - bias); };
+  auto qhi = [&](uint32_t v) {
+    return __builtin_bit_cast(uint32_t, as_h2((v & mhi) | 0x64006400u) * sixteenth - bias16);
+  };
   const int x15 = lane & 15, c4 = 4 * (lane >> 4);   // row within a block, first word of the lane's chunk
 
   auto compute = [&](const uint8_t* st) {
@@ -169,8 +199,7 @@ __global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_dma_kernel(GemvA
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
         const uint32_t p = wv[j][r];
-        auto q2 = [&](uint32_t v) { return __builtin_bit_cast(uint32_t, as_h2((v & mlo) | 0x64006400u) - bias); };
-        bw[j] = __builtin_bit_cast(h8_t, (u4_t){q2(p), q2(p >> 4), q2(p >> 8), q2(p >> 12)});
+        bw[j] = __builtin_bit_cast(h8_t, (u4_t){qlo(p), qhi(p), qlo(p >> 8), qhi(p >> 8)});
       }
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
@@ -189,19 +218,20 @@ __global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_dma_kernel(GemvA
         for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(sc[j], d[i][j][q], acc[i][j][q]);
   };
 
-  // Ring of three stages: group g in ring g % 3, two groups in flight. Every
-  // stage issues exactly kInst loads per thread (past the last group they
-  // reload group G - 1 into the slot no later stage reads), so one wait form
-  // holds everywhere: at stage g the loads of g + 1 are the only ones newer
-  // than those of g. Columns at or past k (a partial last group) are zeroed
-  // in LDS before the last group is multiplied, as the decode GEMV zeroes them.
+  // Ring of NS stages: group g in ring g % NS, NS - 1 groups in flight. With
+  // three stages every stage issues exactly kInst loads per thread (past the
+  // last group they reload group G - 1 into the slot no later stage reads),
+  // so one wait form holds everywhere: at stage g the loads of g + 1 are the
+  // only ones newer than those of g. With two, a stage waits for all its
+  // loads. Columns at or past k (a partial last group) are zeroed in LDS
+  // before the last group is multiplied, as the decode GEMV zeroes them.
   const bool ragged = (a.k & (kGroup - 1)) != 0;
   auto stage = [&](int g, uint8_t* cur, uint8_t* nxt) {
     // this thread's loads of stage g are done; after the barrier every
     // thread's are, and every wavefront has consumed its reads of stage
     // g - 1 (whose ring slot the next loads overwrite). A bare s_barrier:
     // __syncthreads() would also wait for the loads still in flight.
-    wait_vm<T::kInst>();
+    if constexpr (NS == 3) wait_vm<T::kInst>(); else wait_vm<0>();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -214,20 +244,29 @@ __global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_dma_kernel(GemvA
       }
       __syncthreads();
     }
-    issue(min(g + 2, G - 1), nxt);
+    if constexpr (NS == 3) issue(min(g + 2, G - 1), nxt);
+    else if (g + 1 < G) issue(g + 1, nxt);
     compute(cur);
   };
   issue(0, ring0);
-  issue(min(1, G - 1), ring1);
   int g = 0;
-  for (; g + 3 <= G; g += 3) {
-    stage(g, ring0, ring2);
-    stage(g + 1, ring1, ring0);
-    stage(g + 2, ring2, ring1);
-  }
-  if (g < G) {                                       // nested, so no path reads a slot still being filled
-    stage(g, ring0, ring2);
-    if (g + 1 < G) stage(g + 1, ring1, ring0);
+  if constexpr (NS == 3) {
+    issue(min(1, G - 1), ring1);
+    for (; g + 3 <= G; g += 3) {
+      stage(g, ring0, ring2);
+      stage(g + 1, ring1, ring0);
+      stage(g + 2, ring2, ring1);
+    }
+    if (g < G) {                                     // nested, so no path reads a slot still being filled
+      stage(g, ring0, ring2);
+      if (g + 1 < G) stage(g + 1, ring1, ring0);
+    }
+  } else {
+    for (; g + 2 <= G; g += 2) {
+      stage(g, ring0, ring1);
+      stage(g + 1, ring1, ring0);
+    }
+    if (g < G) stage(g, ring0, ring1);
   }
   wait_vm<0>();                                      // no load may land in LDS after the workgroup ends
 
@@ -246,21 +285,27 @@ __global__ __launch_bounds__(WM * WN * 64) void w4_gemm_prefill_dma_kernel(GemvA
       }
 }
 
-template <int EPI, int WM, int WN, int MR, int NTW>
+template <int EPI, int WM, int WN, int MR, int NTW, int NS, int WPE>
 static hipError_t launch_pf_tile(const GemvArgs& a, hipStream_t s) {
-  using T = PfRing<WM, WN, MR, NTW>;
-  hipLaunchKernelGGL((w4_gemm_prefill_dma_kernel<EPI, WM, WN, MR, NTW>),
+  using T = PfRing<WM, WN, MR, NTW, NS>;
+  hipLaunchKernelGGL((w4_gemm_prefill_dma_kernel<EPI, WM, WN, MR, NTW, NS, WPE>),
                      dim3(ceil_div(a.batch, T::kRows), ceil_div(a.tiles, T::kTiles)), dim3(T::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int EPI>
 static hipError_t launch_pf_epi(const GemvArgs& a, hipStream_t s) {
-  // 128 rows x 128 weight rows per workgroup (2 x 2 wavefronts of 64 x 64);
-  // narrower matrices take 64-row x 128-weight-row tiles (1 x 4 wavefronts
-  // of 64 x 32) so the grid still covers the chip
-  if ((long)ceil_div(a.batch, 128) * ceil_div(a.tiles, 8) >= 256) return launch_pf_tile<EPI, 2, 2, 4, 4>(a, s);
-  return launch_pf_tile<EPI, 1, 4, 4, 2>(a, s);
+  // a workgroup's activation rows and weight blocks are addressed by 32-bit
+  // buffer offsets
+  if (2 * (128 * (long)a.x_stride + a.k) > INT32_MAX || 8L * a.groups * 1024 > INT32_MAX) return hipErrorInvalidValue;
+  // One row of four wavefronts, each on its own two weight tiles (no
+  // dequantisation done twice), three workgroups per CU: measured at 512
+  // rows, the gate/up shape (over 1000 workgroups) runs fastest with 64-row
+  // tiles and a two-stage ring (153.7 us against 174.8 with 32-row tiles),
+  // the narrower shapes with 32-row tiles and three stages (qkv 31.1 us,
+  // o-proj 23.5, down 108.3, against 35.8 / 29.2 / 139.7).
+  if ((long)ceil_div(a.batch, 64) * ceil_div(a.tiles, 8) >= 1024) return launch_pf_tile<EPI, 1, 4, 4, 2, 2, 3>(a, s);
+  return launch_pf_tile<EPI, 1, 4, 2, 2, 3, 3>(a, s);
 }
 
 hipError_t launch_w4_gemm_prefill(int epi, const GemvArgs& a, hipStream_t s) {
