@@ -34,8 +34,10 @@ namespace w4 {
 // (buffer_load_dwordx4 ... lds: lane L's 16 bytes land at the LDS base + 16 L)
 // into a ring of two or three stages, each holding one 128-column group: the
 // activation rows in natural order (row r's 16-byte word w at physical slot
-// w ^ (r & 15), so the 16 rows one ds_read_b128 touches are in distinct
-// banks), the workgroup's packed weight blocks, and each wavefront's scales.
+// w ^ swz(r & 15), swz swapping the two 2-bit halves of its argument: measured
+// on gfx950, the 64 reads of one MFMA operand then take 4 LDS cycles per
+// ds_read_b128, against 8 with w ^ (r & 15) or a rotation), the workgroup's
+// packed weight blocks, and each wavefront's scales.
 // One or two groups are in flight while one is multiplied, with no registers
 // spent on staging. MFMA r takes word r of the lane's 16 weight bytes,
 // dequantised in natural column order (the nibbles of columns 2i and 2i + 1
@@ -87,6 +89,9 @@ struct PfRing {
 
 typedef __attribute__((address_space(3))) void* lptr_t;
 
+// LDS slot key of an activation row (mod 16): its 2-bit halves swapped
+__device__ __forceinline__ int swz(int x) { return ((x & 3) << 2) | (x >> 2); }
+
 // A raw buffer of `bytes` bytes at base: loads at or past the end read zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
@@ -136,7 +141,7 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
   const __amdgpu_buffer_rsrc_t rs = range_rsrc(a.w + (size_t)a.tiles * G * 1024 + (size_t)tg0 * G * 32, ntl * G * 32);
 
   // per-thread load offsets, fixed across groups: A (row r, physical word p
-  // <- logical word p ^ (r & 15); rows past the last repeat it), W (the
+  // <- logical word p ^ swz(r & 15); rows past the last repeat it), W (the
   // workgroup's blocks in tile order), S (word l % 8 of tile (l / 8) % NTW of
   // the wavefront's tiles: every lane loads, so every wavefront issues the same
   // count of loads on every path; lanes past 8 NTW repeat words nobody reads)
@@ -145,7 +150,7 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
   for (int i = 0; i < T::kAInst; ++i) {
     const int ci = tid + i * T::kThreads;              // 16-byte chunk of the A region
     const int r = ci >> 4, p = ci & 15;
-    voa[i] = 2 * (min(r, rows - 1) * a.x_stride + 8 * (p ^ (r & 15)));
+    voa[i] = 2 * (min(r, rows - 1) * a.x_stride + 8 * (p ^ swz(r & 15)));
   }
 #pragma unroll
   for (int i = 0; i < T::kWInst; ++i) {
@@ -180,6 +185,7 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
     return __builtin_bit_cast(uint32_t, as_h2((v & mhi) | 0x64006400u) * sixteenth - bias16);
   };
   const int x15 = lane & 15, c4 = 4 * (lane >> 4);   // row within a block, first word of the lane's chunk
+  const int key = swz(x15);
 
   auto compute = [&](const uint8_t* st) {
     const uint8_t* A = st + (size_t)(16 * MR * wm + x15) * (kGroup * 2);
@@ -203,7 +209,7 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < MR; ++i) {
-        const h8_t av = *reinterpret_cast<const h8_t*>(A + (size_t)16 * i * (kGroup * 2) + 16 * ((c4 + r) ^ x15));
+        const h8_t av = *reinterpret_cast<const h8_t*>(A + (size_t)16 * i * (kGroup * 2) + 16 * ((c4 + r) ^ key));
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
           d[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[j], r == 0 ? (f4_t){0.f, 0.f, 0.f, 0.f} : d[i][j],
@@ -240,7 +246,7 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
       for (int i = 0; i < T::kAInst; ++i) {
         const int ci = tid + i * T::kThreads;
         const int r = ci >> 4, p = ci & 15;
-        if (g * kGroup + 8 * (p ^ (r & 15)) >= a.k) *reinterpret_cast<u4_t*>(cur + 16 * ci) = (u4_t){0u, 0u, 0u, 0u};
+        if (g * kGroup + 8 * (p ^ swz(r & 15)) >= a.k) *reinterpret_cast<u4_t*>(cur + 16 * ci) = (u4_t){0u, 0u, 0u, 0u};
       }
       __syncthreads();
     }
