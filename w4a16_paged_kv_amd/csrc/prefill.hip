@@ -89,6 +89,7 @@ struct PfRing {
 
 typedef __attribute__((address_space(3))) void* lptr_t;
 
+
 // LDS slot key of an activation row (mod 16): its 2-bit halves swapped
 __device__ __forceinline__ int swz(int x) { return ((x & 3) << 2) | (x >> 2); }
 
@@ -325,40 +326,53 @@ hipError_t launch_w4_gemm_prefill(int epi, const GemvArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------- causal attention
-// Work item = (16 prompt rows, query head): one wavefront. Prompt row m sits
-// at position start + m and attends positions [0, start + m] of its
-// sequence, read through the page table (token t of the sequence in page
-// page_table[t / 16], slot t % 16: "Building a Custom LLM Inference Runtime
-// on H100", The Three Critical Bugs, Bug 1). The products run on the
-// matrix cores as in the decode kernel, with the 16 query columns being
-// the item's 16 rows instead of a KV group's heads: S^T = K Q^T
-// (v_mfma_f32_16x16x32_f16, lane l ends with S[token 4 (l >> 4) + j][row
-// l & 15]), base-2 online softmax per row in fp32, O^T = V^T P^T
-// (v_mfma_f32_16x16x16_f16, P entering as two fp16 terms). A token past
-// a row's position scores -inf; V values of tokens past the item's last
-// position are zeroed, so slots not written yet (or poisoned) add nothing.
-// A workgroup holds the GQ heads of one KV head for the same 16 rows, so
-// their K/V loads meet in the cache.
+// Work item = (16 prompt rows, query head): one workgroup of kPfaWaves
+// wavefronts. Prompt row m sits at position start + m and attends positions
+// [0, start + m] of its sequence, read through the page table (token t of the
+// sequence in page page_table[t / 16], slot t % 16: "Building a Custom LLM
+// Inference Runtime on H100", The Three Critical Bugs, Bug 1). The products
+// run on the matrix cores as in the decode kernel, with the 16 query columns
+// being the item's 16 rows: S^T = K Q^T (v_mfma_f32_16x16x32_f16, lane l
+// ends with S[token 4 (l >> 4) + j][row l & 15]), base-2 online softmax per
+// row in fp32, O^T = V^T P^T (v_mfma_f32_16x16x16_f16, P entering as two
+// fp16 terms). A token past a row's position scores -inf.
+//
+// The pages go in steps of two (32 tokens, one softmax update per step);
+// wavefront w takes steps w, w + W, w + 2W, ... so the long items of the
+// causal triangle spread over W wavefronts, whose (m, l, O) states merge by
+// log-sum-exp through LDS at the end (as the decode attention merges its
+// splits). Each wavefront keeps a ring of four page buffers in registers:
+// one step is multiplied while its next is in flight.
+constexpr int kPfaWaves = 4;
+
+// 16-byte load with the default cache policy (data written by an earlier kernel)
+__device__ __forceinline__ u4_t ld128_plain(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 template <int D, int GQ>
-__global__ __launch_bounds__(GQ * 64) void prefill_attn_kernel(PrefillAttnArgs a) {
-  constexpr int NK = D / 32, NS = D / 16;
+__global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(PrefillAttnArgs a) {
+  constexpr int NK = D / 32, NS = D / 16, W = kPfaWaves;
+  __shared__ float sm_m[W][16], sm_l[W][16];
+  __shared__ f4_t sm_o[W][NS][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int blk = blockIdx.x, kvh = blockIdx.y;
-  const int h = kvh * GQ + wave;
+  const int blk = blockIdx.x, h = blockIdx.y, kvh = h / GQ;
   const int r0 = 16 * blk;                       // first prompt row of the item
   const int last_row = min(r0 + 15, a.n - 1);
   const int p_last = a.start + last_row;         // the item's last position
-  const int npages = p_last / kPage + 1;
+  const int pe = p_last / kPage + 1;             // pages of the item
   const int qi = lane & 15, kc = 8 * (lane >> 4), tk = 4 * (lane >> 4);
   const int my_pos = a.start + r0 + qi;          // this lane's query row position (for the mask)
 
-  // the 16 rows' queries as the B operand (row qi, dims 32 kk + kc .. + 8)
+  // q and the pages were written by earlier kernels: plain loads, which the
+  // XCD's L2 serves to the item's wavefronts and to the later row blocks.
+  // The 16 rows' queries are the B operand (row qi, dims 32 kk + kc .. + 8).
   const __amdgpu_buffer_rsrc_t rq = coherent_rsrc(a.q);
   const int qrow = min(r0 + qi, a.n - 1);
   u4_t qb[NK];
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) qb[kk] = ld128_agent(rq, 2 * (qrow * a.q_stride + h * D + 32 * kk + kc));
+  for (int kk = 0; kk < NK; ++kk) qb[kk] = ld128_plain(rq, 2 * (qrow * a.q_stride + h * D + 32 * kk + kc));
 
   const float scale = kLog2e / sqrtf((float)D);
   float m_h = -INFINITY, l_h = 0.f;              // softmax state of row qi
@@ -366,81 +380,158 @@ __global__ __launch_bounds__(GQ * 64) void prefill_attn_kernel(PrefillAttnArgs a
 #pragma unroll
   for (int i = 0; i < NS; ++i) acc[i] = (f4_t){0.f, 0.f, 0.f, 0.f};
   const size_t slice = (size_t)kPage * D;
-  u4_t kf[NK], vf[NS / 2], kn[NK], vn[NS / 2];
+  u4_t kb[4][NK], vb[4][NS / 2];
+  bool bad = false;                              // a page id outside the pool (reported once)
+  // the page table is read-only here: read through the constant address space
+  // it becomes a scalar load, which does not wait behind the K/V loads in flight
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)a.page_table;
+  // every step issues its loads (past the item's last page they reread it),
+  // so no branch sits between a load and its use
   auto load_kv = [&](int p, u4_t* kk, u4_t* vv) {
-    int id = a.page_table[min(p, a.max_pages - 1)];
-    if (id < 0 || id >= a.num_pages) {
-      if (lane == 0) atomicAdd(a.err, 1u);
-      id = 0;
-    }
-    id = __builtin_amdgcn_readfirstlane(id);
+    int id = ptab[min(min(p, pe - 1), a.max_pages - 1)];
+    const bool out = id < 0 || id >= a.num_pages;
+    bad |= out;
+    id = __builtin_amdgcn_readfirstlane(out ? 0 : id);
     const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(a.k_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
     const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(a.v_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kk[i] = ld128_agent(rk, 2 * (qi * D + 32 * i + kc));
+    for (int i = 0; i < NK; ++i) kk[i] = ld128_plain(rk, 2 * (qi * D + 32 * i + kc));
 #pragma unroll
-    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128_agent(rv, 16 * (64 * i + lane));
+    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128_plain(rv, 16 * (64 * i + lane));
   };
-  load_kv(0, kf, vf);
-  for (int p = 0; p < npages; ++p) {
-    if (p + 1 < npages) load_kv(p + 1, kn, vn);
-    f4_t sc = {0.f, 0.f, 0.f, 0.f};
+  // Only the prompt's last page can hold slots no prompt row wrote (every
+  // other slot of these pages holds a written token, whose weight is exactly
+  // 0 for rows before it): its V values past the last prompt position are
+  // zeroed, so such slots add nothing even if they hold NaN.
+  const int tail_page = (a.start + a.n - 1) / kPage, tail_valid = (a.start + a.n - 1) % kPage + 1;
+  auto zero_tail = [&](u4_t* vf) {
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, kf[kk]), __builtin_bit_cast(h8_t, qb[kk]),
-                                                  sc, 0, 0, 0);
-    float sv[4];
+    for (int i = 0; i < NS / 2; ++i) {
+      h8_t v8 = __builtin_bit_cast(h8_t, vf[i]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sv[j] = kPage * p + tk + j <= my_pos ? sc[j] * scale : -INFINITY;
-    const float pm = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-    const float n_h = fmaxf(m_h, pm);
-    const float al = n_h == -INFINITY ? 1.f : exp2f(m_h - n_h);
-    float pj[4];
-    h4_t ph, pl;
+      for (int j = 0; j < 8; ++j)
+        if (tk + (j & 3) >= tail_valid) v8[j] = (_Float16)0.f;
+      vf[i] = __builtin_bit_cast(u4_t, v8);
+    }
+  };
+  auto step = [&](int p, const u4_t* k0, u4_t* v0, const u4_t* k1, u4_t* v1) {
+    // uniform: which of the step's pages belong to the item (a page past it
+    // scores -inf, so its weights are exactly 0 and the rescale exactly 1)
+    const bool one = p < pe, two = p + 1 < pe;
+    f4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, k0[kk]), __builtin_bit_cast(h8_t, qb[kk]),
+                                                  s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, k1[kk]), __builtin_bit_cast(h8_t, qb[kk]),
+                                                  s1, 0, 0, 0);
+    }
+    float sv[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      pj[j] = n_h == -INFINITY ? 0.f : exp2f(sv[j] - n_h);
-      ph[j] = (_Float16)pj[j];
-      pl[j] = (_Float16)(pj[j] - (float)ph[j]);
+      sv[j] = one && kPage * p + tk + j <= my_pos ? s0[j] * scale : -INFINITY;
+      sv[4 + j] = two && kPage * (p + 1) + tk + j <= my_pos ? s1[j] * scale : -INFINITY;
     }
-    l_h = l_h * al + rows_sum((pj[0] + pj[1]) + (pj[2] + pj[3]));
+    float lm = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) lm = fmaxf(lm, sv[j]);
+    const float n_h = fmaxf(m_h, rows_max(lm));
+    const bool none = n_h == -INFINITY;          // no token of this row seen yet
+    // raw v_exp_f32: weights below 2^-126 of the row maximum reach no fp16 output
+    const float al = none ? 1.f : __builtin_amdgcn_exp2f(m_h - n_h);
+    float pj[8];
+    h4_t ph0, pl0, ph1, pl1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pj[j] = none ? 0.f : __builtin_amdgcn_exp2f(sv[j] - n_h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ph0[j] = (_Float16)pj[j];
+      pl0[j] = (_Float16)(pj[j] - (float)ph0[j]);
+      ph1[j] = (_Float16)pj[4 + j];
+      pl1[j] = (_Float16)(pj[4 + j] - (float)ph1[j]);
+    }
+    l_h = l_h * al + rows_sum(((pj[0] + pj[1]) + (pj[2] + pj[3])) + ((pj[4] + pj[5]) + (pj[6] + pj[7])));
     m_h = n_h;
-    const int valid = p_last - kPage * p + 1;    // tokens of this page at or before the item's last position
-    if (valid < kPage) {
+    if (p == tail_page) zero_tail(v0);
+    if (p + 1 == tail_page) zero_tail(v1);
+    if (one) {
 #pragma unroll
-      for (int i = 0; i < NS / 2; ++i) {
-        h8_t v8 = __builtin_bit_cast(h8_t, vf[i]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (tk + (j & 3) >= valid) v8[j] = (_Float16)0.f;
-        vf[i] = __builtin_bit_cast(u4_t, v8);
+      for (int i = 0; i < NS; ++i) {
+        const u4_t vp = v0[i >> 1];
+        const h4_t v4 = __builtin_bit_cast(h4_t, (i & 1) ? (u2_t){vp[2], vp[3]} : (u2_t){vp[0], vp[1]});
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, ph0, acc[i] * al, 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, pl0, acc[i], 0, 0, 0);
       }
     }
+    if (two) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const u4_t vp = vf[i >> 1];
-      const h4_t v4 = __builtin_bit_cast(h4_t, (i & 1) ? (u2_t){vp[2], vp[3]} : (u2_t){vp[0], vp[1]});
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, ph, acc[i] * al, 0, 0, 0);
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, pl, acc[i], 0, 0, 0);
+      for (int i = 0; i < NS; ++i) {
+        const u4_t vp = v1[i >> 1];
+        const h4_t v4 = __builtin_bit_cast(h4_t, (i & 1) ? (u2_t){vp[2], vp[3]} : (u2_t){vp[0], vp[1]});
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, ph1, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(v4, pl1, acc[i], 0, 0, 0);
+      }
     }
-    if (p + 1 < npages) {
+  };
+  // this wavefront's steps start at pages 2 wave, 2 (wave + W), ...
+  const int pw = 2 * wave, ps = 2 * W;
 #pragma unroll
-      for (int i = 0; i < NK; ++i) kf[i] = kn[i];
-#pragma unroll
-      for (int i = 0; i < NS / 2; ++i) vf[i] = vn[i];
-    }
+  for (int j = 0; j < 2; ++j) {
+    load_kv(pw + ps * j, kb[2 * j], vb[2 * j]);
+    load_kv(pw + ps * j + 1, kb[2 * j + 1], vb[2 * j + 1]);
+    __builtin_amdgcn_sched_barrier(0);           // issued in step order
   }
-  // lane l: O[row l & 15][dim 16 i + 4 (l >> 4) + j]
+  // at each step exactly the next step's 2 (NK + NS / 2) loads are newer than its own
+  constexpr int kNewer = 2 * (NK + NS / 2);
+  for (int p0 = pw; p0 < pe; p0 += 2 * ps) {
+    wait_vm<kNewer>();
+    __builtin_amdgcn_sched_barrier(0);
+    step(p0, kb[0], vb[0], kb[1], vb[1]);
+    load_kv(p0 + 2 * ps, kb[0], vb[0]);
+    load_kv(p0 + 2 * ps + 1, kb[1], vb[1]);
+    wait_vm<kNewer>();
+    __builtin_amdgcn_sched_barrier(0);
+    step(p0 + ps, kb[2], vb[2], kb[3], vb[3]);
+    load_kv(p0 + 3 * ps, kb[2], vb[2]);
+    load_kv(p0 + 3 * ps + 1, kb[3], vb[3]);
+  }
+  wait_vm<0>();                                  // the rereads past the item land before the merge
+  if (bad && lane == 0) atomicAdd(a.err, 1u);
+
+  // merge the W states: o = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w
+  // (a wavefront that saw no token of a row has m_w = -inf and weight 0)
+  if (lane < 16) {
+    sm_m[wave][qi] = m_h;
+    sm_l[wave][qi] = l_h;
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) sm_o[wave][i][lane] = acc[i];
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < W; ++w) M = fmaxf(M, sm_m[w][qi]);
+  float wt[W], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const float mw = sm_m[w][qi];
+    wt[w] = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    L += wt[w] * sm_l[w][qi];
+  }
+  // lane l: O[row l & 15][dim 16 i + 4 (l >> 4) + j]; wavefront w writes dim blocks i = w, w + W, ...
   const int row = r0 + qi;
   if (row < a.n) {
-    const float inv = l_h > 0.f ? 1.0f / l_h : 0.f;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
     uint16_t* out = a.out + (size_t)row * a.out_stride + h * D;
     const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(out);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
+    for (int i = wave; i < NS; i += W) {
+      f4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < W; ++w) o += wt[w] * sm_o[w][i][lane];
       h4_t r;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = (_Float16)(acc[i][j] * inv);
+      for (int j = 0; j < 4; ++j) r[j] = (_Float16)(o[j] * inv);
       __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, r), ro, 2 * (16 * i + tk), 0, kPolicySc1);
     }
   }
@@ -448,13 +539,13 @@ __global__ __launch_bounds__(GQ * 64) void prefill_attn_kernel(PrefillAttnArgs a
 
 template <int D>
 static hipError_t launch_pfa_d(const PrefillAttnArgs& a, int group, hipStream_t s) {
-  const dim3 grid(ceil_div(a.n, 16), a.n_kv_heads);
+  const dim3 grid(ceil_div(a.n, 16), a.n_heads), block(kPfaWaves * 64);
   switch (group) {
-    case 1: hipLaunchKernelGGL((prefill_attn_kernel<D, 1>), grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), grid, dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((prefill_attn_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((prefill_attn_kernel<D, 7>), grid, dim3(448), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((prefill_attn_kernel<D, 8>), grid, dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((prefill_attn_kernel<D, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((prefill_attn_kernel<D, 4>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((prefill_attn_kernel<D, 7>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((prefill_attn_kernel<D, 8>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
