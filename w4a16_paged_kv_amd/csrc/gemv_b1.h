@@ -88,6 +88,12 @@ __device__ __forceinline__ void st16_agent(uint16_t* p, uint16_t v) {
 __device__ __forceinline__ uint16_t ld16_agent(const uint16_t* p) {
   return __hip_atomic_load(const_cast<uint16_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// PLAIN: the value is read only by later kernels (no device-scope store needed)
+template <bool PLAIN>
+__device__ __forceinline__ void st16(uint16_t* p, uint16_t v) {
+  if constexpr (PLAIN) *p = v;
+  else st16_agent(p, v);
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
@@ -114,13 +120,14 @@ __host__ __device__ __forceinline__ int v_slice_offset(int t, int d) {
 // One token's K or V values (dims dim0, dim1 of KV head kvh) into its page
 // slot. A (page, head) slice of K is [16 tokens][D]; of V it is in the P V
 // operand order above.
+template <bool PLAIN = false>
 __device__ __forceinline__ void kv_store(const QkvEpilogue& e, uint16_t* pool, bool v_layout, int slot, int kvh,
                                          int dim0, int dim1, float v0, float v1) {
   if (slot < 0) return;  // invalid position or page: counted by the token plan
   uint16_t* sl = pool + ((size_t)(slot >> 4) * e.n_kv_heads + kvh) * kPage * e.head_dim;
   const int t = slot & 15;
-  st16_agent(sl + (v_layout ? v_slice_offset(t, dim0) : t * e.head_dim + dim0), f2h(v0));
-  st16_agent(sl + (v_layout ? v_slice_offset(t, dim1) : t * e.head_dim + dim1), f2h(v1));
+  st16<PLAIN>(sl + (v_layout ? v_slice_offset(t, dim0) : t * e.head_dim + dim0), f2h(v0));
+  st16<PLAIN>(sl + (v_layout ? v_slice_offset(t, dim1) : t * e.head_dim + dim1), f2h(v1));
 }
 
 // Rows i and i+8 of tile t hold the rotate-half RoPE pair (dim0, dim0 + D/2)
@@ -133,6 +140,7 @@ __device__ __forceinline__ int qkv_dim0(const QkvEpilogue& e, int t, int i) {
 // q/k heads are rotated by (c, sn), the token plan's rotation of the pair
 // (angle pos * base^(-2 dim0 / D)), and rounded once to fp16; v heads are
 // rounded unrotated. k/v go to the token's page slot.
+template <bool PLAIN = false>
 __device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float y1, float c, float sn,
                         int slot) {
   const QkvEpilogue& e = a.qkv;
@@ -148,13 +156,13 @@ __device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float 
     const float r1 = y1 * c + y0 * sn;
     if (head < e.n_heads) {
       uint16_t* q = e.q_out + (size_t)m * e.q_stride + head * D;
-      st16_agent(q + dim0, f2h(r0));
-      st16_agent(q + dim1, f2h(r1));
+      st16<PLAIN>(q + dim0, f2h(r0));
+      st16<PLAIN>(q + dim1, f2h(r1));
     } else {
-      kv_store(e, e.k_pool, false, slot, head - e.n_heads, dim0, dim1, r0, r1);
+      kv_store<PLAIN>(e, e.k_pool, false, slot, head - e.n_heads, dim0, dim1, r0, r1);
     }
   } else {
-    kv_store(e, e.v_pool, true, slot, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
+    kv_store<PLAIN>(e, e.v_pool, true, slot, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
   }
 }
 

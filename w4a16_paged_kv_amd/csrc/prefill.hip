@@ -47,7 +47,8 @@ namespace w4 {
 
 // The prefill epilogue of one accumulator value: lane l holds weight row
 // l & 15 of tile t for activation row m; its partner (weight row (l & 15) ^ 8)
-// comes from ror8, taken by every lane before any branch.
+// comes from ror8, taken by every lane before any branch. Every output here
+// (and the residual) passes between kernels, so plain loads and stores do.
 template <int EPI>
 __device__ __forceinline__ void pf_epilogue(const GemvArgs& a, int m, int t, int i, float v, float partner) {
   if (m >= a.batch || t >= a.tiles) return;
@@ -55,16 +56,16 @@ __device__ __forceinline__ void pf_epilogue(const GemvArgs& a, int m, int t, int
     if (i < 8) {
       const int pair = qkv_dim0(a.qkv, t, i);
       const float* cs = a.qkv.rope + ((size_t)m * (a.qkv.head_dim / 2) + pair) * 2;
-      epi_qkv(a, m, t, i, v, partner, cs[0], cs[1], a.qkv.slot[m]);
+      epi_qkv<true>(a, m, t, i, v, partner, cs[0], cs[1], a.qkv.slot[m]);
     }
   } else if (EPI == EPI_SILU) {
     const int o = 8 * t + i;
-    if (i < 8 && o < a.n / 2) st16_agent(a.y + (size_t)m * a.y_stride + o, f2h(v / (1.0f + expf(-v)) * partner));
+    if (i < 8 && o < a.n / 2) a.y[(size_t)m * a.y_stride + o] = f2h(v / (1.0f + expf(-v)) * partner);
   } else {
     const int row = kTileRows * t + i;
     if (row < a.n) {
-      if (EPI == EPI_RESID) v += h2f(ld16_agent(a.resid + (size_t)m * a.y_stride + row));
-      st16_agent(a.y + (size_t)m * a.y_stride + row, f2h(v));
+      if (EPI == EPI_RESID) v += h2f(a.resid[(size_t)m * a.y_stride + row]);
+      a.y[(size_t)m * a.y_stride + row] = f2h(v);
     }
   }
 }
