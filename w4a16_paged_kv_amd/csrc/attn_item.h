@@ -62,12 +62,12 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   int pid_cur = pt[min(pw0, a.max_pages - 1)];
   int pid_nxt = pt[min(pw0 + W, a.max_pages - 1)];
   int ctx = a.ctx_lens[b];
-  const __amdgpu_buffer_rsrc_t rq = coherent_rsrc(a.q + (size_t)b * a.q_stride + (size_t)kvh * GQ * D);
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(a.q + (size_t)b * a.q_stride + (size_t)kvh * GQ * D);
   u4_t qv[(GQ * D + NT * 8 - 1) / (NT * 8)];
 #pragma unroll
   for (int r = 0; r < (GQ * D + NT * 8 - 1) / (NT * 8); ++r) {
     const int i = min((int)(threadIdx.x + r * NT) * 8, GQ * D - 8);
-    qv[r] = ld128_agent(rq, 2 * i);
+    qv[r] = ld128(rq, 2 * i);
   }
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * kPage ? a.max_pages * kPage : ctx);
   const int npages = (ctx + kPage - 1) / kPage;
@@ -125,12 +125,12 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   u4_t vf[NS / 2], vn[PF ? NS / 2 : 1];  // V operands of slice pairs (2i, 2i + 1)
   auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
     page = __builtin_amdgcn_readfirstlane(page);  // one page per wavefront: keeps the resources scalar
-    const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
-    const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kk[i] = ld128_agent(rk, 2 * (qh * D + 32 * i + kc));
+    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 2 * (qh * D + 32 * i + kc));
 #pragma unroll
-    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128_agent(rv, 16 * (64 * i + lane));
+    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128(rv, 16 * (64 * i + lane));
   };
   int valid_cur = 0, valid_nxt = 0;
   const int p_stop = pager ? p_end : pw0;  // non-page wavefronts skip the loop
@@ -216,8 +216,8 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   constexpr int PS = D + 4;      // floats per (split, head) partial: o[D], m, l, 2 unused (16-byte rows)
   constexpr int NG = GQ * D / 4;  // four-dim groups of the item's output
   float* part = a.partials + (((size_t)b * a.n_kv_heads + kvh) * a.max_splits + split) * GQ * PS;
-  const __amdgpu_buffer_rsrc_t rpart = coherent_rsrc(part);
-  const __amdgpu_buffer_rsrc_t rout = coherent_rsrc(out);
+  const __amdgpu_buffer_rsrc_t rpart = buf_rsrc(part);
+  const __amdgpu_buffer_rsrc_t rout = buf_rsrc(out);
   for (int g = threadIdx.x; g < NG; g += NT) {
     const int h = g / (D / 4), d0 = 4 * (g % (D / 4));
     float M = -INFINITY;
@@ -271,7 +271,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   constexpr int kU = 8;
   static_assert(GQ * 128 + (TPG - 1) * NG * 4 <= W * GQ * D, "merge scratch fits s_o");
   const float* pb = a.partials + ((size_t)b * a.n_kv_heads + kvh) * a.max_splits * GQ * PS;
-  const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(pb);
+  const __amdgpu_buffer_rsrc_t rp = buf_rsrc(pb);
   float* s_w = &s_o[0][0][0];                                  // reuse: [GQ][nsplit] (nsplit <= 128)
   f4_t* s_x = reinterpret_cast<f4_t*>(&s_o[0][0][0] + GQ * 128);  // [TPG - 1][NG]
   float mm[2] = {-INFINITY, -INFINITY}, ll[2] = {0.f, 0.f};

@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
     // Partial sums move between workgroups (and XCDs) through device-coherent
     // 16-byte stores and loads; each workgroup's stores complete before it
     // counts itself.
-    const __amdgpu_buffer_rsrc_t rp = coherent_rsrc(a.kpart + (size_t)tg * CH * TW * 256);
+    const __amdgpu_buffer_rsrc_t rp = buf_rsrc(a.kpart + (size_t)tg * CH * TW * 256);
     for (int q = threadIdx.x; q < TW * 64; q += NT)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, *reinterpret_cast<const f4_t*>(vals + 4 * q)),
                                              rp, 16 * (kc * TW * 64 + q), 0, kPolicySc1);

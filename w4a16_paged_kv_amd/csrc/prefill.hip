@@ -56,7 +56,7 @@ __device__ __forceinline__ void pf_epilogue(const GemvArgs& a, int m, int t, int
     if (i < 8) {
       const int pair = qkv_dim0(a.qkv, t, i);
       const float* cs = a.qkv.rope + ((size_t)m * (a.qkv.head_dim / 2) + pair) * 2;
-      epi_qkv<true>(a, m, t, i, v, partner, cs[0], cs[1], a.qkv.slot[m]);
+      epi_qkv(a, m, t, i, v, partner, cs[0], cs[1], a.qkv.slot[m]);
     }
   } else if (EPI == EPI_SILU) {
     const int o = 8 * t + i;
@@ -346,11 +346,6 @@ hipError_t launch_w4_gemm_prefill(int epi, const GemvArgs& a, hipStream_t s) {
 // one step is multiplied while its next is in flight.
 constexpr int kPfaWaves = 4;
 
-// 16-byte load with the default cache policy (data written by an earlier kernel)
-__device__ __forceinline__ u4_t ld128_plain(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
 template <int D, int GQ>
 __global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int NK = D / 32, NS = D / 16, W = kPfaWaves;
@@ -369,11 +364,11 @@ __global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(
   // q and the pages were written by earlier kernels: plain loads, which the
   // XCD's L2 serves to the item's wavefronts and to the later row blocks.
   // The 16 rows' queries are the B operand (row qi, dims 32 kk + kc .. + 8).
-  const __amdgpu_buffer_rsrc_t rq = coherent_rsrc(a.q);
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc(a.q);
   const int qrow = min(r0 + qi, a.n - 1);
   u4_t qb[NK];
 #pragma unroll
-  for (int kk = 0; kk < NK; ++kk) qb[kk] = ld128_plain(rq, 2 * (qrow * a.q_stride + h * D + 32 * kk + kc));
+  for (int kk = 0; kk < NK; ++kk) qb[kk] = ld128(rq, 2 * (qrow * a.q_stride + h * D + 32 * kk + kc));
 
   const float scale = kLog2e / sqrtf((float)D);
   float m_h = -INFINITY, l_h = 0.f;              // softmax state of row qi
@@ -394,12 +389,12 @@ __global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(
     const bool out = id < 0 || id >= a.num_pages;
     bad |= out;
     id = __builtin_amdgcn_readfirstlane(out ? 0 : id);
-    const __amdgpu_buffer_rsrc_t rk = coherent_rsrc(a.k_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
-    const __amdgpu_buffer_rsrc_t rv = coherent_rsrc(a.v_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(a.v_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kk[i] = ld128_plain(rk, 2 * (qi * D + 32 * i + kc));
+    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 2 * (qi * D + 32 * i + kc));
 #pragma unroll
-    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128_plain(rv, 16 * (64 * i + lane));
+    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128(rv, 16 * (64 * i + lane));
   };
   // Only the prompt's last page can hold slots no prompt row wrote (every
   // other slot of these pages holds a written token, whose weight is exactly
@@ -524,7 +519,7 @@ __global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(
   if (row < a.n) {
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     uint16_t* out = a.out + (size_t)row * a.out_stride + h * D;
-    const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(out);
+    const __amdgpu_buffer_rsrc_t ro = buf_rsrc(out);
 #pragma unroll
     for (int i = wave; i < NS; i += W) {
       f4_t o = {0.f, 0.f, 0.f, 0.f};
@@ -533,7 +528,7 @@ __global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(
       h4_t r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) r[j] = (_Float16)(o[j] * inv);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, r), ro, 2 * (16 * i + tk), 0, kPolicySc1);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, r), ro, 2 * (16 * i + tk), 0, 0);
     }
   }
 }
