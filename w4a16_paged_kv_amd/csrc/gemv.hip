@@ -467,6 +467,11 @@ __global__ __launch_bounds__(WAVES * 64) void f16_gemm_mfma_kernel(F16GemvArgs a
 
 // y[b] = fp16(x[b] * rsqrt(mean(x[b]^2) + eps) * gamma), zero padded to the
 // next multiple of 128 columns (batched path: the MFMA kernels read it).
+// Rows up to kRmsWords 16-byte words per thread are read once into registers
+// (16-byte loads and stores); others take the element loop. Either way
+// y = (x * rs) * gamma in fp32, rounded once, zeros up to the 128-column pad.
+constexpr int kRmsWords = 4;  // 256 threads x 4 words x 8 = 8192 columns
+template <bool VEC>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* x, int x_stride,
                                                            const uint16_t* gamma, float eps, int k,
                                                            uint16_t* y, int y_stride) {
@@ -474,19 +479,49 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* x, in
   const int b = blockIdx.x;
   const uint16_t* xr = x + (size_t)b * x_stride;
   uint16_t* yr = y + (size_t)b * y_stride;
+  const int kpad = (k + kGroup - 1) / kGroup * kGroup;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < k; i += 256) {
-    const float v = h2f(xr[i]);
-    ss = fmaf(v, v, ss);
+  u4_t xv[VEC ? kRmsWords : 1];
+  if (VEC) {
+#pragma unroll
+    for (int w = 0; w < kRmsWords; ++w) {
+      const int c = 8 * (threadIdx.x + 256 * w);
+      xv[w] = c < k ? *reinterpret_cast<const u4_t*>(xr + c) : (u4_t){0u, 0u, 0u, 0u};
+      const h8_t h = __builtin_bit_cast(h8_t, xv[w]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)h[e], (float)h[e], ss);
+    }
+  } else {
+    for (int i = threadIdx.x; i < k; i += 256) {
+      const float v = h2f(xr[i]);
+      ss = fmaf(v, v, ss);
+    }
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float rs = 1.0f / sqrtf(tot / (float)k + eps);
-  const int kpad = (k + kGroup - 1) / kGroup * kGroup;
-  for (int i = threadIdx.x; i < kpad; i += 256)
-    yr[i] = i < k ? f2h(h2f(xr[i]) * rs * h2f(gamma[i])) : (uint16_t)0;
+  if (VEC) {
+#pragma unroll
+    for (int w = 0; w < kRmsWords; ++w) {
+      const int c = 8 * (threadIdx.x + 256 * w);
+      if (c >= kpad) break;
+      u4_t o = {0u, 0u, 0u, 0u};
+      if (c < k) {
+        const h8_t h = __builtin_bit_cast(h8_t, xv[w]);
+        const h8_t g = __builtin_bit_cast(h8_t, *reinterpret_cast<const u4_t*>(gamma + c));
+        h8_t r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = (_Float16)((float)h[e] * rs * (float)g[e]);
+        o = __builtin_bit_cast(u4_t, r);
+      }
+      *reinterpret_cast<u4_t*>(yr + c) = o;
+    }
+  } else {
+    for (int i = threadIdx.x; i < kpad; i += 256)
+      yr[i] = i < k ? f2h(h2f(xr[i]) * rs * h2f(gamma[i])) : (uint16_t)0;
+  }
 }
 
 __global__ __launch_bounds__(256) void embed_plan_kernel(TokenPlanArgs a) {
@@ -687,8 +722,14 @@ hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s) {
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16_t* gamma, float eps,
                                int32_t k, uint16_t* y, int32_t y_stride, int32_t batch,
                                hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(batch), dim3(256), 0, s, x, x_stride, gamma, eps, k,
-                     y, y_stride);
+  const bool vec = k % 8 == 0 && x_stride % 8 == 0 && y_stride % 8 == 0 && k <= 256 * 8 * kRmsWords &&
+                   ((uintptr_t)x | (uintptr_t)y | (uintptr_t)gamma) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<true>, dim3(batch), dim3(256), 0, s, x, x_stride, gamma, eps, k, y,
+                       y_stride);
+  else
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<false>, dim3(batch), dim3(256), 0, s, x, x_stride, gamma, eps, k, y,
+                       y_stride);
   return hipGetLastError();
 }
 
