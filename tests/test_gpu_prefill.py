@@ -163,6 +163,31 @@ def test_prefill_small_model_matches_oracle(start, n):
     assert not changed[:, :, [p for p in range(w.num_pages) if p not in touched]].any()
 
 
+SPLIT = wl.Shape(hidden=448, n_heads=7, n_kv_heads=1, head_dim=64, ffn=8320, vocab=5000, n_layers=2)
+
+
+def test_prefill_split_down_projection_matches_oracle():
+    """The down projection split over four workgroups (65 groups of 128
+    columns: 16, 16, 16 and 17 per split, partial sums added in split order by
+    the last to arrive) with a partial 64-row block (70 prompt rows) and a
+    partial 8-tile block (448 outputs): logits, final residual rows and every
+    prompt K/V slot against the oracle's prefill; a second prefill gives
+    identical bits (the split order does not depend on arrival order)."""
+    w = wl.custom("prefill_split", 43, SPLIT, [3 + 70], layers=2, lm_head=True, gamma="random")
+    dm = DeviceModel(w)
+    tokens = w.prompt_tokens(70)
+    got, ws = prefill(dm, tokens, 3, keep_ws=True)
+    x1 = ws_rows(dm, ws, 70, w4.BUF_X, SPLIT.hidden)
+    got2, ws2 = prefill(dm, tokens, 3, keep_ws=True)
+    assert np.array_equal(got.view(np.uint16), got2.view(np.uint16))
+    assert np.array_equal(x1.view(np.uint16), ws_rows(dm, ws2, 70, w4.BUF_X, SPLIT.hidden).view(np.uint16))
+    ref = runs.prefill_run(w, tokens, 3, keep_pools=True)
+    mir = runs.prefill_run(w, tokens, 3, mirror=True, keep_pools=True)
+    check_envelope(got, ref["logits"], mir["logits"], "split prefill logits")
+    check_envelope(x1, ref["x"], mir["x"], "split prefill final residual rows")
+    check_kv(dm, ref, mir, 3, 70, 2)
+
+
 def check_kv(dm, ref, mir, start, n, layers):
     """Every prompt K/V slot of every layer: layer 0 element by element (one
     operation from the embedding), deeper layers (the end of a chain of

@@ -904,7 +904,8 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
 namespace w4 {
 
 struct PfLayout {
-  size_t err, tokens, positions, pt, slot, rope, x, xn, q, o, h, lmxn, total;
+  size_t err, tokens, positions, pt, slot, rope, x, xn, q, o, h, lmxn, kpart, kcount, total;
+  size_t kcount_words;
   int xn_stride, o_stride, h_stride;
 };
 
@@ -932,6 +933,18 @@ static PfLayout pf_layout(const w4_config& c, int max_tokens, int max_pages) {
   L.o = take(n * L.o_stride * 2);
   L.h = take(n * L.h_stride * 2);
   L.lmxn = take((size_t)L.xn_stride * 2);
+  // the prefill GEMMs' split sums and counters (the largest any projection uses)
+  const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  const int proj[4][2] = {{qkv_rows, c.hidden}, {c.hidden, c.n_heads * c.head_dim}, {2 * c.ffn, c.hidden},
+                          {c.hidden, c.ffn}};
+  size_t kf = 0, kc = 0;
+  for (const auto& pr : proj) {
+    kf = std::max(kf, pf_split_floats(max_tokens, pr[0], pr[1]));
+    kc = std::max(kc, pf_split_counters(max_tokens, pr[0], pr[1]));
+  }
+  L.kpart = take(kf * 4);
+  L.kcount_words = kc;
+  L.kcount = take(kc * 4);
   L.total = off;
   return L;
 }
@@ -947,6 +960,15 @@ static int enqueue_prefill(w4_model* m, int n, int start, uint8_t* ws, const PfL
   uint16_t* h = reinterpret_cast<uint16_t*>(at(L.h));
   uint32_t* err = reinterpret_cast<uint32_t*>(at(L.err));
   W4_LAUNCH(launch_fill_u32(err, 1, 0u, s));
+  // split counters start at zero; every split GEMM leaves them at zero
+  float* kpart = reinterpret_cast<float*>(at(L.kpart));
+  uint32_t* kcount = reinterpret_cast<uint32_t*>(at(L.kcount));
+  W4_LAUNCH(launch_fill_u32(kcount, L.kcount_words, 0u, s));
+  auto split = [&](GemvArgs g) {
+    g.kpart = kpart;
+    g.kcount = kcount;
+    return g;
+  };
   TokenPlanArgs p{};
   p.tokens = reinterpret_cast<const int32_t*>(at(L.tokens));
   p.table = m->weights.embed;
@@ -980,7 +1002,7 @@ static int enqueue_prefill(w4_model* m, int n, int start, uint8_t* ws, const PfL
     a.qkv.n_heads = c.n_heads;
     a.qkv.n_kv_heads = c.n_kv_heads;
     a.qkv.head_dim = c.head_dim;
-    W4_LAUNCH(launch_w4_gemm_prefill(EPI_QKV, a, s));
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_QKV, split(a), s));
     PrefillAttnArgs pa{};
     pa.q = q;
     pa.q_stride = c.n_heads * c.head_dim;
@@ -997,13 +1019,16 @@ static int enqueue_prefill(w4_model* m, int n, int start, uint8_t* ws, const PfL
     pa.out_stride = L.o_stride;
     pa.err = err;
     W4_LAUNCH(launch_prefill_attention(pa, c.head_dim, c.n_heads / c.n_kv_heads, s));
-    W4_LAUNCH(launch_w4_gemm_prefill(EPI_RESID, gemv_args(W.o, c.hidden, c.n_heads * c.head_dim, o, L.o_stride,
-                                                          nullptr, 0.f, x, c.hidden, x, n), s));
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_RESID, split(gemv_args(W.o, c.hidden, c.n_heads * c.head_dim, o,
+                                                                L.o_stride, nullptr, 0.f, x, c.hidden, x, n)),
+                                     s));
     W4_LAUNCH(launch_rmsnorm_rows(x, c.hidden, W.mlp_norm, c.rms_eps, c.hidden, xn, L.xn_stride, n, s));
-    W4_LAUNCH(launch_w4_gemm_prefill(EPI_SILU, gemv_args(W.gate_up, 2 * c.ffn, c.hidden, xn, L.xn_stride, nullptr,
-                                                         0.f, h, L.h_stride, nullptr, n), s));
-    W4_LAUNCH(launch_w4_gemm_prefill(EPI_RESID, gemv_args(W.down, c.hidden, c.ffn, h, L.h_stride, nullptr, 0.f, x,
-                                                          c.hidden, x, n), s));
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_SILU, split(gemv_args(W.gate_up, 2 * c.ffn, c.hidden, xn, L.xn_stride,
+                                                               nullptr, 0.f, h, L.h_stride, nullptr, n)),
+                                     s));
+    W4_LAUNCH(launch_w4_gemm_prefill(EPI_RESID, split(gemv_args(W.down, c.hidden, c.ffn, h, L.h_stride, nullptr,
+                                                                0.f, x, c.hidden, x, n)),
+                                     s));
   }
   F16GemvArgs f{};
   f.w = static_cast<const uint8_t*>(m->weights.lm_head);

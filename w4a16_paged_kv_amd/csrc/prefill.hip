@@ -15,6 +15,8 @@
 // weights), so the kernel reuses each dequantised block for many rows.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "attn_item.h"
 #include "gemv_b1.h"
 
@@ -113,8 +115,12 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// WPE: wavefronts per SIMD the register allocation must allow.
-template <int EPI, int WM, int WN, int MR, int NTW, int NS, int WPE>
+// WPE: wavefronts per SIMD the register allocation must allow. KS > 1: the
+// 128-column groups are split over KS workgroups (blockIdx.z), whose fp32
+// sums meet in a.kpart; the last of a tile block's workgroups to arrive (a
+// counter in a.kcount, zero between launches) adds them in split order and
+// runs the epilogue.
+template <int EPI, int WM, int WN, int MR, int NTW, int NS, int WPE, int KS>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void w4_gemm_prefill_dma_kernel(GemvArgs a) {
   using T = PfRing<WM, WN, MR, NTW, NS>;
@@ -129,6 +135,8 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
   const int m0 = blockIdx.x * T::kRows;                // row blocks fastest: neighbours share weights
   const int tg0 = blockIdx.y * T::kTiles;              // the workgroup's first weight tile
   const int G = a.groups;
+  const int kz = KS > 1 ? (int)blockIdx.z : 0;
+  const int gb = kz * G / KS, ng = (kz + 1) * G / KS - gb;   // this workgroup's groups [gb, gb + ng)
   // Buffer resources rebased at the workgroup's first row and first tile:
   // every offset fits 32 bits at any batch, a group advances through the
   // scalar offset alone (no per-load address arithmetic), and the hardware's
@@ -226,15 +234,17 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
         for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(sc[j], d[i][j][q], acc[i][j][q]);
   };
 
-  // Ring of NS stages: group g in ring g % NS, NS - 1 groups in flight. With
-  // three stages every stage issues exactly kInst loads per thread (past the
-  // last group they reload group G - 1 into the slot no later stage reads),
-  // so one wait form holds everywhere: at stage g the loads of g + 1 are the
-  // only ones newer than those of g. With two, a stage waits for all its
-  // loads. Columns at or past k (a partial last group) are zeroed in LDS
-  // before the last group is multiplied, as the decode GEMV zeroes them.
+  // Ring of NS stages: the workgroup's l-th group in ring l % NS, NS - 1
+  // groups in flight. With three stages every stage issues exactly kInst
+  // loads per thread (past the last group they reload it into the slot no
+  // later stage reads), so one wait form holds everywhere: at stage l the
+  // loads of l + 1 are the only ones newer than those of l. With two, a stage
+  // waits for all its loads. Columns at or past k (a partial last group) are
+  // zeroed in LDS before that group is multiplied, as the decode GEMV zeroes
+  // them.
   const bool ragged = (a.k & (kGroup - 1)) != 0;
-  auto stage = [&](int g, uint8_t* cur, uint8_t* nxt) {
+  auto stage = [&](int l, uint8_t* cur, uint8_t* nxt) {
+    const int g = gb + l;
     // this thread's loads of stage g are done; after the barrier every
     // thread's are, and every wavefront has consumed its reads of stage
     // g - 1 (whose ring slot the next loads overwrite). A bare s_barrier:
@@ -252,31 +262,71 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
       }
       __syncthreads();
     }
-    if constexpr (NS == 3) issue(min(g + 2, G - 1), nxt);
-    else if (g + 1 < G) issue(g + 1, nxt);
+    if constexpr (NS == 3) issue(gb + min(l + 2, ng - 1), nxt);
+    else if (l + 1 < ng) issue(g + 1, nxt);
     compute(cur);
   };
-  issue(0, ring0);
-  int g = 0;
+  issue(gb, ring0);
+  int l = 0;
   if constexpr (NS == 3) {
-    issue(min(1, G - 1), ring1);
-    for (; g + 3 <= G; g += 3) {
-      stage(g, ring0, ring2);
-      stage(g + 1, ring1, ring0);
-      stage(g + 2, ring2, ring1);
+    issue(gb + min(1, ng - 1), ring1);
+    for (; l + 3 <= ng; l += 3) {
+      stage(l, ring0, ring2);
+      stage(l + 1, ring1, ring0);
+      stage(l + 2, ring2, ring1);
     }
-    if (g < G) {                                     // nested, so no path reads a slot still being filled
-      stage(g, ring0, ring2);
-      if (g + 1 < G) stage(g + 1, ring1, ring0);
+    if (l < ng) {                                    // nested, so no path reads a slot still being filled
+      stage(l, ring0, ring2);
+      if (l + 1 < ng) stage(l + 1, ring1, ring0);
     }
   } else {
-    for (; g + 2 <= G; g += 2) {
-      stage(g, ring0, ring1);
-      stage(g + 1, ring1, ring0);
+    for (; l + 2 <= ng; l += 2) {
+      stage(l, ring0, ring1);
+      stage(l + 1, ring1, ring0);
     }
-    if (g < G) stage(g, ring0, ring1);
+    if (l < ng) stage(l, ring0, ring1);
   }
   wait_vm<0>();                                      // no load may land in LDS after the workgroup ends
+
+  if constexpr (KS > 1) {
+    // Partial sums move between workgroups (and XCDs) through device-scope
+    // 16-byte stores and loads; each workgroup's stores complete before it
+    // counts itself. Lane l's block (i, j) of wavefront w sits at f4 index
+    // ((w MR + i) NTW + j) 64 + l of the workgroup's split slice.
+    constexpr int PB = T::kThreads / 64 * MR * NTW * 64;          // f4 per split slice
+    const int blk = blockIdx.y * gridDim.x + blockIdx.x;
+    const __amdgpu_buffer_rsrc_t rp = buf_rsrc(a.kpart + (size_t)blk * KS * PB * 4);
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, acc[i][j]), rp,
+                                               16 * (kz * PB + ((wave * MR + i) * NTW + j) * 64 + lane), 0,
+                                               kPolicySc1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ int s_last;
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(a.kcount + blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(KS - 1);
+    __syncthreads();
+    if (!s_last) return;                             // uniform across the workgroup
+#pragma unroll
+    for (int i = 0; i < MR; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        f4_t part[KS];                               // every split's load in flight, then the sum in split order
+#pragma unroll
+        for (int c = 0; c < KS; ++c)
+          part[c] = c == kz ? acc[i][j]
+                            : __builtin_bit_cast(f4_t, ld128_agent(rp, 16 * (c * PB + ((wave * MR + i) * NTW + j) * 64 + lane)));
+        f4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KS; ++c) v += part[c];
+        acc[i][j] = v;
+      }
+    if (tid == 0) __hip_atomic_store(a.kcount + blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   const int i16 = lane & 15;
   const int t0 = tg0 + wn * NTW;
@@ -293,12 +343,40 @@ void w4_gemm_prefill_dma_kernel(GemvArgs a) {
       }
 }
 
-template <int EPI, int WM, int WN, int MR, int NTW, int NS, int WPE>
+template <int EPI, int WM, int WN, int MR, int NTW, int NS, int WPE, int KS = 1>
 static hipError_t launch_pf_tile(const GemvArgs& a, hipStream_t s) {
   using T = PfRing<WM, WN, MR, NTW, NS>;
-  hipLaunchKernelGGL((w4_gemm_prefill_dma_kernel<EPI, WM, WN, MR, NTW, NS, WPE>),
-                     dim3(ceil_div(a.batch, T::kRows), ceil_div(a.tiles, T::kTiles)), dim3(T::kThreads), 0, s, a);
+  hipLaunchKernelGGL((w4_gemm_prefill_dma_kernel<EPI, WM, WN, MR, NTW, NS, WPE, KS>),
+                     dim3(ceil_div(a.batch, T::kRows), ceil_div(a.tiles, T::kTiles), KS), dim3(T::kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// Groups split over four workgroups when split storage is given, for long
+// rows (64 groups and more) with fewer 64-row workgroups than three per CU:
+// 64-row tiles then, instead of 32-row tiles. Measured at 512 rows: down
+// (148 groups) 99-109 us unsplit with 32-row tiles, 83.3 us split; o-proj and
+// qkv (28 groups) split in two took 30.1 and 39.8 us against 24 and 35 us
+// unsplit, the split's stores, counter and reloads outweighing its gain.
+static int pf_splits(int rows, int tiles, int groups) {
+  const long wg64 = (long)ceil_div(rows, 64) * ceil_div(tiles, 8);
+  return wg64 < 768 && groups >= 64 ? 4 : 1;
+}
+
+// Split storage of one prefill GEMM, enough for any row count up to `rows`:
+// KS slices of every 64-row x 8-tile block's fp32 sums and one arrival
+// counter per block. A GEMM splits only below 768 blocks, so the most blocks
+// a split launch has is min(ceil(rows / 64), 767 / tile blocks) row blocks.
+static long pf_split_blocks(int rows, int n) {
+  const long tb = ceil_div(w4_tiles(n), 8);
+  return std::min<long>(ceil_div(rows, 64), 767 / tb) * tb;
+}
+size_t pf_split_floats(int rows, int n, int k) {
+  if (pf_splits(1, w4_tiles(n), w4_groups(k)) == 1) return 0;          // never splits
+  return (size_t)pf_splits(1, w4_tiles(n), w4_groups(k)) * pf_split_blocks(rows, n) * 64 * 128;
+}
+size_t pf_split_counters(int rows, int n, int k) {
+  if (pf_splits(1, w4_tiles(n), w4_groups(k)) == 1) return 0;
+  return (size_t)pf_split_blocks(rows, n);
 }
 
 template <int EPI>
@@ -313,6 +391,10 @@ static hipError_t launch_pf_epi(const GemvArgs& a, hipStream_t s) {
   // the narrower shapes with 32-row tiles and three stages (qkv 31.1 us,
   // o-proj 23.5, down 108.3, against 35.8 / 29.2 / 139.7).
   if ((long)ceil_div(a.batch, 64) * ceil_div(a.tiles, 8) >= 1024) return launch_pf_tile<EPI, 1, 4, 4, 2, 2, 3>(a, s);
+  if (a.kpart && a.kcount) {                         // split storage given (w4_prefill)
+    const int ks = pf_splits(a.batch, a.tiles, a.groups);
+    if (ks == 4) return launch_pf_tile<EPI, 1, 4, 4, 2, 2, 3, 4>(a, s);
+  }
   return launch_pf_tile<EPI, 1, 4, 2, 2, 3, 3>(a, s);
 }
 

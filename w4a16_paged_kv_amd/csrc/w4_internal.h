@@ -221,6 +221,11 @@ hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStrea
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t s);
 // Prefill (prefill.hip): a.batch = prompt rows (any count); epilogues as the
 // decode projections, with row m's token plan entries for EPI_QKV.
+// Split storage a prefill GEMM of `rows` rows, n outputs and k inputs uses
+// (fp32 sums and arrival counters; 0 if it does not split). Counters start
+// at zero and every split GEMM leaves them at zero.
+size_t pf_split_floats(int rows, int n, int k);
+size_t pf_split_counters(int rows, int n, int k);
 hipError_t launch_w4_gemm_prefill(int epi, const GemvArgs& a, hipStream_t s);
 hipError_t launch_prefill_attention(const PrefillAttnArgs& a, int head_dim, int group, hipStream_t s);
 hipError_t launch_kv_pages(const KvCopyArgs& a, hipStream_t s);
