@@ -55,13 +55,18 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool pager = wave < W;  // this wavefront streams pages
-  const int32_t* pt = a.page_tables + (size_t)b * a.max_pages;
+  // The page table and context lengths are read-only here: read through the
+  // constant address space they are scalar loads, so fetching the next page's
+  // id does not wait behind the K/V loads in flight (with a vector load it
+  // did, and a wavefront then had one page in flight at a time).
+  typedef const __attribute__((address_space(4))) int32_t* cptr_t;
+  const cptr_t pt = (cptr_t)(a.page_tables + (size_t)b * a.max_pages);
   // the context length, this wavefront's first two page ids and the queries
   // are independent: issue them together (page ids are validated below)
   const int pw0 = split * a.pages_per_split + wave;
   int pid_cur = pt[min(pw0, a.max_pages - 1)];
   int pid_nxt = pt[min(pw0 + W, a.max_pages - 1)];
-  int ctx = a.ctx_lens[b];
+  int ctx = ((cptr_t)a.ctx_lens)[b];
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc(a.q + (size_t)b * a.q_stride + (size_t)kvh * GQ * D);
   u4_t qv[(GQ * D + NT * 8 - 1) / (NT * 8)];
 #pragma unroll
