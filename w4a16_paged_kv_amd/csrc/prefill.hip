@@ -435,7 +435,9 @@ __global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(
   __shared__ f4_t sm_o[W][NS][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int blk = blockIdx.x, h = blockIdx.y, kvh = h / GQ;
+  // longest items first (the last row blocks attend the most pages), every
+  // head of an item together: the short items fill the end of the launch
+  const int blk = gridDim.y - 1 - blockIdx.y, h = blockIdx.x, kvh = h / GQ;
   const int r0 = 16 * blk;                       // first prompt row of the item
   const int last_row = min(r0 + 15, a.n - 1);
   const int p_last = a.start + last_row;         // the item's last position
@@ -617,7 +619,7 @@ __global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(
 
 template <int D>
 static hipError_t launch_pfa_d(const PrefillAttnArgs& a, int group, hipStream_t s) {
-  const dim3 grid(ceil_div(a.n, 16), a.n_heads), block(kPfaWaves * 64);
+  const dim3 grid(a.n_heads, ceil_div(a.n, 16)), block(kPfaWaves * 64);
   switch (group) {
     case 1: hipLaunchKernelGGL((prefill_attn_kernel<D, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((prefill_attn_kernel<D, 2>), grid, block, 0, s, a); break;
