@@ -151,10 +151,9 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
   const uint16_t* sb = reinterpret_cast<const uint16_t*>(a.w + (size_t)a.tiles * G * 1024) + base * 16 + (lane & 15);
   const uint16_t* xl = xs + (size_t)(lane & 15) * KW + 32 * (lane >> 4);
   const uint32_t mlo = vgpr_const(kMaskLo), mhi = vgpr_const(kMaskHi);
-  const int e = threadIdx.x & 1;
   const bool one_window = G <= GW;
   __shared__ __align__(16) float s_rs[16];
-  __shared__ __align__(16) float s_ss[kRowsThreads / 64][16];
+  __shared__ __align__(16) float s_ss[kRowsThreads / 64][8];
   // RMSNorm over rows longer than one window: wavefront w sums the squares
   // of rows w, w + NW, .. in a pre-pass
   if (a.gamma && !one_window) {
@@ -205,78 +204,112 @@ __global__ __launch_bounds__(kRowsThreads) void w4_gemm_rows_kernel(GemvArgs a, 
           acc += d * h2f((uint16_t)sc[u]);
         }
     };
-    // word cw of every row: columns 128 g0 + 8 cw .. +8 (zero past k, past the
-    // window and for rows >= batch); unconditional loads from clamped addresses
-    const int cw = threadIdx.x;
-    const int col = 128 * g0 + 8 * cw;
-    const bool cin = cw < 16 * gn && col < a.k;
-    const int colc = min(col, a.k - 8);
-    u4_t xv[16];
+    // Staging: thread t takes rows 8 h .. 8 h + 8 (h = t / JW, uniform per
+    // wavefront) of the window's 16-column segment sj = t % JW, as two natural
+    // 8-column words per row. The slot groups 2 p and 2 p + 1 of a 32-column
+    // chunk hold the 32-bit pairs (0, 2) and (1, 3) of the chunk's words 2 p
+    // and 2 p + 1, so a segment's two slot words come from its own two words
+    // (no exchange between lanes). Loads past k and of rows >= batch read zero.
+    const int JW = (8 * GW + 63) & ~63;
+    const int hh = __builtin_amdgcn_readfirstlane((int)threadIdx.x / JW);
+    const int sj = (int)threadIdx.x % JW;
+    const int col = 128 * g0 + 16 * sj;
+    const bool stager = hh < 2;
+    u4_t xa[8], xb[8];
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-      xv[m] = *reinterpret_cast<const u4_t*>(a.x + (size_t)min(m, a.batch - 1) * a.x_stride + colc);
-    const u4_t gv = a.gamma ? *reinterpret_cast<const u4_t*>(a.gamma + colc) : (u4_t){0u, 0u, 0u, 0u};
+    for (int r = 0; r < 8; ++r) {
+      const int m = 8 * hh + r;
+      const __amdgpu_buffer_rsrc_t rx =
+          range_rsrc(a.x + (size_t)min(m, 15) * a.x_stride, stager && m < a.batch ? 2 * a.k : 0);
+      xa[r] = ld128(rx, 2 * col);
+      xb[r] = ld128(rx, 2 * col + 16);
+    }
+    const __amdgpu_buffer_rsrc_t rg = range_rsrc(a.gamma ? a.gamma : a.x, a.gamma ? 2 * a.k : 0);
+    const u4_t ga = ld128(rg, 2 * col), gb = ld128(rg, 2 * col + 16);
     __builtin_amdgcn_sched_barrier(0);
     load(bufA, scA, 0);  // the window's first weight batch, behind the activation loads
     __builtin_amdgcn_sched_barrier(0);
+    if (a.gamma && one_window) {  // each row's sum of squares: per thread, per wavefront, then in wavefront order
+      float ss[8];
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-      if (!(cin && m < a.batch)) xv[m] = (u4_t){0u, 0u, 0u, 0u};
-    if (a.gamma && one_window) {  // this thread's share of each row's sum of squares, in order
-      float ss[16];
+      for (int r = 0; r < 8; ++r) {
+        ss[r] = 0.f;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        ss[m] = 0.f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const h2_t h = as_h2(xv[m][c]);
-          ss[m] = fmaf((float)h[0], (float)h[0], ss[m]);
-          ss[m] = fmaf((float)h[1], (float)h[1], ss[m]);
+        for (int c = 0; c < 8; ++c) {  // two squares per fp16 dot product, accumulated in fp32
+          const h2_t h = as_h2(c < 4 ? xa[r][c] : xb[r][c - 4]);
+          ss[r] = __builtin_amdgcn_fdot2(h, h, ss[r], false);
         }
       }
-      // the 16 rows' reductions without a branch between them, so their
+      // the rows' reductions without a branch between them, so their
       // dependent DPP chains interleave
 #pragma unroll
-      for (int m = 0; m < 16; ++m) ss[m] = wave_sum(ss[m]);
-      if (lane == 0)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f4_t*>(&s_ss[wave][4 * q]) = (f4_t){ss[4 * q], ss[4 * q + 1], ss[4 * q + 2], ss[4 * q + 3]};
+      for (int r = 0; r < 8; ++r) ss[r] = wave_sum(ss[r]);
+      if (lane == 0 && stager) {
+        *reinterpret_cast<f4_t*>(&s_ss[wave][0]) = (f4_t){ss[0], ss[1], ss[2], ss[3]};
+        *reinterpret_cast<f4_t*>(&s_ss[wave][4]) = (f4_t){ss[4], ss[5], ss[6], ss[7]};
+      }
       __syncthreads();
-      if (threadIdx.x < 16) {
+      if (threadIdx.x < 16) {  // row 8 h + r: the wavefronts of half h
+        const int h = threadIdx.x >> 3, r = threadIdx.x & 7;
         float tot = 0.f;
-        for (int w = 0; w < NW; ++w) tot += s_ss[w][threadIdx.x];
+        for (int w = h * (JW / 64); w < (h + 1) * (JW / 64); ++w) tot += s_ss[w][r];
         s_rs[threadIdx.x] = 1.0f / sqrtf(tot / (float)a.k + a.eps);
       }
     }
     __syncthreads();  // s_rs ready; the previous window's reads of xs are done
-    if (a.gamma) {  // fp16(x * rs * gamma), the batch-1 staging's rounding
-      float rsv[16];
+    {
+      // per row: fp16(x * rs * gamma) with RMSNorm (the batch-1 staging's
+      // rounding), the normalised row to xn_out from workgroup 0, the two slot
+      // words to LDS
+      float rsv[8];
+      if (a.gamma) {
+        const int hs = stager ? hh : 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4_t r4 = *reinterpret_cast<const f4_t*>(&s_rs[4 * q]);
+        for (int q = 0; q < 2; ++q) {
+          const f4_t r4 = *reinterpret_cast<const f4_t*>(&s_rs[8 * hs + 4 * q]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rsv[4 * q + j] = r4[j];
+          for (int j = 0; j < 4; ++j) rsv[4 * q + j] = r4[j];
+        }
       }
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const float rs = rsv[m];
+      // (x rs) gamma as two fused multiply-adds with a zero addend: the same
+      // roundings as the products (up to the sign of a zero result), and each
+      // takes its fp16 operand without a separate conversion
+      auto scale = [&](u4_t& w, const u4_t g, float rs) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const h2_t hv = as_h2(xv[m][c]), hg = as_h2(gv[c]);
+          const h2_t hv = as_h2(w[c]), hg = as_h2(g[c]);
           h2_t r;
-          r[0] = (_Float16)((float)hv[0] * rs * (float)hg[0]);
-          r[1] = (_Float16)((float)hv[1] * rs * (float)hg[1]);
-          xv[m][c] = __builtin_bit_cast(uint32_t, r);
+          r[0] = (_Float16)fmaf(fmaf((float)hv[0], rs, 0.f), (float)hg[0], 0.f);
+          r[1] = (_Float16)fmaf(fmaf((float)hv[1], rs, 0.f), (float)hg[1], 0.f);
+          w[c] = __builtin_bit_cast(uint32_t, r);
         }
-        if (a.xn_out && blockIdx.x == 0 && cin && m < a.batch)
-          *reinterpret_cast<u4_t*>(a.xn_out + (size_t)m * a.xn_stride + col) = xv[m];
-      }
-    }
+      };
+      const bool xn = a.gamma && a.xn_out && blockIdx.x == 0 && stager;
+      const bool store = stager && sj < 8 * GW;
+      const h2_t q16 = {(_Float16)0.0625f, (_Float16)0.0625f};  // odd slot groups: x / 16 (see slot_word)
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const u4_t o = slot_word(xv[m], e);  // every lane: quad permutes
-      if (cw < 16 * GW) *reinterpret_cast<u4_t*>(xs + (size_t)m * KW + 8 * cw) = o;
+      for (int r = 0; r < 8; ++r) {
+        const int m = 8 * hh + r;
+        if (a.gamma) {
+          scale(xa[r], ga, rsv[r]);
+          scale(xb[r], gb, rsv[r]);
+        }
+        if (xn && m < a.batch) {
+          uint16_t* xo = a.xn_out + (size_t)m * a.xn_stride + col;
+          if (col < a.k) *reinterpret_cast<u4_t*>(xo) = xa[r];
+          if (col + 8 < a.k) *reinterpret_cast<u4_t*>(xo + 8) = xb[r];
+        }
+        if (store) {
+          const u4_t ev = {xa[r][0], xa[r][2], xb[r][0], xb[r][2]};
+          const u4_t od = {__builtin_bit_cast(uint32_t, as_h2(xa[r][1]) * q16),
+                           __builtin_bit_cast(uint32_t, as_h2(xa[r][3]) * q16),
+                           __builtin_bit_cast(uint32_t, as_h2(xb[r][1]) * q16),
+                           __builtin_bit_cast(uint32_t, as_h2(xb[r][3]) * q16)};
+          uint16_t* dst = xs + (size_t)m * KW + 16 * sj;
+          *reinterpret_cast<u4_t*>(dst) = ev;
+          *reinterpret_cast<u4_t*>(dst + 8) = od;
+        }
+      }
     }
     __syncthreads();
     for (int i = 0; i < ng; i += 2 * kUnroll) {
@@ -664,8 +697,9 @@ static hipError_t launch_w4_epi(const GemvArgs& a, hipStream_t s) {
     // the split-K path needs its buffers, and RMSNorm needs whole rows
     if ((a.kpart == nullptr) != (a.kcount == nullptr)) return hipErrorInvalidValue;
     const RowsPlan p = w4_rows_plan(a.tiles, a.groups, a.kpart != nullptr && a.gamma == nullptr);
-    // activation window: at most 4096 columns (128 KiB of LDS); a thread per window word
-    const int nt = std::max({256, 64 * p.s * p.tw, (int)round_up(16 * p.gw, 64)});
+    // activation window: at most 4096 columns (128 KiB of LDS); two threads
+    // per 16-column segment, each half of the threads a whole number of wavefronts
+    const int nt = std::max({256, 64 * p.s * p.tw, 2 * (int)round_up(8 * p.gw, 64)});
     const size_t lds = (size_t)16 * (p.gw * kGroup + 8) * 2 + ((size_t)(nt / 64) * 256 + (size_t)p.tw * 256) * 4;
     hipError_t e = hipSuccess;
     switch (p.s) {

@@ -94,6 +94,11 @@ __device__ __forceinline__ void st16_agent(uint16_t* p, uint16_t v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
+// A raw buffer of `bytes` bytes at base: loads at or past the end read zero
+// without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 __device__ __forceinline__ u4_t ld128(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }

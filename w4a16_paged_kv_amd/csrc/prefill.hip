@@ -96,10 +96,6 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // LDS slot key of an activation row (mod 16): its 2-bit halves swapped
 __device__ __forceinline__ int swz(int x) { return ((x & 3) << 2) | (x >> 2); }
 
-// A raw buffer of `bytes` bytes at base: loads at or past the end read zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
 // buffer-to-LDS copies: lane L's 16 (4) bytes at voffset + soffset land at the
 // LDS base + 16 L (4 L)
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_base) {
