@@ -112,3 +112,13 @@ def test_layer_long_ffn_split_k(ffn, ctx):
     cover five chunks and a partial last tile group."""
     sh = wl.Shape(hidden=448, n_heads=7, n_kv_heads=1, head_dim=64, ffn=ffn, vocab=64, n_layers=1)
     staged(wl.custom(f"ffn{ffn}", 24, sh, ctx, gamma="random"))
+
+
+def test_layer_wide_hidden_two_windows():
+    """Batch > 1 with hidden 4608 (36 groups, more than one 32-group activation
+    window): the RMSNorm'd projections take their sums of squares from a
+    pre-pass over the rows and stage them in two windows, the second with 4
+    groups of 32."""
+    sh = wl.Shape(hidden=4608, n_heads=72, n_kv_heads=9, head_dim=64, ffn=512, vocab=64, n_layers=1)
+    staged(wl.custom("wide", 25, sh, [40, 3, 129], gamma="random"), bias=True)
+
