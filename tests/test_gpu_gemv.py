@@ -38,6 +38,24 @@ def test_w4_gemv_matches_oracle(n, k, batch):
         assert_close(got[b], od.r16(od.gemv_w4(q, s, x[b])), f"row {b}")
 
 
+@pytest.mark.parametrize("n,k", [(600, 448), (1000, 4224), (300, 200)])
+@pytest.mark.parametrize("batch", [2, 8, 9, 15])
+def test_w4_gemv_batches_across_the_row_halves(n, k, batch):
+    """Batch 2..15: the activation rows are staged by two halves of the
+    workgroup's threads (rows 0-7 and 8-15), so these batches leave one half
+    partly or wholly empty; k = 448 and 200 end inside a group, k = 4224 (33
+    groups) needs a second activation window."""
+    print(f"w4_gemv n={n} k={k} batch={batch}", flush=True)
+    q, s = wl.int4_matrix(79, 0, 0, n, k)
+    x = wl.f16_normal(wl.rng(79, 0, 1), (batch, k))
+    y = torch.empty((batch, n), dtype=torch.float16, device="cuda")
+    w4.w4_gemv(to_dev(w4.pack_weights_w4g128(q, s)), to_dev(x), y, n, k, batch)
+    torch.cuda.synchronize()
+    got = to_np16(y)
+    for b in range(batch):
+        assert_close(got[b], od.r16(od.gemv_w4(q, s, x[b])), f"batch {batch} row {b}")
+
+
 def test_w4_gemv_one_hot_is_exact():
     n, k = 256, 384
     q, s = wl.int4_matrix(78, 0, 0, n, k)
