@@ -182,11 +182,16 @@ typedef struct w4_config {
 
 /* Device KV cache: fp16 [L][2][P][Hkv][16 * D] -- for layer l, K pages then V
  * pages, each page holding one 4 KiB (for D = 128) slice per KV head
- * [RT-arch]. A K slice is [16 tokens][D]. A V slice holds value (token t,
- * dim d) at element ((d / 32) * 64 + d % 16 + 16 (t / 4)) * 8 + ((d / 16) % 2)
- * * 4 + t % 4: four consecutive tokens of one dimension are one operand of
- * the attention's P V product on the matrix cores, and a lane's operands of
- * two neighbouring 16-dim slices are 16 contiguous bytes. */
+ * [RT-arch]. A K slice holds value (token t, dim d) at element ((d / 32) * 64
+ * + 16 ((d / 8) % 4) + t) * 8 + d % 8: eight consecutive dims of one token
+ * are one 16-byte operand of the attention's scores on the matrix cores, and
+ * the 64 operands of one 32-dim step are 1 KiB of contiguous memory. A V
+ * slice holds value (token t, dim d) at element ((d / 32) * 64 + d % 16 + 16
+ * (t / 4)) * 8 + ((d / 16) % 2) * 4 + t % 4: four consecutive tokens of one
+ * dimension are one operand of the attention's P V product, and a lane's
+ * operands of two neighbouring 16-dim slices are 16 contiguous bytes.
+ * kv_write_pages / kv_read_pages convert from and to natural [token][D]
+ * rows. */
 size_t kv_cache_bytes(const w4_config* cfg, int32_t num_pages);
 
 typedef struct w4_layer_weights {
@@ -314,7 +319,8 @@ int64_t w4_prefill_buffer(const w4_config* cfg, int32_t n_tokens, int32_t max_pa
                           int32_t* row_stride);
 
 /* Copies between natural-layout K/V rows and one layer of a KV cache laid out
- * as above (K slices [16][D], V slices in the P V operand order), so callers
+ * as above (K slices in the score operand order, V slices in the P V operand
+ * order), so callers
  * can fill pages from K/V computed elsewhere or read them back ([H100-kv]:
  * the cache is addressed through the page table). Token i of the call sits
  * at position start + i, in page page_table[(start + i) / 16], slot
@@ -387,9 +393,9 @@ int  w4_gemv_f16(const void* packed, const uint16_t* x, uint16_t* y, int32_t n, 
 /* Paged-attention decode [H100-kv]: for each sequence b and query head h,
  * out[b][h] = fp16(sum_t softmax_t(q[b][h] . K_t / sqrt(D)) V_t) over tokens
  * t in [0, ctx_lens[b]), K_t/V_t read from KV head h / (Hq/Hkv) through the
- * page table. q: device fp16 [batch][Hq][D]; k_pool: device fp16
- * [num_pages][Hkv][16][D]; v_pool: device fp16 [num_pages][Hkv][16 * D] (the
- * KV cache's slice layouts); page_tables: device int32 [batch][max_pages];
+ * page table. q: device fp16 [batch][Hq][D]; k_pool, v_pool: device fp16
+ * [num_pages][Hkv][16 * D] (the KV cache's K and V slice layouts above);
+ * page_tables: device int32 [batch][max_pages];
  * ctx_lens: device int32 [batch]; out: device fp16 [batch][Hq][D].
  * Device-resident indices are clamped like decode_step_device: a page id
  * outside [0, num_pages) contributes nothing, ctx_lens are clamped to

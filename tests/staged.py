@@ -11,7 +11,7 @@ import workloads as wl
 from oracle import decode as od
 from oracle import runs
 from tests.gpu_util import assert_close, to_np16
-from workloads.device import DeviceModel, to_dev, v_pages_host
+from workloads.device import DeviceModel, k_pages_host, to_dev, v_pages_host
 
 
 def buf(dm, which, batch):
@@ -21,11 +21,10 @@ def buf(dm, which, batch):
 
 
 def kv_slot(dm, layer, which, page, slot):
-    """The [Hkv][D] values of one token slot (V slices in the device order)."""
+    """The [Hkv][D] values of one token slot (K and V slices in the device orders)."""
     pool = dm.kv_cache[layer, which]
-    if which == 1:
-        return to_np16(v_pages_host(pool[page])[:, slot])
-    return to_np16(pool[page, :, slot])
+    host = v_pages_host if which == 1 else k_pages_host
+    return to_np16(host(pool[page])[:, slot])
 
 
 def staged_layer(dm, w, layer, x_in, lw, kp, vp, tag="", log=print, live=None):

@@ -10,13 +10,13 @@ import w4a16_paged_kv_amd as w4
 import workloads as wl
 from oracle import runs
 from tests.gpu_util import assert_close, to_np16
-from workloads.device import to_dev, v_pages_device
+from workloads.device import k_pages_device, to_dev, v_pages_device
 
 pytestmark = pytest.mark.gpu
 
 
 def run_attn(q, k, v, pt, ctx, n_heads, n_kv, d):
-    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v_pages_device(v))
+    qd, kd, vd = to_dev(q), to_dev(k_pages_device(k)), to_dev(v_pages_device(v))
     ptd = torch.from_numpy(np.ascontiguousarray(pt, np.int32)).cuda()
     cd = torch.from_numpy(np.ascontiguousarray(ctx, np.int32)).cuda()
     ws = torch.empty(w4.paged_attention_workspace_bytes(len(ctx), n_heads, n_kv, d, pt.shape[1]),

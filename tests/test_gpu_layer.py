@@ -16,7 +16,7 @@ import workloads as wl
 from oracle import runs
 from tests.gpu_util import assert_close, to_np16
 from tests.staged import check_envelope, staged_layer
-from workloads.device import DeviceModel, to_dev, v_pages_host
+from workloads.device import DeviceModel, k_pages_host, to_dev, v_pages_host
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def run_layer(dm: DeviceModel, x_in: np.ndarray, layer: int = 0):
 
 def check_kv_writes_only_the_slot(dm, w, cache0):
     diff = dm.kv_cache.cpu().view(torch.int16) != cache0.cpu().view(torch.int16)    # [L,2,P,Hkv,16,D]
-    k_changed = diff[:, 0].any(dim=-1)                                                 # K slices [16][D]
+    k_changed = k_pages_host(diff[:, 0]).any(dim=-1)                                  # K slices, device order
     v_changed = v_pages_host(diff[:, 1]).any(dim=-1)                                  # V slices, device order
     changed = torch.stack([k_changed, v_changed], dim=1)                                # [L,2,P,Hkv,16]
     expect = torch.zeros_like(changed)

@@ -14,7 +14,7 @@ from oracle import prefill as op
 from oracle import runs
 from tests.gpu_util import assert_close, to_np16
 from tests.staged import check_envelope
-from workloads.device import DeviceModel, to_dev, v_pages_device, v_pages_host
+from workloads.device import DeviceModel, k_pages_device, k_pages_host, to_dev, v_pages_device, v_pages_host
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,8 @@ def test_prefill_gemm_matches_oracle(n, k, m):
 
 def test_kv_pages_write_read_round_trip_and_layout():
     """kv_write_pages puts natural-layout K/V rows at their page slots in the
-    cache's layouts (K [16][D], V in P V operand order) and nothing else;
+    cache's layouts (K in score operand order, V in P V operand order) and
+    nothing else;
     kv_read_pages gives them back; a token whose page id is invalid is
     skipped."""
     cfg = w4.make_config(448, 7, 2, 64, 1536, 100, 3, 1e-6, 1e6)
@@ -68,14 +69,14 @@ def test_kv_pages_write_read_round_trip_and_layout():
         page = pt_host[p // 16]
         if page < 0:
             continue
-        kc[page, :, p % 16] = k[i].view(np.uint16)
-        vh = np.zeros((hkv, 16, d), np.uint16)
-        vh[:, p % 16] = v[i].view(np.uint16)
         mask = np.zeros((hkv, 16, d), bool)
         mask[:, p % 16] = True
-        vd = v_pages_device(vh.view(np.float16)).view(np.uint16)
-        md = v_pages_device(mask)
-        vc[page][md] = vd[md]
+        for dst, row, to_device in ((kc, k[i], k_pages_device), (vc, v[i], v_pages_device)):
+            h = np.zeros((hkv, 16, d), np.uint16)
+            h[:, p % 16] = row.view(np.uint16)
+            hd = to_device(h.view(np.float16)).view(np.uint16)
+            md = to_device(mask)
+            dst[page][md] = hd[md]
     got = cache.cpu().numpy().view(np.uint16)
     assert np.array_equal(got, expect)
     kb = torch.empty((n, hkv, d), dtype=torch.float16, device="cuda")
@@ -113,7 +114,7 @@ def check_prefill_attention(dm, ws, tokens, start, tag):
     q = ws_rows(dm, ws, n, w4.BUF_Q, nq).reshape(n, sh.n_heads, sh.head_dim)
     o = ws_rows(dm, ws, n, w4.BUF_O, nq)
     layer = sh.n_layers - 1
-    kp = to_np16(dm.kv_cache[layer, 0]).astype(np.float64)
+    kp = k_pages_host(to_np16(dm.kv_cache[layer, 0])).astype(np.float64)
     vp = v_pages_host(to_np16(dm.kv_cache[layer, 1])).astype(np.float64)
     pt = dm.w.page_tables[0]
     ref = np.stack([od.attention_decode(q[i], kp, vp, pt, start + i + 1).reshape(-1) for i in range(n)])

@@ -11,7 +11,7 @@ import w4a16_paged_kv_amd as w4
 import workloads as wl
 from oracle import runs
 from tests.gpu_util import assert_close, to_np16
-from workloads.device import to_dev, v_pages_device
+from workloads.device import k_pages_device, to_dev, v_pages_device
 
 
 def _poison(k, v, pt, ctx):
@@ -27,7 +27,7 @@ def _poison(k, v, pt, ctx):
 
 def _both(w, q, k, v):
     sh = w.shape
-    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v_pages_device(v))
+    qd, kd, vd = to_dev(q), to_dev(k_pages_device(k)), to_dev(v_pages_device(v))
     ptd = torch.from_numpy(np.ascontiguousarray(w.page_tables, np.int32)).cuda()
     cd = torch.from_numpy(np.ascontiguousarray(w.ctx_lens, np.int32)).cuda()
     args = (qd, kd, vd, ptd, cd, sh.n_heads, sh.n_kv_heads, sh.head_dim, k.shape[0])

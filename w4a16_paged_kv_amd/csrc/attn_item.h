@@ -88,7 +88,8 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   const int p_end = min(npages, p_begin + a.pages_per_split);
 
   // Scores on the matrix cores: S^T = K q^T with v_mfma_f32_16x16x32_f16, A =
-  // the page's K (lane l: token l & 15, columns 32 kk + 8 (l >> 4) .. +8), B =
+  // the page's K (lane l: token l & 15, columns 32 kk + 8 (l >> 4) .. +8; the
+  // K slice stores each step's 64 operands contiguously, k_slice_offset), B =
   // the group's queries (lane l: head l & 15, same columns; heads past GQ are
   // zero), so lane l ends with S[token 4 (l >> 4) + j][head l & 15], j < 4.
   // The queries pass through LDS once into that operand layout.
@@ -133,7 +134,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 2 * (qh * D + 32 * i + kc));
+    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 16 * (64 * i + lane));  // K slice in score operand order
 #pragma unroll
     for (int i = 0; i < NS / 2; ++i) vv[i] = ld128(rv, 16 * (64 * i + lane));
   };

@@ -122,16 +122,27 @@ __host__ __device__ __forceinline__ int v_slice_offset(int t, int d) {
   return ((d >> 5) * 64 + (d & 15) + 16 * (t >> 2)) * 8 + ((d >> 4) & 1) * 4 + (t & 3);
 }
 
+// Element (token t, dim d) of a (page, head) K slice sits in the operand
+// order of the attention's scores (v_mfma_f32_16x16x32_f16, A = the page's
+// K): for the 32-dim step i = d / 32, lane L = t + 16 ((d / 8) % 4) holds
+// dims 32 i + 8 ((d / 8) % 4) .. +8 of token t, so the 64 lanes' operands of
+// one step are 1 KiB of contiguous memory (one coalesced 16-byte load per
+// lane; rows of the natural [16][D] slice read 64 bytes of each of 16 rows
+// per instruction, at a third of the rate from L2): offset (64 i + L) * 8 +
+// d % 8.
+__host__ __device__ __forceinline__ int k_slice_offset(int t, int d) {
+  return ((d >> 5) * 64 + 16 * ((d >> 3) & 3) + t) * 8 + (d & 7);
+}
+
 // One token's K or V values (dims dim0, dim1 of KV head kvh) into its page
-// slot. A (page, head) slice of K is [16 tokens][D]; of V it is in the P V
-// operand order above.
+// slot, in the slice orders above.
 __device__ __forceinline__ void kv_store(const QkvEpilogue& e, uint16_t* pool, bool v_layout, int slot, int kvh,
                                          int dim0, int dim1, float v0, float v1) {
   if (slot < 0) return;  // invalid position or page: counted by the token plan
   uint16_t* sl = pool + ((size_t)(slot >> 4) * e.n_kv_heads + kvh) * kPage * e.head_dim;
   const int t = slot & 15;
-  sl[v_layout ? v_slice_offset(t, dim0) : t * e.head_dim + dim0] = f2h(v0);
-  sl[v_layout ? v_slice_offset(t, dim1) : t * e.head_dim + dim1] = f2h(v1);
+  sl[v_layout ? v_slice_offset(t, dim0) : k_slice_offset(t, dim0)] = f2h(v0);
+  sl[v_layout ? v_slice_offset(t, dim1) : k_slice_offset(t, dim1)] = f2h(v1);
 }
 
 // Rows i and i+8 of tile t hold the rotate-half RoPE pair (dim0, dim0 + D/2)

@@ -411,8 +411,9 @@ hipError_t launch_w4_gemm_prefill(int epi, const GemvArgs& a, hipStream_t s) {
 // sequence in page page_table[t / 16], slot t % 16: "Building a Custom LLM
 // Inference Runtime on H100", The Three Critical Bugs, Bug 1). The products
 // run on the matrix cores as in the decode kernel, with the 16 query columns
-// being the item's 16 rows: S^T = K Q^T (v_mfma_f32_16x16x32_f16, lane l
-// ends with S[token 4 (l >> 4) + j][row l & 15]), base-2 online softmax per
+// being the item's 16 rows: S^T = K Q^T (v_mfma_f32_16x16x32_f16, the K
+// slice in its operand order, lane l ends with S[token 4 (l >> 4) + j][row
+// l & 15]), base-2 online softmax per
 // row in fp32, O^T = V^T P^T (v_mfma_f32_16x16x16_f16, P entering as two
 // fp16 terms). A token past a row's position scores -inf.
 //
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(kPfaWaves * 64) __attribute__((amdgpu_waves_per_eu(
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(a.v_pool + ((size_t)id * a.n_kv_heads + kvh) * slice);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 2 * (qi * D + 32 * i + kc));
+    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 16 * (64 * i + lane));  // K slice in score operand order
 #pragma unroll
     for (int i = 0; i < NS / 2; ++i) vv[i] = ld128(rv, 16 * (64 * i + lane));
   };
@@ -641,8 +642,8 @@ namespace w4 {
 
 // ------------------------------------------------------------ KV page copies
 // Natural-layout K/V rows (token, KV head, D values) to and from the cache's
-// page slices: K slices [16 tokens][D], V slices in the P V operand order of
-// v_slice_offset. One thread per (token, KV head, 8 dims); token i of the
+// page slices: K slices in the score operand order of k_slice_offset, V
+// slices in the P V operand order of v_slice_offset. One thread per (token, KV head, 8 dims); token i of the
 // call sits at position start + i, in page page_table[pos / 16], slot
 // pos % 16. A page id outside [0, num_pages) skips the token (nothing is
 // read or written for it; the host validates ids it can see).
@@ -658,7 +659,8 @@ __global__ __launch_bounds__(256) void kv_pages_kernel(KvCopyArgs a) {
   const size_t slice = ((size_t)page * a.n_kv_heads + kvh) * kPage * a.head_dim;
   const int t = pos & 15;
   const size_t nat = ((size_t)tok * a.n_kv_heads + kvh) * a.head_dim + d0;
-  uint16_t* kp = a.k_pool + slice + (size_t)t * a.head_dim + d0;
+  // the 8 dims d0 .. d0 + 8 of token t are one 16-byte word of the K slice
+  uint16_t* kp = a.k_pool + slice + k_slice_offset(t, d0);
   uint16_t* vp = a.v_pool + slice;
   if (a.to_pages) {
     *reinterpret_cast<u4_t*>(kp) = *reinterpret_cast<const u4_t*>(a.k + nat);

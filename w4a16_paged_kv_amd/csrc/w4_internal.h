@@ -61,7 +61,7 @@ enum Epi : int {
 struct QkvEpilogue {
   uint16_t* q_out;            // [B][q_stride] fp16, q heads in logical order
   int32_t q_stride;
-  uint16_t* k_pool;           // [P][Hkv][16][D]
+  uint16_t* k_pool;           // [P][Hkv][16 * D], slices in score operand order (k_slice_offset)
   uint16_t* v_pool;           // [P][Hkv][16 * D], slices in P V operand order (v_slice_offset)
   const uint16_t* bias;       // fp16 [(Hq+2Hkv)D] logical order, or nullptr
   const int32_t* slot;        // token plan: [B] page * 16 + position % 16, or -1 (no K/V store)
@@ -132,7 +132,7 @@ struct F16GemvArgs {
 struct AttnArgs {
   const uint16_t* q;          // [B][q_stride], heads of D values
   int32_t q_stride;
-  const uint16_t* k_pool;     // [P][Hkv][16][D]
+  const uint16_t* k_pool;     // [P][Hkv][16 * D], slices in score operand order (k_slice_offset)
   const uint16_t* v_pool;     // [P][Hkv][16 * D], slices in P V operand order (v_slice_offset)
   const int32_t* page_tables; // [B][max_pages]
   const int32_t* ctx_lens;    // [B]
@@ -152,7 +152,7 @@ struct AttnArgs {
 struct PrefillAttnArgs {
   const uint16_t* q;          // [n][q_stride], heads of D values (after RoPE)
   int32_t q_stride;
-  const uint16_t* k_pool;     // [P][Hkv][16][D]
+  const uint16_t* k_pool;     // [P][Hkv][16 * D], slices in score operand order (k_slice_offset)
   const uint16_t* v_pool;     // [P][Hkv][16 * D], slices in P V operand order
   const int32_t* page_table;  // [max_pages] of the sequence
   int32_t max_pages, num_pages;
@@ -178,7 +178,7 @@ hipError_t launch_w4ax_gemv(const W4AxArgs& a, bool int8, hipStream_t s);
 
 // Copies between natural-layout K/V rows [n][Hkv][D] and one layer's pages.
 struct KvCopyArgs {
-  uint16_t* k_pool;           // [P][Hkv][16][D]
+  uint16_t* k_pool;           // [P][Hkv][16 * D], slices in score operand order (k_slice_offset)
   uint16_t* v_pool;           // [P][Hkv][16 * D], P V operand order
   const int32_t* page_table;  // device [>= ceil((start + n) / 16)]
   int32_t num_pages, n_kv_heads, head_dim;

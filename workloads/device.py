@@ -47,6 +47,27 @@ def upload_layer(w: Workload, l: int, bias: bool = False, device="cuda") -> Dict
     return d
 
 
+def k_pages_device(k: np.ndarray) -> np.ndarray:
+    """K pages [..][16 tokens][D] in the device's slice order, same shape:
+    value (t, d) at flat ((d // 32) * 64 + 16 ((d // 8) % 4) + t) * 8 + d % 8
+    of its slice (the operand order of the attention's scores)."""
+    *lead, T, D = k.shape
+    n = len(lead)
+    s = k.reshape(*lead, T, D // 32, 4, 8)             # t, d = 32P + 8c + e
+    s = s.transpose(*range(n), n + 1, n + 2, n, n + 3)  # [P][c][t][e]
+    return np.ascontiguousarray(s).reshape(*lead, T, D)
+
+
+def k_pages_host(kd):
+    """Inverse of k_pages_device (numpy arrays or torch tensors)."""
+    *lead, T, D = kd.shape
+    n = len(lead)
+    s = kd.reshape(*lead, D // 32, 4, T, 8)             # [P][c][t][e]
+    order = (*range(n), n + 2, n, n + 1, n + 3)         # -> [t][P][c][e]
+    s = s.permute(*order) if hasattr(s, "permute") else s.transpose(*order)
+    return s.reshape(*lead, T, D)
+
+
 def v_pages_device(v: np.ndarray) -> np.ndarray:
     """V pages [..][16 tokens][D] in the device's slice order, same shape:
     value (t, d) at flat ((d // 32) * 64 + d % 16 + 16 (t // 4)) * 8 +
@@ -71,9 +92,9 @@ def v_pages_host(vd):
 
 def upload_kv(w: Workload, kv_cache: torch.Tensor, l: int, kv=None) -> None:
     """Copy layer l's generated K and V pages into the [L][2][P][Hkv][16 x D] cache
-    (K slices [16][D], V slices in the device order of v_pages_device)."""
+    (K and V slices in the device orders of k_pages_device and v_pages_device)."""
     k, v = kv if kv is not None else w.kv(l)
-    kv_cache[l, 0].copy_(to_dev(k, kv_cache.device))
+    kv_cache[l, 0].copy_(to_dev(k_pages_device(k), kv_cache.device).view(kv_cache[l, 0].shape))
     kv_cache[l, 1].copy_(to_dev(v_pages_device(v), kv_cache.device).view(kv_cache[l, 1].shape))
 
 
