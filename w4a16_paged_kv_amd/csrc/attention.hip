@@ -16,9 +16,9 @@ namespace w4 {
 // dispatcher sends every sequence's first splits before any later ones and
 // the items past a short sequence's last split (which exit at once) come at
 // the end (32 sequences, contexts 128-8192: 78 -> 75 us).
-template <int D, int GQ>
+template <int D, int GQ, bool EARLY>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void paged_attn_kernel(AttnArgs a) {
-  attn_item<D, GQ, kAttnWaves * 64>(a, blockIdx.z, blockIdx.y, blockIdx.x);
+  attn_item<D, GQ, kAttnWaves * 64, EARLY>(a, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 bool attention_supported(int head_dim, int group) {
@@ -47,8 +47,13 @@ int attention_pages_per_split(int batch, int n_kv_heads, int max_pages) {
 
 template <int D, int GQ>
 static hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((paged_attn_kernel<D, GQ>), dim3(a.batch, a.n_kv_heads, a.max_splits),
-                     dim3(kAttnWaves * 64), 0, s, a);
+  const dim3 grid(a.batch, a.n_kv_heads, a.max_splits), block(kAttnWaves * 64);
+  // several pages per wavefront: the first page's loads go out before the
+  // queries are staged
+  if (a.pages_per_split > kAttnWaves)
+    hipLaunchKernelGGL((paged_attn_kernel<D, GQ, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((paged_attn_kernel<D, GQ, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

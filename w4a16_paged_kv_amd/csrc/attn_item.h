@@ -40,7 +40,10 @@ constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time e
 // coherently.
 // PF: keep the next page's K/V in flight while the current page is processed
 // (two K/V register sets; without it the kernel fits a 1024-thread launch).
-template <int D, int GQ, int NT, bool PF = true>
+// EARLY: issue the wavefront's first page before the queries are staged
+// (items of several pages per wavefront: their first pages then overlap the
+// query staging; with one page per wavefront the queries are better first).
+template <int D, int GQ, int NT, bool EARLY, bool PF = true>
 __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(GQ >= 1 && GQ <= 8, "group");
@@ -77,6 +80,34 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   ctx = ctx < 0 ? 0 : (ctx > a.max_pages * kPage ? a.max_pages * kPage : ctx);
   const int npages = (ctx + kPage - 1) / kPage;
   const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
+  const int p_begin = split * a.pages_per_split;
+  const int p_end = min(npages, p_begin + a.pages_per_split);
+  const int p_stop = pager ? p_end : pw0;  // non-page wavefronts skip the loop
+  const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
+  constexpr int NK = D / 32;               // MFMA k-steps per page
+  const int lane_ = threadIdx.x & 63;
+  // page p's id, validated (an invalid id is counted and read as page 0,
+  // with no valid tokens)
+  auto checked = [&](int p, int id, int& valid) {
+    const bool bad = id < 0 || id >= a.num_pages;
+    if (bad && lane_ == 0) atomicAdd(a.err, 1u);
+    valid = bad ? 0 : min(kPage, ctx - p * kPage);
+    return bad ? 0 : id;
+  };
+  u4_t kf[NK], kn[PF ? NK : 1];
+  u4_t vf[NS / 2], vn[PF ? NS / 2 : 1];  // V operands of slice pairs (2i, 2i + 1)
+  auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
+    page = __builtin_amdgcn_readfirstlane(page);  // one page per wavefront: keeps the resources scalar
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 16 * (64 * i + lane_));  // K slice in score operand order
+#pragma unroll
+    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128(rv, 16 * (64 * i + lane_));
+  };
+  int valid_cur = 0, valid_nxt = 0;
+  // (a split past the context has pw0 >= p_stop: no load, no id check)
+  if (EARLY && pw0 < p_stop) load_kv(checked(pw0, pid_cur, valid_cur), kf, vf);
   uint16_t* out = a.out + (size_t)b * a.out_stride + (size_t)kvh * GQ * D;
   if (npages == 0) {  // empty context: zeros
     if (split == 0)
@@ -84,8 +115,6 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     return;
   }
   if (split >= nsplit) return;
-  const int p_begin = split * a.pages_per_split;
-  const int p_end = min(npages, p_begin + a.pages_per_split);
 
   // Scores on the matrix cores: S^T = K q^T with v_mfma_f32_16x16x32_f16, A =
   // the page's K (lane l: token l & 15, columns 32 kk + 8 (l >> 4) .. +8; the
@@ -99,7 +128,6 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
     if (i < GQ * D) *reinterpret_cast<u4_t*>(&s_q[i]) = qv[r];
   }
   __syncthreads();
-  constexpr int NK = D / 32;               // MFMA k-steps per page
   const int qh = lane & 15, kc = 8 * (lane >> 4);
   const int qrow = min(qh, GQ - 1);        // heads past GQ read a real row and are zeroed
 
@@ -117,30 +145,7 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
 #pragma unroll
   for (int sl = 0; sl < NS; ++sl) acc[sl] = (f4_t){0.f, 0.f, 0.f, 0.f};
   const int tk = 4 * (lane >> 4);          // this lane's tokens in the P V operands
-  const size_t slice = (size_t)kPage * D;  // elements per (page, kv head)
-
-  // page p's id, validated (an invalid id is counted and read as page 0,
-  // with no valid tokens)
-  auto checked = [&](int p, int id, int& valid) {
-    const bool bad = id < 0 || id >= a.num_pages;
-    if (bad && lane == 0) atomicAdd(a.err, 1u);
-    valid = bad ? 0 : min(kPage, ctx - p * kPage);
-    return bad ? 0 : id;
-  };
-  u4_t kf[NK], kn[PF ? NK : 1];
-  u4_t vf[NS / 2], vn[PF ? NS / 2 : 1];  // V operands of slice pairs (2i, 2i + 1)
-  auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
-    page = __builtin_amdgcn_readfirstlane(page);  // one page per wavefront: keeps the resources scalar
-    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
-    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
-#pragma unroll
-    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 16 * (64 * i + lane));  // K slice in score operand order
-#pragma unroll
-    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128(rv, 16 * (64 * i + lane));
-  };
-  int valid_cur = 0, valid_nxt = 0;
-  const int p_stop = pager ? p_end : pw0;  // non-page wavefronts skip the loop
-  if (pw0 < p_stop) load_kv(checked(pw0, pid_cur, valid_cur), kf, vf);
+  if (!EARLY && pw0 < p_stop) load_kv(checked(pw0, pid_cur, valid_cur), kf, vf);
   for (int p = pw0; p < p_stop; p += W) {
     const int valid = valid_cur;
     if (PF && p + W < p_stop) {
