@@ -27,19 +27,20 @@ bool attention_supported(int head_dim, int group) {
 }
 
 // Pages per split: one page per wavefront until the launch would exceed
-// about 256 workgroups, then up to eight (several pages per wavefront overlap
+// about 256 workgroups, then up to 32 (several pages per wavefront overlap
 // one page's K/V latency with the previous page's work, and longer items
 // spend less of their time in the combine and merge tail; measured at 16
 // sequences of 1024-4096 tokens: 2048 workgroups 45.6 us, 512 28.2 us, and
 // with page ids read by scalar loads 512 workgroups 24.5 us, 256 (eight pages
 // per wavefront) 2.407 against 2.463 ms per step; at 32 sequences of
-// 128-8192 tokens: four pages per wavefront 75 us, eight 69 us, sixteen
-// 70.5 us); at most 128 splits per sequence (the merge keeps two floats per
-// (head, split) in LDS).
+// 128-8192 tokens, with K slices in score operand order and the first page
+// issued early: eight pages per wavefront 54.5 us, sixteen 53.1 us,
+// thirty-two 51.0 us); at most 128 splits per sequence (the merge keeps two
+// floats per (head, split) in LDS).
 int attention_pages_per_split(int batch, int n_kv_heads, int max_pages) {
   const long units = (long)batch * n_kv_heads * max_pages;
   int per_wave = 1;
-  while (per_wave < 8 && units / ((long)kAttnWaves * per_wave) > 256) per_wave *= 2;
+  while (per_wave < 32 && units / ((long)kAttnWaves * per_wave) > 256) per_wave *= 2;
   int pps = kAttnWaves * per_wave;
   while ((max_pages + pps - 1) / pps > 128) pps *= 2;
   return pps;
