@@ -67,7 +67,9 @@ def test_w4_gemv_one_hot_is_exact():
     assert np.array_equal(to_np16(y)[0], q[:, 131].astype(np.float16))
 
 
-@pytest.mark.parametrize("n,k,batch", [(16384, 3584, 1), (4000, 3584, 16), (1000, 448, 5), (152064, 3584, 1)])
+@pytest.mark.parametrize("n,k,batch", [(16384, 3584, 1), (4000, 3584, 16), (1000, 448, 5), (152064, 3584, 1),
+                                       (152064, 3584, 16), (37, 24, 2), (700, 200, 15), (2000, 4064, 16),
+                                       (1500, 4096, 9)])
 def test_f16_gemv_matches_oracle(n, k, batch):
     print(f"w4_gemv_f16 n={n} k={k} batch={batch}", flush=True)
     g = wl.rng(79, 0, 0)
@@ -80,3 +82,30 @@ def test_f16_gemv_matches_oracle(n, k, batch):
     rows = np.arange(n) if n <= 16384 else np.random.default_rng(0).choice(n, 4096, replace=False)
     ref = od.r16(wgt[rows].astype(np.float64) @ x.astype(np.float64).T).T
     assert_close(got[:, rows], ref, "f16 gemv")
+
+
+@pytest.mark.parametrize("n,k,batch", [(9, 1000, 16), (300, 1000, 3), (4099, 3584, 16), (40, 24, 7)])
+def test_f16_gemm_batched_stays_in_its_outputs_and_repeats(n, k, batch):
+    """Batch 2..16 lm_head: every output of the ragged last tile and of
+    wavefronts whose second tile lies past the end (their re-read blocks are
+    not stored) is written, nothing past the batch x n outputs changes, and a
+    second call gives the same bits (one 16 x 16 tile at n = 9; a partial last
+    32-column chunk at k = 1000; one chunk at k = 24)."""
+    print(f"w4_gemv_f16 guard n={n} k={k} batch={batch}", flush=True)
+    g = wl.rng(80, n, k)
+    wgt = wl.f16_normal(g, (n, k), 0.02)
+    x = wl.f16_normal(g, (batch, k))
+    guard = 4096
+    ybuf = torch.full((batch * n + guard,), float("nan"), dtype=torch.float16, device="cuda")
+    y = ybuf[:batch * n].view(batch, n)
+    wd, xd = to_dev(w4.pack_weights_f16(wgt)), to_dev(x)
+    w4.w4_gemv_f16(wd, xd, y, n, k, batch)
+    torch.cuda.synchronize()
+    got = to_np16(y)
+    assert not np.isnan(got).any(), "an output was not written"
+    assert torch.isnan(ybuf[batch * n:]).all(), "a value past the outputs changed"
+    ref = od.r16(wgt.astype(np.float64) @ x.astype(np.float64).T).T
+    assert_close(got, ref, "f16 gemm batched")
+    w4.w4_gemv_f16(wd, xd, y, n, k, batch)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np16(y).view(np.uint16), got.view(np.uint16)), "second call differs"
