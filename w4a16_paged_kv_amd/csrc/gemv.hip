@@ -457,8 +457,10 @@ __global__ __launch_bounds__(WAVES * 64) void f16_gemv_b1_kernel(F16GemvArgs a, 
 // activation operand (16 rows x 32 columns, from L2) serves TT weight blocks
 // (batch-16 7B lm_head: one tile per wavefront 200 us, two 186 us, four
 // 193 us). Weight blocks past the last tile re-read it; their rows are not
-// stored.
-template <int WAVES>
+// stored. OP: the activations come in the A-operand order (a.xop, written
+// by the RMSNorm kernel: chunk c's 64 lanes as 1 KiB of contiguous memory)
+// instead of as rows (16 rows x 64 bytes per load): 184-185 -> 178-179 us.
+template <int WAVES, bool OP>
 __global__ __launch_bounds__(WAVES * 64) void f16_gemm_mfma_kernel(F16GemvArgs a) {
   constexpr int TT = 2, U = 8;
   const int C = a.cblocks;
@@ -476,7 +478,10 @@ __global__ __launch_bounds__(WAVES * 64) void f16_gemm_mfma_kernel(F16GemvArgs a
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = base + u;
-      xv[u] = (c < C && 32 * c + 8 * (lane >> 4) < a.k) ? *reinterpret_cast<const u4_t*>(xr + 32 * c)
+      if (OP)
+        xv[u] = c < C ? *reinterpret_cast<const u4_t*>(a.xop + ((size_t)c * 64 + lane) * 8) : (u4_t){0u, 0u, 0u, 0u};
+      else
+        xv[u] = (c < C && 32 * c + 8 * (lane >> 4) < a.k) ? *reinterpret_cast<const u4_t*>(xr + 32 * c)
                                                            : (u4_t){0u, 0u, 0u, 0u};
 #pragma unroll
       for (int q = 0; q < TT; ++q) {
@@ -506,14 +511,16 @@ __global__ __launch_bounds__(WAVES * 64) void f16_gemm_mfma_kernel(F16GemvArgs a
 
 // y[b] = fp16(x[b] * rsqrt(mean(x[b]^2) + eps) * gamma), zero padded to the
 // next multiple of 128 columns (batched path: the MFMA kernels read it).
+// With yop (rows b < 16, vectorised path only), the same values also go to
+// yop in the A-operand order of v_mfma_f32_16x16x32_f16: 8-column word w of
+// row b at lane b + 16 (w % 4) of 32-column chunk w / 4, 16 bytes per lane.
 // Rows up to kRmsWords 16-byte words per thread are read once into registers
 // (16-byte loads and stores); others take the element loop. Either way
 // y = (x * rs) * gamma in fp32, rounded once, zeros up to the 128-column pad.
-constexpr int kRmsWords = 4;  // 256 threads x 4 words x 8 = 8192 columns
 template <bool VEC>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* x, int x_stride,
                                                            const uint16_t* gamma, float eps, int k,
-                                                           uint16_t* y, int y_stride) {
+                                                           uint16_t* y, int y_stride, uint16_t* yop) {
   __shared__ float red[4];
   const int b = blockIdx.x;
   const uint16_t* xr = x + (size_t)b * x_stride;
@@ -556,6 +563,10 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* x, in
         o = __builtin_bit_cast(u4_t, r);
       }
       *reinterpret_cast<u4_t*>(yr + c) = o;
+      if (yop) {
+        const int w = c / 8;
+        *reinterpret_cast<u4_t*>(yop + ((size_t)(w >> 2) * 64 + b + 16 * (w & 3)) * 8) = o;
+      }
     }
   } else {
     for (int i = threadIdx.x; i < kpad; i += 256)
@@ -754,22 +765,28 @@ hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s) {
                        tpw);
   } else {
     constexpr int WAVES = 4;
-    hipLaunchKernelGGL((f16_gemm_mfma_kernel<WAVES>), dim3(ceil_div(a.tiles, WAVES * 2)), dim3(WAVES * 64), 0, s, a);
+    if (a.xop)
+      hipLaunchKernelGGL((f16_gemm_mfma_kernel<WAVES, true>), dim3(ceil_div(a.tiles, WAVES * 2)), dim3(WAVES * 64), 0,
+                         s, a);
+    else
+      hipLaunchKernelGGL((f16_gemm_mfma_kernel<WAVES, false>), dim3(ceil_div(a.tiles, WAVES * 2)), dim3(WAVES * 64), 0,
+                         s, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16_t* gamma, float eps,
                                int32_t k, uint16_t* y, int32_t y_stride, int32_t batch,
-                               hipStream_t s) {
-  const bool vec = k % 8 == 0 && x_stride % 8 == 0 && y_stride % 8 == 0 && k <= 256 * 8 * kRmsWords &&
-                   ((uintptr_t)x | (uintptr_t)y | (uintptr_t)gamma) % 16 == 0;
+                               hipStream_t s, uint16_t* yop) {
+  const bool vec = rmsnorm_rows_vectorised(k, x_stride, y_stride) &&
+                   ((uintptr_t)x | (uintptr_t)y | (uintptr_t)gamma | (uintptr_t)yop) % 16 == 0;
+  if (yop && (!vec || batch > 16)) return hipErrorInvalidValue;
   if (vec)
     hipLaunchKernelGGL(rmsnorm_rows_kernel<true>, dim3(batch), dim3(256), 0, s, x, x_stride, gamma, eps, k, y,
-                       y_stride);
+                       y_stride, yop);
   else
     hipLaunchKernelGGL(rmsnorm_rows_kernel<false>, dim3(batch), dim3(256), 0, s, x, x_stride, gamma, eps, k, y,
-                       y_stride);
+                       y_stride, yop);
   return hipGetLastError();
 }
 

@@ -30,13 +30,6 @@ typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float h2f(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
 __device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
 
-// Nibbles at bits 4i and 16+4i of a packed word -> the exact fp16 pair
-// (q_{2i}, q_{2i+1}). 0x6400 is 1024.0; its ulp is 1, so 0x6400|u == 1024+u.
-__device__ __forceinline__ h2_t nib_pair(uint32_t word, int i) {
-  const uint32_t v = ((word >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
-  return __builtin_bit_cast(h2_t, v) - (h2_t){(_Float16)1032.0f, (_Float16)1032.0f};
-}
-
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 
 __device__ __forceinline__ int f_bits(float v) { return __builtin_bit_cast(int, v); }

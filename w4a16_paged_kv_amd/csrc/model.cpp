@@ -22,8 +22,8 @@
 namespace w4 {
 
 struct WsLayout {
-  size_t err, counters, tokens, positions, ctx, pt, slot, rope, x, xn, q, o, h, partials, kpart, kcount, amax,
-      total;
+  size_t err, counters, tokens, positions, ctx, pt, slot, rope, x, xn, xop, q, o, h, partials, kpart, kcount,
+      amax, total;
   int xn_stride, o_stride, h_stride, max_splits;
 };
 
@@ -50,6 +50,9 @@ static WsLayout ws_layout(const w4_config& c, int max_batch, int max_pages) {
   L.rope = take((size_t)max_batch * (c.head_dim / 2) * 2 * 4);
   L.x = take((size_t)max_batch * c.hidden * 2);
   L.xn = take((size_t)max_batch * L.xn_stride * 2);
+  // batch > 1: the final RMSNorm's rows again in the lm_head's A-operand
+  // order (16 rows x 32 columns per KiB)
+  L.xop = max_batch > 1 ? take((size_t)L.xn_stride * 32) : 0;
   L.q = take((size_t)max_batch * c.n_heads * c.head_dim * 2);
   L.o = take((size_t)max_batch * L.o_stride * 2);
   L.h = take((size_t)max_batch * L.h_stride * 2);
@@ -300,10 +303,12 @@ static int enqueue_lm_head(w4_model* m, const uint16_t* x, int batch, uint16_t* 
     f.xn_out = m->at<uint16_t>(m->L.xn);
   } else {
     uint16_t* xn = m->at<uint16_t>(m->L.xn);
+    uint16_t* xop = rmsnorm_rows_vectorised(c.hidden, c.hidden, m->L.xn_stride) ? m->at<uint16_t>(m->L.xop) : nullptr;
     W4_LAUNCH(launch_rmsnorm_rows(x, c.hidden, m->weights.final_norm, c.rms_eps, c.hidden, xn,
-                                  m->L.xn_stride, batch, s));
+                                  m->L.xn_stride, batch, s, xop));
     f.x = xn;
     f.x_stride = m->L.xn_stride;
+    f.xop = xop;
   }
   W4_LAUNCH(launch_f16_gemv(f, s));
   return W4_OK;

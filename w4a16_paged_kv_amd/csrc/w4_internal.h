@@ -45,7 +45,6 @@ constexpr int kTileRows = 16;   // rows per packed tile
 // ----------------------------------------------------------- packed sizes
 __host__ __device__ inline int w4_tiles(int n) { return ceil_div(n, kTileRows); }
 __host__ __device__ inline int w4_groups(int k) { return ceil_div(k, kGroup); }
-inline size_t w4_nibble_bytes(int n, int k) { return (size_t)w4_tiles(n) * w4_groups(k) * 1024; }
 
 // --------------------------------------------------------- kernel arguments
 enum Epi : int {
@@ -127,6 +126,7 @@ struct F16GemvArgs {
   uint16_t* xn_out;       // with gamma: workgroup 0 also stores the normalised rows here, or nullptr
   int32_t xn_stride;      // row stride of xn_out (batch > 1)
   int32_t batch;
+  const uint16_t* xop;    // batch 2..16: x in the A-operand order (launch_rmsnorm_rows' yop), or nullptr
 };
 
 struct AttnArgs {
@@ -215,7 +215,13 @@ hipError_t launch_w4_gemv(int epi, const GemvArgs& a, hipStream_t s);
 hipError_t launch_f16_gemv(const F16GemvArgs& a, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const uint16_t* x, int32_t x_stride, const uint16_t* gamma,
                                float eps, int32_t k, uint16_t* y, int32_t y_stride,
-                               int32_t batch, hipStream_t s);
+                               int32_t batch, hipStream_t s, uint16_t* yop = nullptr);
+// Whether launch_rmsnorm_rows takes its vectorised path (16-byte accesses,
+// the only one that can also write yop), given 16-byte aligned pointers.
+constexpr int kRmsWords = 4;  // 16-byte words per thread: 256 x 4 x 8 = 8192 columns
+inline bool rmsnorm_rows_vectorised(int k, int x_stride, int y_stride) {
+  return k % 8 == 0 && x_stride % 8 == 0 && y_stride % 8 == 0 && k <= 256 * 8 * kRmsWords;
+}
 hipError_t launch_embed_plan(const TokenPlanArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int head_dim, int group, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t count, uint32_t value, hipStream_t s);
