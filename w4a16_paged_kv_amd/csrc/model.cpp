@@ -105,6 +105,11 @@ struct w4_model {
   // key: batch, logits, device-input pointers (null for host inputs)
   typedef std::tuple<int, const void*, const void*, const void*, const void*, const void*> Key;
   std::map<Key, hipGraphExec_t> graphs;
+  // greedy generation: two pinned host images of the staged positions /
+  // context lengths / page tables region and one of the chosen tokens
+  // (allocated on the first w4_generate_greedy call)
+  uint8_t* gen_stage = nullptr;
+  int32_t* gen_tokens = nullptr;
 
   template <class T>
   T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
@@ -521,6 +526,8 @@ W4_EXPORT void w4_model_destroy(w4_model* m) {
   if (!handle_release(m)) return;  // null, already destroyed or never created
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  if (m->gen_stage) (void)hipHostFree(m->gen_stage);
+  if (m->gen_tokens) (void)hipHostFree(m->gen_tokens);
   delete m;
 }
 
@@ -855,47 +862,79 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_steps == 0) return W4_OK;
+  // The staged positions, context lengths and page tables are consecutive
+  // workspace regions: each step's go to the device as one copy from a pinned
+  // host image, and the chosen tokens come back into pinned memory (one copy
+  // each way per step, asynchronous; pageable copies were five per step).
+  const WsLayout& L = m->L;
+  const size_t stage_bytes = round_up(L.pt - L.positions + (size_t)m->max_batch * m->max_pages * 4, 256);
+  if (!m->gen_stage && hipHostMalloc(reinterpret_cast<void**>(&m->gen_stage), 2 * stage_bytes, 0) != hipSuccess) {
+    m->gen_stage = nullptr;
+    return fail(W4_EHIP, "w4_generate_greedy: pinned staging buffer of %zu bytes", stage_bytes);
+  }
+  if (!m->gen_tokens &&
+      hipHostMalloc(reinterpret_cast<void**>(&m->gen_tokens), (size_t)m->max_batch * 4, 0) != hipSuccess) {
+    m->gen_tokens = nullptr;
+    return fail(W4_EHIP, "w4_generate_greedy: pinned token buffer");
+  }
+  const size_t copy_bytes = L.pt - L.positions + (size_t)batch * m->max_pages * 4;
   std::vector<int32_t> pos(first_positions, first_positions + batch);
-  std::vector<int32_t> ctx(batch), pt((size_t)batch * m->max_pages);
-  // validates and stages the positions of the next step (tokens: host array
-  // for the first step, else already in the staged slot)
-  auto stage_step = [&](const int32_t* tokens) -> int {
+  // validates and stages step `step`'s positions into pinned image step % 2,
+  // then copies it (the tokens are already in the staged slot: the first
+  // step's from the host, later ones from the device argmax). Image i is
+  // rewritten for step s + 2 only after the host has waited for step s, whose
+  // wait covers the copy of image i made before step s ran.
+  auto stage_step = [&](const int32_t* tokens, int step) -> int {
+    uint8_t* img = m->gen_stage + (size_t)(step & 1) * stage_bytes;
+    int32_t* h_pos = reinterpret_cast<int32_t*>(img);
+    int32_t* h_ctx = reinterpret_cast<int32_t*>(img + (L.ctx - L.positions));
+    int32_t* h_pt = reinterpret_cast<int32_t*>(img + (L.pt - L.positions));
     for (int b = 0; b < batch; ++b) {
-      ctx[b] = pos[b] + 1;
-      int r = kv_seq_reserve(pool, seqs[b], ctx[b]);
+      h_pos[b] = pos[b];
+      h_ctx[b] = pos[b] + 1;
+      int r = kv_seq_reserve(pool, seqs[b], h_ctx[b]);
       if (r) return r;
     }
-    int r = page_table(pool, seqs, batch, m->max_pages, pt.data());
+    int r = page_table(pool, seqs, batch, m->max_pages, h_pt);
     if (r) return r;
-    r = validate_inputs(m, tokens, pos.data(), pt.data(), ctx.data(), batch);
+    r = validate_inputs(m, tokens, h_pos, h_pt, h_ctx, batch);
     if (r) return r;
-    return stage_inputs(m, tokens, pos.data(), pt.data(), ctx.data(), batch, s);
+    if (tokens) W4_HIP(hipMemcpyAsync(m->ws + L.tokens, tokens, batch * 4, hipMemcpyHostToDevice, s));
+    W4_HIP(hipMemcpyAsync(m->ws + L.positions, img, copy_bytes, hipMemcpyHostToDevice, s));
+    return W4_OK;
   };
-  rc = stage_step(first_tokens);
+  int32_t* tok_dev = m->at<int32_t>(L.tokens);
+  // next_tokens gets the last chosen tokens once, on every return after a step
+  auto finish = [&](int ret) -> int {
+    if (hipMemcpyAsync(next_tokens, tok_dev, batch * sizeof(int32_t), hipMemcpyDeviceToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return ret ? ret : fail(W4_EHIP, "w4_generate_greedy: copy of the last tokens");
+    return ret;
+  };
+  rc = stage_step(first_tokens, 0);
   if (rc) return rc;
-  int32_t* tok_dev = m->at<int32_t>(m->L.tokens);
   for (int step = 0; step < n_steps; ++step) {
     rc = run_step(m, staged(m), batch, logits, s, nullptr);
     if (rc) return rc;
-    W4_HIP(launch_argmax_f16(logits, batch, m->cfg.vocab, m->ws + m->L.amax, tok_dev, s));
-    // the next step's inputs are staged first: the copy of the chosen tokens
-    // into pageable host memory may block until the step has finished
+    W4_HIP(launch_argmax_f16(logits, batch, m->cfg.vocab, m->ws + L.amax, tok_dev, s));
+    W4_HIP(hipMemcpyAsync(m->gen_tokens, tok_dev, batch * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    // the next step's inputs are staged while this step runs (the host work
+    // and the copy, which the stream orders after this step's reads)
     int stage_rc = W4_OK;
     if (step + 1 < n_steps) {
       for (int b = 0; b < batch; ++b) ++pos[b];
-      stage_rc = stage_step(nullptr);
+      stage_rc = stage_step(nullptr, step + 1);
     }
-    int32_t* row = out_tokens + (size_t)step * batch;
-    W4_HIP(hipMemcpyAsync(next_tokens, tok_dev, batch * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
-    W4_HIP(hipMemcpyAsync(row, tok_dev, batch * sizeof(int32_t), hipMemcpyDeviceToHost, s));
     W4_HIP(hipStreamSynchronize(s));
+    int32_t* row = out_tokens + (size_t)step * batch;
+    std::memcpy(row, m->gen_tokens, batch * sizeof(int32_t));
     for (int b = 0; b < batch; ++b)
       if (row[b] < 0)
-        return fail(W4_ERANGE, "w4_generate_greedy: step %d, sequence %d: every logit is NaN", step, b);
+        return finish(fail(W4_ERANGE, "w4_generate_greedy: step %d, sequence %d: every logit is NaN", step, b));
     if (steps_done) *steps_done = step + 1;
-    if (stage_rc) return stage_rc;
+    if (stage_rc) return finish(stage_rc);
   }
-  return W4_OK;
+  return finish(W4_OK);
 }
 
 // ------------------------------------------------------------------ prefill
