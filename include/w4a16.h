@@ -247,7 +247,11 @@ int  w4_set_graph(w4_model* model, int enabled);
  * attention reads tokens [0, ctx_lens[b]). logits: device fp16 [batch][V].
  * The host arrays are validated (W4_ERANGE) and copied into the workspace on
  * `stream` before any kernel runs, never inside a captured graph [H100-bug,
- * Bug 3]. */
+ * Bug 3]: on return they have been read (the caller may reuse them); their
+ * values reach the device as one copy from one of two pinned host images of
+ * the model, the call first waiting for the copy made from that image two
+ * calls earlier (so the host runs at most two calls ahead of those copies),
+ * or, while `stream` is being captured, as four pageable copies. */
 int  decode_step(w4_model* model, const int32_t* tokens, const int32_t* positions,
                  const int32_t* page_tables, const int32_t* ctx_lens, int32_t batch,
                  uint16_t* logits, void* stream);

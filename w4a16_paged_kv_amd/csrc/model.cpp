@@ -105,11 +105,15 @@ struct w4_model {
   // key: batch, logits, device-input pointers (null for host inputs)
   typedef std::tuple<int, const void*, const void*, const void*, const void*, const void*> Key;
   std::map<Key, hipGraphExec_t> graphs;
-  // greedy generation: two pinned host images of the staged positions /
-  // context lengths / page tables region and one of the chosen tokens
-  // (allocated on the first w4_generate_greedy call)
-  uint8_t* gen_stage = nullptr;
-  int32_t* gen_tokens = nullptr;
+  // Host inputs reach the staged tokens / positions / ctx / page-table slots
+  // (consecutive workspace regions) as one copy from a pinned host image of
+  // that region. Two images are used in turn; the event recorded after an
+  // image's copy is waited on before the image is rewritten.
+  uint8_t* stage_img = nullptr;  // 2 x stage_bytes, pinned
+  size_t stage_bytes = 0;
+  hipEvent_t stage_ev[2] = {nullptr, nullptr};
+  int stage_next = 0;
+  int32_t* gen_tokens = nullptr;  // pinned [max_batch]: the greedy loop's chosen tokens
 
   template <class T>
   T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
@@ -120,6 +124,15 @@ struct w4_model {
     return kv + (size_t)(2 * l + 1) * num_pages * cfg.n_kv_heads * kPage * cfg.head_dim;
   }
 };
+
+// The model's own stream, events and pinned buffers (any may be null).
+static void release_model_resources(w4_model* m) {
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  for (hipEvent_t ev : m->stage_ev)
+    if (ev) (void)hipEventDestroy(ev);
+  if (m->stage_img) (void)hipHostFree(m->stage_img);
+  if (m->gen_tokens) (void)hipHostFree(m->gen_tokens);
+}
 
 namespace w4 {
 
@@ -394,16 +407,62 @@ static int validate_inputs(const w4_model* m, const int32_t* tokens, const int32
                        ctx_lens, batch);
 }
 
+// The pinned image of the staged-input region that the next copy uses,
+// viewed as its four slots; waits until the image's previous copy has run,
+// so the caller may overwrite it.
+struct StageImage {
+  int idx;
+  uint8_t* base;
+  int32_t *tokens, *positions, *ctx, *pt;
+};
+static int stage_image(w4_model* m, StageImage& im) {
+  const WsLayout& L = m->L;
+  im.idx = m->stage_next;
+  W4_HIP(hipEventSynchronize(m->stage_ev[im.idx]));
+  im.base = m->stage_img + (size_t)im.idx * m->stage_bytes;
+  im.tokens = reinterpret_cast<int32_t*>(im.base);
+  im.positions = reinterpret_cast<int32_t*>(im.base + (L.positions - L.tokens));
+  im.ctx = reinterpret_cast<int32_t*>(im.base + (L.ctx - L.tokens));
+  im.pt = reinterpret_cast<int32_t*>(im.base + (L.pt - L.tokens));
+  return W4_OK;
+}
+// One copy of the image to the staged slots (from the tokens slot, or from
+// the positions slot when the tokens are not staged), then the image's event.
+static int stage_commit(w4_model* m, const StageImage& im, bool with_tokens, int batch, hipStream_t s) {
+  const WsLayout& L = m->L;
+  const size_t from = with_tokens ? 0 : L.positions - L.tokens;
+  const size_t bytes = L.pt - L.tokens + (size_t)batch * m->max_pages * 4 - from;
+  W4_HIP(hipMemcpyAsync(m->ws + L.tokens + from, im.base + from, bytes, hipMemcpyHostToDevice, s));
+  W4_HIP(hipEventRecord(m->stage_ev[im.idx], s));
+  m->stage_next = im.idx ^ 1;
+  return W4_OK;
+}
+
+// Host arrays to the staged slots: one pinned copy, or, while the stream is
+// being captured (a pinned copy would become a graph node that reads the
+// image at every replay), the arrays copied one by one.
 static int stage_inputs(w4_model* m, const int32_t* tokens, const int32_t* positions,
                         const int32_t* page_tables, const int32_t* ctx_lens, int batch,
                         hipStream_t s) {
   const WsLayout& L = m->L;
-  if (tokens) W4_HIP(hipMemcpyAsync(m->ws + L.tokens, tokens, batch * 4, hipMemcpyHostToDevice, s));
-  W4_HIP(hipMemcpyAsync(m->ws + L.positions, positions, batch * 4, hipMemcpyHostToDevice, s));
-  W4_HIP(hipMemcpyAsync(m->ws + L.ctx, ctx_lens, batch * 4, hipMemcpyHostToDevice, s));
-  W4_HIP(hipMemcpyAsync(m->ws + L.pt, page_tables, (size_t)batch * m->max_pages * 4,
-                        hipMemcpyHostToDevice, s));
-  return W4_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  W4_HIP(hipStreamIsCapturing(s, &cs));
+  if (cs != hipStreamCaptureStatusNone) {
+    if (tokens) W4_HIP(hipMemcpyAsync(m->ws + L.tokens, tokens, batch * 4, hipMemcpyHostToDevice, s));
+    W4_HIP(hipMemcpyAsync(m->ws + L.positions, positions, batch * 4, hipMemcpyHostToDevice, s));
+    W4_HIP(hipMemcpyAsync(m->ws + L.ctx, ctx_lens, batch * 4, hipMemcpyHostToDevice, s));
+    W4_HIP(hipMemcpyAsync(m->ws + L.pt, page_tables, (size_t)batch * m->max_pages * 4,
+                          hipMemcpyHostToDevice, s));
+    return W4_OK;
+  }
+  StageImage im;
+  int rc = stage_image(m, im);
+  if (rc) return rc;
+  if (tokens) std::memcpy(im.tokens, tokens, batch * 4);
+  std::memcpy(im.positions, positions, batch * 4);
+  std::memcpy(im.ctx, ctx_lens, batch * 4);
+  std::memcpy(im.pt, page_tables, (size_t)batch * m->max_pages * 4);
+  return stage_commit(m, im, tokens != nullptr, batch, s);
 }
 
 static StepInputs staged(w4_model* m) {
@@ -509,11 +568,15 @@ W4_EXPORT int w4_model_create(const w4_config* cfg, const w4_weights* weights, v
   m->max_pages = max_pages;
   m->ws = static_cast<uint8_t*>(workspace);
   m->L = L;
+  m->stage_bytes = round_up(L.pt - L.tokens + (size_t)max_batch * max_pages * 4, 256);
   hipError_t e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
   if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(m->ws), L.total / 4, 0u, m->cap_stream);
   if (e == hipSuccess) e = hipStreamSynchronize(m->cap_stream);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&m->stage_img), 2 * m->stage_bytes, 0);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&m->gen_tokens), (size_t)max_batch * 4, 0);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&m->stage_ev[i], hipEventDisableTiming);
   if (e != hipSuccess) {
-    if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+    release_model_resources(m);
     delete m;
     return fail(W4_EHIP, "w4_model_create: %s", hipGetErrorString(e));
   }
@@ -525,9 +588,7 @@ W4_EXPORT int w4_model_create(const w4_config* cfg, const w4_weights* weights, v
 W4_EXPORT void w4_model_destroy(w4_model* m) {
   if (!handle_release(m)) return;  // null, already destroyed or never created
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
-  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
-  if (m->gen_stage) (void)hipHostFree(m->gen_stage);
-  if (m->gen_tokens) (void)hipHostFree(m->gen_tokens);
+  release_model_resources(m);
   delete m;
 }
 
@@ -862,46 +923,31 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_steps == 0) return W4_OK;
-  // The staged positions, context lengths and page tables are consecutive
-  // workspace regions: each step's go to the device as one copy from a pinned
-  // host image, and the chosen tokens come back into pinned memory (one copy
-  // each way per step, asynchronous; pageable copies were five per step).
+  // Each step's positions, context lengths and page tables go to the device
+  // as one copy from a pinned image (stage_image / stage_commit), and the
+  // chosen tokens come back into pinned memory: one copy each way per step,
+  // asynchronous (pageable copies were five per step).
   const WsLayout& L = m->L;
-  const size_t stage_bytes = round_up(L.pt - L.positions + (size_t)m->max_batch * m->max_pages * 4, 256);
-  if (!m->gen_stage && hipHostMalloc(reinterpret_cast<void**>(&m->gen_stage), 2 * stage_bytes, 0) != hipSuccess) {
-    m->gen_stage = nullptr;
-    return fail(W4_EHIP, "w4_generate_greedy: pinned staging buffer of %zu bytes", stage_bytes);
-  }
-  if (!m->gen_tokens &&
-      hipHostMalloc(reinterpret_cast<void**>(&m->gen_tokens), (size_t)m->max_batch * 4, 0) != hipSuccess) {
-    m->gen_tokens = nullptr;
-    return fail(W4_EHIP, "w4_generate_greedy: pinned token buffer");
-  }
-  const size_t copy_bytes = L.pt - L.positions + (size_t)batch * m->max_pages * 4;
   std::vector<int32_t> pos(first_positions, first_positions + batch);
-  // validates and stages step `step`'s positions into pinned image step % 2,
-  // then copies it (the tokens are already in the staged slot: the first
-  // step's from the host, later ones from the device argmax). Image i is
-  // rewritten for step s + 2 only after the host has waited for step s, whose
-  // wait covers the copy of image i made before step s ran.
-  auto stage_step = [&](const int32_t* tokens, int step) -> int {
-    uint8_t* img = m->gen_stage + (size_t)(step & 1) * stage_bytes;
-    int32_t* h_pos = reinterpret_cast<int32_t*>(img);
-    int32_t* h_ctx = reinterpret_cast<int32_t*>(img + (L.ctx - L.positions));
-    int32_t* h_pt = reinterpret_cast<int32_t*>(img + (L.pt - L.positions));
+  // validates and stages the next step's inputs while the current step runs;
+  // the tokens are already in the staged slot after the first step (the
+  // device argmax writes them there)
+  auto stage_step = [&](const int32_t* tokens) -> int {
+    StageImage im;
+    int r = stage_image(m, im);
+    if (r) return r;
     for (int b = 0; b < batch; ++b) {
-      h_pos[b] = pos[b];
-      h_ctx[b] = pos[b] + 1;
-      int r = kv_seq_reserve(pool, seqs[b], h_ctx[b]);
+      im.positions[b] = pos[b];
+      im.ctx[b] = pos[b] + 1;
+      r = kv_seq_reserve(pool, seqs[b], im.ctx[b]);
       if (r) return r;
     }
-    int r = page_table(pool, seqs, batch, m->max_pages, h_pt);
+    r = page_table(pool, seqs, batch, m->max_pages, im.pt);
     if (r) return r;
-    r = validate_inputs(m, tokens, h_pos, h_pt, h_ctx, batch);
+    r = validate_inputs(m, tokens, im.positions, im.pt, im.ctx, batch);
     if (r) return r;
-    if (tokens) W4_HIP(hipMemcpyAsync(m->ws + L.tokens, tokens, batch * 4, hipMemcpyHostToDevice, s));
-    W4_HIP(hipMemcpyAsync(m->ws + L.positions, img, copy_bytes, hipMemcpyHostToDevice, s));
-    return W4_OK;
+    if (tokens) std::memcpy(im.tokens, tokens, batch * 4);
+    return stage_commit(m, im, tokens != nullptr, batch, s);
   };
   int32_t* tok_dev = m->at<int32_t>(L.tokens);
   // next_tokens gets the last chosen tokens once, on every return after a step
@@ -911,7 +957,7 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
       return ret ? ret : fail(W4_EHIP, "w4_generate_greedy: copy of the last tokens");
     return ret;
   };
-  rc = stage_step(first_tokens, 0);
+  rc = stage_step(first_tokens);
   if (rc) return rc;
   for (int step = 0; step < n_steps; ++step) {
     rc = run_step(m, staged(m), batch, logits, s, nullptr);
@@ -923,7 +969,7 @@ W4_EXPORT int w4_generate_greedy(w4_model* m, w4_kv_pool* pool, const int32_t* s
     int stage_rc = W4_OK;
     if (step + 1 < n_steps) {
       for (int b = 0; b < batch; ++b) ++pos[b];
-      stage_rc = stage_step(nullptr, step + 1);
+      stage_rc = stage_step(nullptr);
     }
     W4_HIP(hipStreamSynchronize(s));
     int32_t* row = out_tokens + (size_t)step * batch;
