@@ -93,6 +93,46 @@ def test_device_inputs_match_host_inputs():
     assert dm.model.w4_device_errors() == 0
 
 
+@pytest.mark.parametrize("graph", [True, False])
+def test_back_to_back_host_input_steps(graph):
+    """Six host-input steps enqueued without a synchronisation in between,
+    each with its own tokens, positions, page table and context lengths: the
+    host staging images are reused while earlier copies may still be queued,
+    so every step must still see its own inputs. Reference: the same six steps
+    with device-resident inputs from the same initial KV cache (same kernels,
+    so bit-identical)."""
+    dm = small_model([60, 30])
+    w, m = dm.w, dm.model
+    rs = np.random.default_rng(11)
+    calls = []
+    for _ in range(6):
+        c0 = int(rs.integers(1, 16 * w.max_pages + 1))
+        room = min(w.max_pages, w.num_pages - (c0 + 15) // 16)
+        ctx = np.array([c0, rs.integers(1, 16 * room + 1)], np.int32)
+        pt = np.full_like(w.page_tables, -1)
+        perm = rs.permutation(w.num_pages).astype(np.int32)
+        n0, n1 = (ctx + 15) // 16
+        pt[0, :n0] = perm[:n0]
+        pt[1, :n1] = perm[n0:n0 + n1]
+        toks = rs.integers(0, SMALL.vocab, 2).astype(np.int32)
+        calls.append((toks, ctx - 1, pt, ctx))
+    snap = dm.kv_cache.clone()
+    m.w4_set_graph(graph)
+    outs = [torch.empty((2, SMALL.vocab), dtype=torch.float16, device="cuda") for _ in calls]
+    for (t, p, pt, c), o in zip(calls, outs):
+        m.decode_step(t, p, pt, c, o)            # host arrays, no wait between the calls
+    torch.cuda.synchronize()
+    got = [to_np16(o) for o in outs]
+    dm.kv_cache.copy_(snap)
+    for i, (t, p, pt, c) in enumerate(calls):
+        dev = [torch.from_numpy(np.ascontiguousarray(x, np.int32)).cuda() for x in (t, p, pt, c)]
+        ref = torch.empty((2, SMALL.vocab), dtype=torch.float16, device="cuda")
+        m.decode_step_device(*dev, ref)
+        torch.cuda.synchronize()
+        assert np.array_equal(got[i].view(np.uint16), to_np16(ref).view(np.uint16)), f"call {i}"
+    assert m.w4_device_errors() == 0
+
+
 def test_destroyed_model_handle_is_rejected():
     """A destroyed model is refused (W4_ESTATE, -1 for the error count), and a
     second destroy does nothing."""
