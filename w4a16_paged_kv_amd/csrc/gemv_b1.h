@@ -75,12 +75,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Device-coherent accesses, for data that workgroups of one launch exchange:
 // 16-bit stores through the atomic builtins, buffer loads and stores with the
-// sc1 policy bit. Data passed from one launch to a later one needs neither
-// (the batch-1 residual epilogues still store this way: written through, their
-// rows leave no dirty lines for the launch's end, measured 0.2 us faster per
-// launch than plain stores).
+// sc1 policy bit. Data passed from one launch to a later one needs neither,
+// but the decode epilogues still store this way (residual rows, SiLU rows,
+// q and the new token's K/V): written through, they leave no dirty lines for
+// the launch's end (batch-1 o-proj and down 0.2 us faster per launch than
+// plain stores; with the SiLU and qkv stores written through too, the
+// batch-1 step 1.2380-1.2395 -> 1.2343-1.2349 ms, batch 16 unchanged).
 __device__ __forceinline__ void st16_agent(uint16_t* p, uint16_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A 16-bit store, written through (device scope) or plain.
+__device__ __forceinline__ void st16(uint16_t* p, uint16_t v, bool through) {
+  if (through)
+    st16_agent(p, v);
+  else
+    *p = v;
 }
 
 // a raw buffer of 2^31 - 1 bytes at base
@@ -128,14 +137,14 @@ __host__ __device__ __forceinline__ int k_slice_offset(int t, int d) {
 }
 
 // One token's K or V values (dims dim0, dim1 of KV head kvh) into its page
-// slot, in the slice orders above.
+// slot, in the slice orders above (written through, or plain).
 __device__ __forceinline__ void kv_store(const QkvEpilogue& e, uint16_t* pool, bool v_layout, int slot, int kvh,
-                                         int dim0, int dim1, float v0, float v1) {
+                                         int dim0, int dim1, float v0, float v1, bool through) {
   if (slot < 0) return;  // invalid position or page: counted by the token plan
   uint16_t* sl = pool + ((size_t)(slot >> 4) * e.n_kv_heads + kvh) * kPage * e.head_dim;
   const int t = slot & 15;
-  sl[v_layout ? v_slice_offset(t, dim0) : k_slice_offset(t, dim0)] = f2h(v0);
-  sl[v_layout ? v_slice_offset(t, dim1) : k_slice_offset(t, dim1)] = f2h(v1);
+  st16(&sl[v_layout ? v_slice_offset(t, dim0) : k_slice_offset(t, dim0)], f2h(v0), through);
+  st16(&sl[v_layout ? v_slice_offset(t, dim1) : k_slice_offset(t, dim1)], f2h(v1), through);
 }
 
 // Rows i and i+8 of tile t hold the rotate-half RoPE pair (dim0, dim0 + D/2)
@@ -147,9 +156,11 @@ __device__ __forceinline__ int qkv_dim0(const QkvEpilogue& e, int t, int i) {
 
 // q/k heads are rotated by (c, sn), the token plan's rotation of the pair
 // (angle pos * base^(-2 dim0 / D)), and rounded once to fp16; v heads are
-// rounded unrotated. k/v go to the token's page slot.
+// rounded unrotated. k/v go to the token's page slot. through: q and k/v
+// written through (decode) or plain (prefill, whose attention re-reads the
+// pages from L2).
 __device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float y1, float c, float sn,
-                        int slot) {
+                        int slot, bool through) {
   const QkvEpilogue& e = a.qkv;
   const int D = e.head_dim;
   const int head = qkv_head(e, t);
@@ -163,13 +174,13 @@ __device__ void epi_qkv(const GemvArgs& a, int m, int t, int i, float y0, float 
     const float r1 = y1 * c + y0 * sn;
     if (head < e.n_heads) {
       uint16_t* q = e.q_out + (size_t)m * e.q_stride + head * D;
-      q[dim0] = f2h(r0);
-      q[dim1] = f2h(r1);
+      st16(&q[dim0], f2h(r0), through);
+      st16(&q[dim1], f2h(r1), through);
     } else {
-      kv_store(e, e.k_pool, false, slot, head - e.n_heads, dim0, dim1, r0, r1);
+      kv_store(e, e.k_pool, false, slot, head - e.n_heads, dim0, dim1, r0, r1, through);
     }
   } else {
-    kv_store(e, e.v_pool, true, slot, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1);
+    kv_store(e, e.v_pool, true, slot, head - e.n_heads - e.n_kv_heads, dim0, dim1, y0, y1, through);
   }
 }
 
@@ -185,12 +196,12 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int m, int t, int i,
   if (EPI == EPI_QKV) {
     const int pair = qkv_dim0(a.qkv, t, i);
     const float* cs = a.qkv.rope + ((size_t)m * (a.qkv.head_dim / 2) + pair) * 2;
-    epi_qkv(a, m, t, i, vals[i], vals[i + 8], cs[0], cs[1], a.qkv.slot[m]);
+    epi_qkv(a, m, t, i, vals[i], vals[i + 8], cs[0], cs[1], a.qkv.slot[m], true);
   } else if (EPI == EPI_SILU) {
     const int o = 8 * t + i;
     if (o < a.n / 2) {
       const float g = vals[i], u = vals[i + 8];
-      a.y[(size_t)m * a.y_stride + o] = f2h(g / (1.0f + expf(-g)) * u);
+      st16_agent(&a.y[(size_t)m * a.y_stride + o], f2h(g / (1.0f + expf(-g)) * u));
     }
   } else {
     const int row = kTileRows * t + i;
@@ -545,7 +556,7 @@ struct GemvB1 {
       if (tt < a.tiles) {
         const int i = threadIdx.x % per;
         if (EPI == EPI_QKV)
-          epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], pre.c, pre.s, pre.slot);
+          epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], pre.c, pre.s, pre.slot, true);
         else if (EPI == EPI_RESID) {
           const int row = kTileRows * tt + i;
           if (row < a.n) st16_agent(a.y + row, f2h(vals[tl * 16 + i] + pre.resid));  // write-through: measured faster here
@@ -669,7 +680,7 @@ struct GemvB1Range {
       if (tt < a.tiles) {
         const int i = threadIdx.x % per;
         if (EPI == EPI_QKV)
-          epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], pre.c, pre.s, pre.slot);
+          epi_qkv(a, 0, tt, i, vals[tl * 16 + i], vals[tl * 16 + i + 8], pre.c, pre.s, pre.slot, true);
         else if (EPI == EPI_RESID) {
           const int row = kTileRows * tt + i;
           if (row < a.n) st16_agent(a.y + row, f2h(vals[tl * 16 + i] + pre.resid));  // write-through: measured faster here

@@ -58,7 +58,7 @@ __device__ __forceinline__ void pf_epilogue(const GemvArgs& a, int m, int t, int
     if (i < 8) {
       const int pair = qkv_dim0(a.qkv, t, i);
       const float* cs = a.qkv.rope + ((size_t)m * (a.qkv.head_dim / 2) + pair) * 2;
-      epi_qkv(a, m, t, i, v, partner, cs[0], cs[1], a.qkv.slot[m]);
+      epi_qkv(a, m, t, i, v, partner, cs[0], cs[1], a.qkv.slot[m], false);
     }
   } else if (EPI == EPI_SILU) {
     const int o = 8 * t + i;
