@@ -133,6 +133,27 @@ def test_back_to_back_host_input_steps(graph):
     assert m.w4_device_errors() == 0
 
 
+def test_destroy_right_after_an_asynchronous_host_input_step():
+    """A model destroyed while its last host-input steps may still be queued
+    (no synchronisation in between) releases its staging buffers only after
+    their copies ran: the queued steps finish with the inputs they were given."""
+    import w4a16_paged_kv_amd as w4
+    dm = small_model([45, 9])
+    ref = step(dm, graph=True)
+    t, p, pt, c = dm.step_inputs()
+    outs = [torch.empty((2, SMALL.vocab), dtype=torch.float16, device="cuda") for _ in range(3)]
+    snap = dm.kv_cache.clone()
+    for o in outs:
+        dm.kv_cache.copy_(snap)                  # same KV state for every call (stream-ordered)
+        dm.model.decode_step(t, p, pt, c, o)
+    h = dm.model.handle
+    w4.lib().w4_model_destroy(h)
+    dm.model.handle = None
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(to_np16(o).view(np.uint16), ref.view(np.uint16))
+
+
 def test_destroyed_model_handle_is_rejected():
     """A destroyed model is refused (W4_ESTATE, -1 for the error count), and a
     second destroy does nothing."""

@@ -125,11 +125,16 @@ struct w4_model {
   }
 };
 
-// The model's own stream, events and pinned buffers (any may be null).
+// The model's own stream, events and pinned buffers (any may be null). A
+// staging copy may still be queued behind the caller's work: each image is
+// freed only after its event.
 static void release_model_resources(w4_model* m) {
   if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
   for (hipEvent_t ev : m->stage_ev)
-    if (ev) (void)hipEventDestroy(ev);
+    if (ev) {
+      (void)hipEventSynchronize(ev);
+      (void)hipEventDestroy(ev);
+    }
   if (m->stage_img) (void)hipHostFree(m->stage_img);
   if (m->gen_tokens) (void)hipHostFree(m->gen_tokens);
 }
