@@ -12,7 +12,7 @@ import workloads as wl
 from oracle import generate as og
 from tests.gpu_util import assert_close, to_np16
 from tests.staged import kv_slot
-from workloads.device import DeviceModel
+from workloads.device import DeviceModel, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -88,12 +88,12 @@ def run_generation(dm, pool, w, p0, n, graph=True):
     return toks, to_np16(logits)
 
 
-@pytest.mark.parametrize("starts,n,wid", [([29, 13], 20, 31), ([0, 16, 5], 18, 33)])
+@pytest.mark.parametrize("starts,n,wid", [([29, 13], 20, 31), ([0, 16, 5], 18, 33), ([29], 20, 34)])
 def test_generation_matches_oracle(starts, n, wid):
     """20 steps from positions 29 and 13 (pages grow at 32, 48 and 16, 32),
     or 18 steps of three sequences: one with no prior context (its first page
     is reserved by the first step), one starting exactly on a page boundary,
-    one mid-page. The pool ends exactly full. Teacher-forced with the GPU's
+    one mid-page, or one sequence alone. The pool ends exactly full. Teacher-forced with the GPU's
     tokens, the oracle confirms every choice: the chosen token's oracle logit is
     the maximum up to the logits' tolerance, and it is the oracle's own argmax
     wherever the oracle's top two are further apart than that. The last
@@ -189,4 +189,42 @@ def test_generation_full_size_matches_decode_step():
     torch.cuda.synchronize()
     again = to_np16(logits)
     assert np.array_equal(again.view(np.uint16), last.view(np.uint16))
+    assert dm.model.w4_device_errors() == 0
+
+
+def test_generation_skips_nan_logits_and_stops_on_all_nan():
+    """Through the generation loop (batch 1): lm_head rows set to NaN (every
+    third row and the previously chosen one) give NaN logits that are never
+    chosen (the choice equals the oracle's rule on the step's own logits), and
+    with every row NaN the loop stops with W4_ERANGE before a second step,
+    next_tokens reading -1."""
+    from workloads import lm_head_chunk, n_chunks
+    p0 = np.array([21], dtype=np.int32)
+    w = wl.custom("gen_nan", 35, SMALL, p0 + 2, layers=3, lm_head=True, gamma="random")
+    dm, pool = setup_generation(w, p0)
+    sh = w.shape
+    W = np.concatenate([lm_head_chunk(w.workload_id, sh, c) for c in range(n_chunks(sh))])
+    toks, last = run_generation(dm, pool, w, p0, 1)
+    best = og.greedy_token(last[0].astype(np.float64))
+    assert toks[0, 0] == best
+    Wn = W.copy()
+    nan_rows = np.unique(np.concatenate([[best], np.arange(0, sh.vocab, 3)]))
+    Wn[nan_rows] = np.nan                        # the previous best among them
+    dm.lm_head.copy_(to_dev(w4.pack_weights_f16(Wn)).view(torch.uint8).view(-1))
+    pool2 = w4.KvPool(w.num_pages, 1)
+    pool2.kv_seq_reserve(0, int(p0[0]))
+    toks2, last2 = run_generation(dm, pool2, w, p0, 1)
+    assert np.isnan(last2[0, nan_rows]).all() and not np.isnan(np.delete(last2[0], nan_rows)).any()
+    assert toks2[0, 0] == og.greedy_token(last2[0].astype(np.float64)) and toks2[0, 0] not in nan_rows
+    Wn[:] = np.nan
+    dm.lm_head.copy_(to_dev(w4.pack_weights_f16(Wn)).view(torch.uint8).view(-1))
+    pool3 = w4.KvPool(w.num_pages, 1)
+    pool3.kv_seq_reserve(0, int(p0[0]))
+    logits = torch.empty((1, sh.vocab), dtype=torch.float16, device="cuda")
+    nxt = torch.empty((1,), dtype=torch.int32, device="cuda")
+    with pytest.raises(w4.W4Error, match="every logit is NaN") as e:
+        dm.model.w4_generate_greedy(pool3, [0], w.tokens(), p0, 2, logits, nxt)
+    assert e.value.steps_done == 0
+    torch.cuda.synchronize()
+    assert int(nxt.cpu()[0]) == -1
     assert dm.model.w4_device_errors() == 0
