@@ -202,6 +202,15 @@ def full_check(w, check_layers, n_rows=None, force_layers=(), chains=False, log=
     m.w4_model_run_op(w4.OP_LM_HEAD, 0, B, logits)
     torch.cuda.synchronize()
     xf = to_np16(buf(dm, w4.BUF_XN, B)[:, :sh.hidden])
+    if B > 1:
+        # the model's lm_head reads the final RMSNorm's rows in the MFMA
+        # operand order; the public call reads the same rows as rows: same
+        # kernel, same accumulation order, so the same bits
+        xrows = buf(dm, w4.BUF_XN, B)[:, :sh.hidden].contiguous()
+        again = torch.empty_like(logits)
+        w4.w4_gemv_f16(dm.lm_head, xrows, again, sh.vocab, sh.hidden, B)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), logits.view(torch.int16)), "lm_head row orders differ"
     for b in live:
         assert_close(xf[b], od.rmsnorm(x[b], w.final_norm(), sh.eps), f"{w.name} seq {b}: final rmsnorm")
     rows = (np.arange(sh.vocab) if n_rows is None else
