@@ -33,9 +33,11 @@
  *     device memory (for example a torch tensor's data_ptr()). Every device
  *     pointer must be 256-byte aligned (W4_EALIGN otherwise).
  *   - The caller owns every buffer. The library owns only the opaque
- *     handles (w4_kv_pool, w4_model) and the graphs it captures, released by
- *     the matching *_destroy. The library never allocates device memory:
- *     its scratch lives in the caller's workspace.
+ *     handles (w4_kv_pool, w4_model) and what a model keeps inside: the
+ *     graphs it captures, a capture stream, two events and a few KB of
+ *     pinned host memory for staging host inputs (hipHostMalloc), all
+ *     released by the matching *_destroy. The library never allocates device
+ *     memory: its scratch lives in the caller's workspace.
  *   - Device work is enqueued asynchronously on the caller's HIP stream
  *     (`stream` is a hipStream_t; NULL means the default stream). Outputs are
  *     valid once that stream has been synchronised.
