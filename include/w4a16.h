@@ -34,9 +34,10 @@
  *     pointer must be 256-byte aligned (W4_EALIGN otherwise).
  *   - The caller owns every buffer. The library owns only the opaque
  *     handles (w4_kv_pool, w4_model) and what a model keeps inside: the
- *     graphs it captures, a capture stream, two events and a few KB of
- *     pinned host memory for staging host inputs (hipHostMalloc), all
- *     released by the matching *_destroy. The library never allocates device
+ *     graphs it captures, a capture stream, two events and pinned host
+ *     memory for staging host inputs (hipHostMalloc: two images of about
+ *     max_batch * (3 + max_pages_per_seq) * 4 bytes each), all released by
+ *     the matching *_destroy. The library never allocates device
  *     memory: its scratch lives in the caller's workspace.
  *   - Device work is enqueued asynchronously on the caller's HIP stream
  *     (`stream` is a hipStream_t; NULL means the default stream). Outputs are
