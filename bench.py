@@ -7,10 +7,11 @@ W4A16 weights, fp16 lm_head), batch 1, 2048-token context. One step = one
 decode_step over all layers + lm_head for the batch, inputs already resident
 in HBM. Prints one JSON line: ms/token, tokens/s, effective HBM GB/s against
 the 8 TB/s peak, the roofline of the dominant kernel and the CPU oracle
-timed on a bounded sample of the same workload. Two more workloads are timed
-on the same weights and reported under their own keys: the batch-16 step
+timed on a bounded sample of the same workload. More workloads are timed and
+reported under their own keys: on the same weights the batch-16 step
 (step_b16: 16 sequences, contexts 1024..4096) and the prefill of a
-512-token prompt (prefill_512: time to first token).
+512-token prompt (prefill_512: time to first token), and paged attention
+alone on 32 sequences with contexts 128..8192 (attn_stress).
 """
 from __future__ import annotations
 
@@ -165,7 +166,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="step_b1", choices=["step_b1", "step_b16"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="skip the batch-16 step and the prefill")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the batch-16 step, the prefill, the W4A8 variant and the attention stress workload")
     ap.add_argument("--op-reps", type=int, default=20)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run three plain device copies of MIB MiB each, so that HBM byte "
@@ -414,6 +416,44 @@ def main():
             del packed
         print(f"[bench] variants {variants}", file=sys.stderr, flush=True)
 
+    # ---- paged attention alone on 32 sequences with contexts U[128, 8192]
+    # (one layer's KV pool), warm: ten calls captured in a graph and replayed
+    stress = None
+    if args.workload == "step_b1" and not args.no_extra:
+        from workloads.device import to_dev, v_pages_device
+        ws_ = wl.attn_stress()
+        ssh, nseq = ws_.shape, len(ws_.ctx_lens)
+        kq, vq = ws_.kv(0)
+        qd, kd, vd = to_dev(ws_.attn_q()), to_dev(kq), to_dev(v_pages_device(vq))
+        ptd = torch.from_numpy(np.ascontiguousarray(ws_.page_tables, np.int32)).cuda()
+        cd = torch.from_numpy(np.ascontiguousarray(ws_.ctx_lens, np.int32)).cuda()
+        aws = torch.empty((w4.paged_attention_workspace_bytes(nseq, ssh.n_heads, ssh.n_kv_heads, ssh.head_dim,
+                                                              ws_.page_tables.shape[1]),),
+                          dtype=torch.uint8, device="cuda")
+        aout = torch.empty((nseq, ssh.n_heads, ssh.head_dim), dtype=torch.float16, device="cuda")
+        call = lambda: w4.paged_attention_decode(qd, kd, vd, ptd, cd, ssh.n_heads, ssh.n_kv_heads,
+                                                 ssh.head_dim, kq.shape[0], aws, aout)
+        call()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(10):
+                call()
+        g.replay()
+        reps = [timed(g.replay, 1) / 10 for _ in range(max(10, args.op_reps))]
+        us = float(np.median(reps)) * 1e3
+        sbytes = int(ws_.ctx_lens.sum()) * ssh.n_kv_heads * ssh.head_dim * 2 * 2 \
+            + nseq * ssh.n_heads * ssh.head_dim * 2 * 2
+        stress = {"us_per_call": round(us, 2), "sequences": nseq,
+                  "ctx": {"min": int(ws_.ctx_lens.min()), "max": int(ws_.ctx_lens.max()),
+                          "sum": int(ws_.ctx_lens.sum())},
+                  "bytes_per_call": sbytes, "GBps": round(sbytes / (us * 1e-6) / 1e9, 1),
+                  "pct_of_peak": round(100 * sbytes / (us * 1e-6) / PEAK_HBM, 2),
+                  "clock": "events around one replay of ten captured calls, median of the replays"}
+        del g, qd, kd, vd, ptd, cd, aws, aout
+        torch.cuda.empty_cache()
+        print(f"[bench] attn_stress {us:.2f} us/call", file=sys.stderr, flush=True)
+
     cpu = None if args.no_cpu else cpu_baseline(w)
 
     tok_s = B * 1e3 / ms
@@ -456,6 +496,7 @@ def main():
         "step_b16": b16,
         "prefill_512": pf,
         "w4a8_variant": variants,
+        "attn_stress": stress,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
