@@ -156,3 +156,69 @@ def test_empty_context_and_invalid_pages_are_safe():
     got = run_attn(q, k, v, w.page_tables, np.array([0, 40], np.int32), 28, 4, 128)
     assert np.all(got[0] == 0)
     assert np.array_equal(got[1].view(np.uint16), ref[1].view(np.uint16))
+
+
+def fixed_pages_per_split(batch, n_kv, max_pages):
+    """The launcher's fixed split size (pages): one page per wavefront until
+    about 256 workgroups, at most 32 pages per wavefront, at most 128 splits."""
+    units, pw = batch * n_kv * max_pages, 1
+    while pw < 32 and units // (8 * pw) > 256:
+        pw *= 2
+    pps = 8 * pw
+    while -(-max_pages // pps) > 128:
+        pps *= 2
+    return pps
+
+
+@pytest.mark.parametrize("d,hq,hkv,ctx,width", [
+    (128, 28, 4, [1, 17, 300, 3000, 2500, 16, 1200, 129], 4096),   # a few sequences, uneven
+    (64, 7, 1, "u64", 512),                                         # 64 sequences
+    (128, 16, 2, [5000, 10, 7000], 8192),                           # GQ 8
+    (64, 8, 4, "u64", 1024),                                        # GQ 2, 256 (sequence, KV head) pairs
+    (64, 8, 8, "u64", 1024),                                        # 512 pairs
+    (128, 7, 1, [20000, 16], 16384),                                # a long sequence beside a short one
+])
+def test_uneven_contexts_in_long_splits(d, hq, hkv, ctx, width):
+    """Page tables padded with -1 to `width` columns set the split size to
+    16-32 pages per wavefront (first page issued early, default K/V load
+    policy) while the contexts stay short enough for the oracle: most
+    sequences end inside their first split, several wavefronts of a split
+    have no page, a long one spans splits. A second call on the same
+    workspace must give the same bits (the merging workgroup resets its
+    arrival counter), and sequences whose context is then set to 0 give
+    zeros while the others still match."""
+    if isinstance(ctx, str):
+        ctx = wl.rng(67, hq, width).integers(1, 2000, 64)
+    ctx = np.asarray(ctx, np.int32)
+    assert 1 < len(ctx) <= 64 and fixed_pages_per_split(len(ctx), hkv, width) >= 128
+    sh = wl.Shape(hidden=hq * d, n_heads=hq, n_kv_heads=hkv, head_dim=d, ffn=8, vocab=8, n_layers=1)
+    w = wl.custom("longsplit", 68 + hkv, sh, ctx)
+    q = w.attn_q()
+    k, v = w.kv(0)
+    poison(k, v, w.page_tables, w.ctx_lens)
+    pt = np.full((len(ctx), width), -1, np.int32)
+    pt[:, :w.page_tables.shape[1]] = w.page_tables
+    print(f"long-split attention d={d} heads={hq}/{hkv} batch={len(ctx)} width={width} "
+          f"ctx {ctx.min()}..{ctx.max()}", flush=True)
+    qd, kd, vd = to_dev(q), to_dev(k_pages_device(k)), to_dev(v_pages_device(v))
+    ptd = torch.from_numpy(pt).cuda()
+    cd = torch.from_numpy(ctx.copy()).cuda()
+    ws = torch.empty(w4.paged_attention_workspace_bytes(len(ctx), hq, hkv, d, width), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((len(ctx), hq, d), dtype=torch.float16, device="cuda")
+    call = lambda: w4.paged_attention_decode(qd, kd, vd, ptd, cd, hq, hkv, d, k.shape[0], ws, out)
+    call()
+    torch.cuda.synchronize()
+    got = to_np16(out)
+    ref = runs.attention_batch(w, q, k, v)
+    assert_close(got, ref, f"long splits d={d} gqa={hq // hkv}")
+    call()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np16(out).view(np.uint16), got.view(np.uint16)), "second call differs"
+    zero = np.arange(len(ctx)) % 3 == 1
+    cd.copy_(torch.from_numpy(np.where(zero, 0, ctx).astype(np.int32)))
+    call()
+    torch.cuda.synchronize()
+    got2 = to_np16(out)
+    assert np.all(got2[zero] == 0)
+    assert_close(got2[~zero], ref[~zero], "long splits, some contexts empty")

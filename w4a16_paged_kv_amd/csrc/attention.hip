@@ -16,9 +16,9 @@ namespace w4 {
 // dispatcher sends every sequence's first splits before any later ones and
 // the items past a short sequence's last split (which exit at once) come at
 // the end (32 sequences, contexts 128-8192: 78 -> 75 us).
-template <int D, int GQ, bool EARLY>
+template <int D, int GQ, bool EARLY, bool NTL>
 __global__ __launch_bounds__(kAttnWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void paged_attn_kernel(AttnArgs a) {
-  attn_item<D, GQ, kAttnWaves * 64, EARLY>(a, blockIdx.z, blockIdx.y, blockIdx.x);
+  attn_item<D, GQ, kAttnWaves * 64, EARLY, NTL>(a, blockIdx.z, blockIdx.y, blockIdx.x);
 }
 
 bool attention_supported(int head_dim, int group) {
@@ -50,11 +50,17 @@ template <int D, int GQ>
 static hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.batch, a.n_kv_heads, a.max_splits), block(kAttnWaves * 64);
   // several pages per wavefront: the first page's loads go out before the
-  // queries are staged
-  if (a.pages_per_split > kAttnWaves)
-    hipLaunchKernelGGL((paged_attn_kernel<D, GQ, true>), grid, block, 0, s, a);
+  // queries are staged. With two to eight pages per wavefront K/V are read
+  // non-temporally: the batch-16 step (16 sequences of 1024-4096 tokens)
+  // 2.177 -> 2.124 ms, while one page per wavefront (batch 1: 1.2368 ->
+  // 1.2438 ms per step) and 32 (32 sequences of 128-8192 tokens: 52.6 ->
+  // 55.7 us) keep the default policy.
+  if (a.pages_per_split > kAttnWaves && a.pages_per_split <= 8 * kAttnWaves)
+    hipLaunchKernelGGL((paged_attn_kernel<D, GQ, true, true>), grid, block, 0, s, a);
+  else if (a.pages_per_split > kAttnWaves)
+    hipLaunchKernelGGL((paged_attn_kernel<D, GQ, true, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((paged_attn_kernel<D, GQ, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((paged_attn_kernel<D, GQ, false, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

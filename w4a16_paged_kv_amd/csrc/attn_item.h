@@ -29,6 +29,7 @@ namespace w4 {
 constexpr float kLog2e = 1.4426950408889634f;
 
 constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time each
+constexpr int kPolicyNt = 2;    // buffer instruction cache-policy operand: nt (non-temporal)
 
 
 // One work item (split of pages, KV head, sequence) on one workgroup of NT
@@ -43,7 +44,8 @@ constexpr int kAttnWaves = 8;  // wavefronts per workgroup, one page at a time e
 // EARLY: issue the wavefront's first page before the queries are staged
 // (items of several pages per wavefront: their first pages then overlap the
 // query staging; with one page per wavefront the queries are better first).
-template <int D, int GQ, int NT, bool EARLY, bool PF = true>
+// NTL: read K/V with non-temporal loads (chosen by the launcher).
+template <int D, int GQ, int NT, bool EARLY, bool NTL = false, bool PF = true>
 __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(GQ >= 1 && GQ <= 8, "group");
@@ -96,14 +98,17 @@ __device__ void attn_item(const AttnArgs& a, int split, int kvh, int b) {
   };
   u4_t kf[NK], kn[PF ? NK : 1];
   u4_t vf[NS / 2], vn[PF ? NS / 2 : 1];  // V operands of slice pairs (2i, 2i + 1)
+  auto ld_kv = [](__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NTL ? kPolicyNt : 0));
+  };
   auto load_kv = [&](int page, u4_t* kk, u4_t* vv) {
     page = __builtin_amdgcn_readfirstlane(page);  // one page per wavefront: keeps the resources scalar
     const __amdgpu_buffer_rsrc_t rk = buf_rsrc(a.k_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
     const __amdgpu_buffer_rsrc_t rv = buf_rsrc(a.v_pool + ((size_t)page * a.n_kv_heads + kvh) * slice);
 #pragma unroll
-    for (int i = 0; i < NK; ++i) kk[i] = ld128(rk, 16 * (64 * i + lane_));  // K slice in score operand order
+    for (int i = 0; i < NK; ++i) kk[i] = ld_kv(rk, 16 * (64 * i + lane_));  // K slice in score operand order
 #pragma unroll
-    for (int i = 0; i < NS / 2; ++i) vv[i] = ld128(rv, 16 * (64 * i + lane_));
+    for (int i = 0; i < NS / 2; ++i) vv[i] = ld_kv(rv, 16 * (64 * i + lane_));
   };
   int valid_cur = 0, valid_nxt = 0;
   // (a split past the context has pw0 >= p_stop: no load, no id check)
