@@ -121,10 +121,10 @@ def read_traffic(kernel, digest):
         return None
 
 
-def cpu_baseline(w, budget_s=20.0):
+def cpu_baseline(w, budget_s=30.0):
     """The oracle as it stands, on host cores: whole decoder layers of the same
-    workload (weights already generated) plus a slice of the lm_head rows,
-    scaled to one full step."""
+    workload (weights already generated) and then lm_head row chunks, each
+    part scaled to the full step if the time budget stops it early."""
     from threadpoolctl import threadpool_info
     from oracle import decode as od
     from oracle import runs
@@ -141,20 +141,24 @@ def cpu_baseline(w, budget_s=20.0):
         x, _, _ = runs.layer_batch(w, l, x, pools=(kp, vp), weights=lw)
         layer_s.append(time.perf_counter() - t0)
         l += 1
-    rows = np.arange(min(sh.vocab, wl.ROW_CHUNK))
-    blk = wl.lm_head_chunk(w.workload_id, sh, 0)
     gamma = w.final_norm()
-    t0 = time.perf_counter()
-    for b in range(w.batch):
-        od.lm_head(x[b], gamma, blk, sh.eps)
-    lm_s = (time.perf_counter() - t0) * sh.vocab / len(rows)
+    rows, lm_t, c = 0, 0.0, 0
+    while rows < sh.vocab and (rows == 0 or time.perf_counter() - t_all < budget_s):
+        blk = wl.lm_head_chunk(w.workload_id, sh, c)
+        t0 = time.perf_counter()
+        for b in range(w.batch):
+            od.lm_head(x[b], gamma, blk, sh.eps)
+        lm_t += time.perf_counter() - t0
+        rows += blk.shape[0]
+        c += 1
+    lm_s = lm_t * sh.vocab / rows
     step_s = float(np.mean(layer_s)) * sh.n_layers + lm_s
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": round(step_s * 1e3 / w.batch, 1), "unit": "ms/token", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{len(layer_s)} of {sh.n_layers} decoder layers (float64 oracle, batch {w.batch}, "
-                      f"ctx {int(w.ctx_lens.max())}) + {len(rows)} of {sh.vocab} lm_head rows, scaled to one "
-                      f"step; {sum(layer_s) + lm_s * len(rows) / sh.vocab:.1f} s of CPU work"}
+                      f"ctx {int(w.ctx_lens.max())}) + {rows} of {sh.vocab} lm_head rows, scaled to one "
+                      f"step; {sum(layer_s) + lm_t:.1f} s of CPU work"}
 
 
 # ------------------------------------------------------------------ main
