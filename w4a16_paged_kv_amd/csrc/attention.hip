@@ -51,10 +51,10 @@ static hipError_t launch_dg(const AttnArgs& a, hipStream_t s) {
   const dim3 grid(a.batch, a.n_kv_heads, a.max_splits), block(kAttnWaves * 64);
   // several pages per wavefront: the first page's loads go out before the
   // queries are staged. With two to eight pages per wavefront K/V are read
-  // non-temporally: the batch-16 step (16 sequences of 1024-4096 tokens)
-  // 2.177 -> 2.124 ms, while one page per wavefront (batch 1: 1.2368 ->
-  // 1.2438 ms per step) and 32 (32 sequences of 128-8192 tokens: 52.6 ->
-  // 55.7 us) keep the default policy.
+  // non-temporally (batch-16 step, 16 sequences of 1024-4096 tokens: 2.177
+  // -> 2.124 ms). Non-temporal loads were slower with one page per
+  // wavefront (batch-1 step 1.2368 -> 1.2438 ms) and with 32 (32 sequences
+  // of 128-8192 tokens: 52.6 -> 55.7 us), so those keep the default policy.
   if (a.pages_per_split > kAttnWaves && a.pages_per_split <= 8 * kAttnWaves)
     hipLaunchKernelGGL((paged_attn_kernel<D, GQ, true, true>), grid, block, 0, s, a);
   else if (a.pages_per_split > kAttnWaves)
